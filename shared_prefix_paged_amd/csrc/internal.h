@@ -1,0 +1,81 @@
+// Internal declarations shared by the host runtime (C++) and the HIP launchers.
+#pragma once
+
+#include <cstdint>
+#include <cstddef>
+#include <string>
+
+#include "spkv.h"
+
+#if defined(__HIPCC__)
+#define SPKV_HD __host__ __device__
+#else
+#define SPKV_HD
+#endif
+
+namespace spkv {
+
+// Thread-local error text behind spkv_last_error().
+spkv_status fail(spkv_status code, const std::string &msg);
+void clear_error();
+
+// Limits of this build.
+constexpr int kMaxGroups = 512;        // groups per step (cascade bitmask size)
+constexpr int kMaxGqa = 8;             // Hq / Hkv
+constexpr int kMaxKvHeads = 16;
+constexpr int kFlatSplitCap = 64;      // partials per row from the flat pass
+constexpr int kPrefixSplitCap = 64;    // partials per row from the prefix pass
+constexpr int kPrefixKeyTile = 32;     // keys per MFMA tile in the prefix kernel
+constexpr int kFlatGranule = 16;       // flat chunks are multiples of this many tokens
+
+// Per-group cascade bitmask passed to kernels by value.
+struct GroupMask {
+    uint32_t bits[kMaxGroups / 32];
+};
+
+// The launch plan of one decode call (host-computed, deterministic).
+struct Plan {
+    GroupMask cascade;        // bit g set: group g takes the prefix contraction
+    int32_t num_groups;
+    int32_t flat_chunk;       // base tau for the flat pass
+    int32_t flat_splits;      // grid x of the flat kernel (max partials per row)
+    int32_t prefix_chunk;     // base tau for the prefix pass (multiple of kPrefixKeyTile)
+    int32_t prefix_splits;    // grid x of the prefix kernel
+    int32_t prefix_waves;     // waves per prefix block (32 rows each)
+    int32_t prefix_mtiles;    // grid y of the prefix kernel
+    int32_t splits_total;     // prefix_splits + flat_splits (partial stride per row)
+    int64_t flat_items;
+    int64_t prefix_items;
+    int64_t ws_bytes;
+    bool run_prefix;          // some cascade group has Lp > 0 (bf16)
+    bool prefix_as_flat;      // float32 pools: prefix part via a per-request pass
+};
+
+// Chunk length of one request or group: at least `tau`, large enough that at
+// most `cap` chunks cover `len`, rounded up to `granule`.
+SPKV_HD inline int32_t chunk_for(int64_t len, int32_t tau, int32_t cap, int32_t granule) {
+    int64_t c = tau;
+    int64_t need = (len + cap - 1) / cap;
+    if (need > c) c = need;
+    c = (c + granule - 1) / granule * granule;
+    return (int32_t)c;
+}
+SPKV_HD inline int32_t splits_for(int64_t len, int32_t chunk) {
+    return len <= 0 ? 0 : (int32_t)((len + chunk - 1) / chunk);
+}
+
+// Validate a batch descriptor and its pools (host side only; device arrays
+// are not read).  kv may be null for plan-only calls.
+spkv_status validate_batch(const spkv_batch *b, const spkv_kv *kv);
+
+// Build the plan for a per-group choice (cascade[g] != 0 -> cascade; null -> all cascade).
+spkv_status make_plan(const spkv_batch *b, const int32_t *cascade, int32_t num_cus, Plan *out);
+
+// Compute units the split plan targets (MI355X: 256).  A constant, so plans
+// and workspace sizes are the same with or without a device present.
+constexpr int32_t kPlanCUs = 256;
+
+// Upper bound of Plan::ws_bytes for any per-group choice.
+size_t workspace_bound(const spkv_batch *b);
+
+}  // namespace spkv

@@ -1,0 +1,989 @@
+// HIP kernels for gfx950 (MI355X) and the device-op entry points of the C ABI.
+//
+// Decode attention over HOT/COLD storage (GraniKV paper, Sections 2.3, 3.2,
+// 3.3, 3.5): the prefix part is one batched contraction of every member query
+// of a prefix group against its contiguous HOT slab (bf16 MFMA, K/V tiles
+// staged through LDS); the suffix part is a per-request paged pass over the
+// COLD pool ("Paged KV cache" page, How it works step 3); partial states are
+// combined with the log-sum-exp merge of the paper's Eq. (1).  The flat
+// fallback runs the paged pass over [HOT prefix ; COLD suffix] per request.
+//
+// Internal conventions: scores are kept in log2 units (q.k * scale * log2 e)
+// so exp2 maps to the hardware's v_exp_f32; partial LSE values stored in the
+// workspace are base 2, and only outputs are converted to natural log.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "internal.h"
+
+using spkv::fail;
+using spkv::GroupMask;
+using spkv::Plan;
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kPartPrefix = 0;   // flat kernel covers the HOT prefix of cascade groups only
+constexpr int kPartRest = 1;     // flat kernel covers COLD tokens (plus HOT for flat-mode groups)
+constexpr int kFlatWavesMax = 4; // KV heads per flat block
+
+struct Args {
+    const void *q;
+    int32_t B, Hq, Hkv, G;
+    float scale_log2;
+    int32_t ng;
+    const int32_t *group_of;
+    const int32_t *indptr;
+    const int32_t *members;
+    const int64_t *hot_base;
+    const int32_t *hot_len;
+    int32_t page_size, max_blocks;
+    const int32_t *tables;
+    const int32_t *cold_lens;
+    const void *k_hot;
+    const void *v_hot;
+    int64_t hot_capacity;
+    const void *k_cold;
+    const void *v_cold;
+    int64_t cold_slots;
+    float *o_part;          // [B*Hq, splits_total, D]
+    float *lse_part;        // [B*Hq, splits_total], base-2
+    int32_t splits_total;
+    int32_t prefix_splits;  // offset of the flat partials inside a row
+    int32_t flat_splits;    // flat partial slots per row
+    int32_t flat_tau, prefix_tau, prefix_granule;
+    GroupMask cascade;
+};
+
+__device__ __forceinline__ bool mask_get(const GroupMask &m, int g) { return (m.bits[g >> 5] >> (g & 31)) & 1u; }
+
+// Geometry of one request, clamped so that no index can leave its buffer.
+struct Req {
+    int g;          // group or -1
+    int64_t base;   // HOT slab base
+    int lp;         // HOT prefix length (0 without a group)
+    int ls;         // COLD tokens
+    bool casc;      // group takes the prefix contraction
+};
+
+__device__ __forceinline__ Req req_geo(const Args &a, int b) {
+    Req r;
+    int g = a.group_of[b];
+    r.g = (g >= 0 && g < a.ng) ? g : -1;
+    r.base = 0;
+    r.lp = 0;
+    r.casc = false;
+    if (r.g >= 0) {
+        int64_t base = a.hot_base[r.g];
+        int lp = a.hot_len[r.g];
+        if (base >= 0 && lp > 0 && base + lp <= a.hot_capacity) {
+            r.base = base;
+            r.lp = lp;
+        }
+        r.casc = mask_get(a.cascade, r.g);
+    }
+    int ls = a.cold_lens[b];
+    const int64_t cap = (int64_t)a.max_blocks * a.page_size;
+    r.ls = ls < 0 ? 0 : (ls > cap ? (int)cap : ls);
+    if (a.cold_slots < a.page_size) r.ls = 0;   // no COLD page to read
+    return r;
+}
+
+// Tokens of request b covered by one flat launch: [lo, hi) of [HOT prefix ; COLD suffix].
+__device__ __forceinline__ void flat_range(const Req &r, int part, int &lo, int &hi) {
+    if (part == kPartPrefix) {
+        lo = 0;
+        hi = (r.g >= 0 && r.casc) ? r.lp : 0;
+    } else {
+        lo = (r.g >= 0 && r.casc) ? r.lp : 0;
+        hi = r.lp + r.ls;
+    }
+}
+
+template <int N>
+__device__ __forceinline__ float dpp_sum(float v);
+
+// Sum over aligned groups of N lanes (N = 8, 16, 32); every lane gets its group's sum.
+template <>
+__device__ __forceinline__ float dpp_sum<8>(float v) {
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));  // quad_perm 1,0,3,2
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));  // quad_perm 2,3,0,1
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, true)); // row_half_mirror
+    return v;
+}
+template <>
+__device__ __forceinline__ float dpp_sum<16>(float v) {
+    v = dpp_sum<8>(v);
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, true)); // row_mirror
+    return v;
+}
+template <>
+__device__ __forceinline__ float dpp_sum<32>(float v) {
+    v = dpp_sum<16>(v);
+    v += __shfl_xor(v, 16, 64);
+    return v;
+}
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ float fdot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// ---------------------------------------------------------------------------
+// Flat paged pass.  One block = one (chunk, request) and up to 4 KV heads,
+// one wave per head.  Inside a wave, LPT lanes hold one token's K (or V) row
+// as 16-byte pieces, so a wave-wide load covers TPW tokens; each group of LPT
+// lanes keeps its own online-softmax state, combined once at the end.
+// Row addresses (HOT slab row or COLD slot row) are computed once per 64
+// tokens, one per lane, and fetched with a lane permute.
+// ---------------------------------------------------------------------------
+template <bool BF16, int D, int G>
+__global__ __launch_bounds__(256) void flat_kernel(Args a, int part) {
+    constexpr int ESZ = BF16 ? 2 : 4;
+    constexpr int VEC = 16 / ESZ;            // elements per 16-byte piece
+    constexpr int LPT = D / VEC;             // lanes per token row
+    constexpr int TPW = 64 / LPT;            // tokens per wave-wide load
+    constexpr int U = (G <= 4) ? 4 : 2;      // loads in flight per operand
+    constexpr int TPI = TPW * U;             // tokens per iteration
+    static_assert(64 % TPI == 0, "iteration must divide 64 tokens");
+
+    const int s = blockIdx.x;
+    const int b = blockIdx.y;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int h = blockIdx.z * kFlatWavesMax + wave;
+    if (h >= a.Hkv) return;
+
+    const Req r = req_geo(a, b);
+    int lo, hi;
+    flat_range(r, part, lo, hi);
+    const int L = hi - lo;
+    const int tau = part == kPartPrefix ? a.prefix_tau : a.flat_tau;
+    const int chunk = spkv::chunk_for(L, tau, part == kPartPrefix ? spkv::kPrefixSplitCap : spkv::kFlatSplitCap,
+                                      part == kPartPrefix ? a.prefix_granule : spkv::kFlatGranule);
+    const int nsplit = spkv::splits_for(L, chunk);
+    if (s >= nsplit) return;
+    const int t0 = lo + s * chunk;
+    const int t1 = min(hi, t0 + chunk);
+
+    const int sub = lane % LPT;              // 16-byte piece of the row
+    const int grp = lane / LPT;              // token group inside the wave
+    const int row0 = b * a.Hq + h * G;       // first query row of this head
+
+    // Query rows in registers.
+    uint32_t qw[G][4];
+    {
+        const char *qb = (const char *)a.q + ((int64_t)row0 * D + sub * VEC) * ESZ;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            u32x4_t v = *(const u32x4_t *)(qb + (int64_t)g * D * ESZ);
+            qw[g][0] = v.x; qw[g][1] = v.y; qw[g][2] = v.z; qw[g][3] = v.w;
+        }
+    }
+
+    float m[G], l[G], acc[G][VEC];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        m[g] = -INFINITY;
+        l[g] = 0.f;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[g][e] = 0.f;
+    }
+
+    const char *khot = (const char *)a.k_hot;
+    const char *vhot = (const char *)a.v_hot;
+    const char *kcold = (const char *)a.k_cold;
+    const char *vcold = (const char *)a.v_cold;
+    const int32_t *table = a.tables + (int64_t)b * a.max_blocks;
+    const int64_t num_pages = a.cold_slots / a.page_size;
+    const uint32_t hot_row0 = (uint32_t)(r.base * a.Hkv + (int64_t)h * r.lp);
+
+    for (int blk = t0; blk < t1; blk += 64) {
+        // Row code of token blk + lane: bit 31 = HOT, low bits = row index.
+        uint32_t code;
+        {
+            int t = min(blk + lane, t1 - 1);
+            if (t < r.lp) {
+                code = 0x80000000u | (hot_row0 + (uint32_t)t);
+            } else {
+                int tc = t - r.lp;
+                int64_t page = table[tc / a.page_size];
+                page = page < 0 ? 0 : (page >= num_pages ? num_pages - 1 : page);
+                int64_t slot = page * a.page_size + tc % a.page_size;
+                code = (uint32_t)(slot * a.Hkv + h);
+            }
+        }
+        const int nblk = min(64, t1 - blk);
+        for (int it = 0; it < nblk; it += TPI) {
+            u32x4_t kv[U], vv[U];
+            bool valid[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int ti = it + u * TPW + grp;          // token index inside the 64-block
+                valid[u] = ti < nblk;
+                const uint32_t c = (uint32_t)__shfl((int)code, min(ti, nblk - 1), 64);
+                const bool hot = c >> 31;
+                const int64_t off = ((int64_t)(c & 0x7fffffffu) * D + sub * VEC) * ESZ;
+                kv[u] = *(const u32x4_t *)((hot ? khot : kcold) + off);
+                vv[u] = *(const u32x4_t *)((hot ? vhot : vcold) + off);
+            }
+            float sc[U][G];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    float d;
+                    if constexpr (BF16) {
+                        d = fdot2(qw[g][0], kv[u].x, 0.f);
+                        d = fdot2(qw[g][1], kv[u].y, d);
+                        d = fdot2(qw[g][2], kv[u].z, d);
+                        d = fdot2(qw[g][3], kv[u].w, d);
+                    } else {
+                        d = __uint_as_float(qw[g][0]) * __uint_as_float(kv[u].x);
+                        d = fmaf(__uint_as_float(qw[g][1]), __uint_as_float(kv[u].y), d);
+                        d = fmaf(__uint_as_float(qw[g][2]), __uint_as_float(kv[u].z), d);
+                        d = fmaf(__uint_as_float(qw[g][3]), __uint_as_float(kv[u].w), d);
+                    }
+                    d = dpp_sum<LPT>(d);
+                    sc[u][g] = valid[u] ? d * a.scale_log2 : -INFINITY;
+                }
+            }
+            float vf[U][VEC];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if constexpr (BF16) {
+                    vf[u][0] = bf16lo(vv[u].x); vf[u][1] = bf16hi(vv[u].x);
+                    vf[u][2] = bf16lo(vv[u].y); vf[u][3] = bf16hi(vv[u].y);
+                    vf[u][4] = bf16lo(vv[u].z); vf[u][5] = bf16hi(vv[u].z);
+                    vf[u][6] = bf16lo(vv[u].w); vf[u][7] = bf16hi(vv[u].w);
+                } else {
+                    vf[u][0] = __uint_as_float(vv[u].x); vf[u][1] = __uint_as_float(vv[u].y);
+                    vf[u][2] = __uint_as_float(vv[u].z); vf[u][3] = __uint_as_float(vv[u].w);
+                }
+            }
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                float mx = sc[0][g];
+#pragma unroll
+                for (int u = 1; u < U; ++u) mx = fmaxf(mx, sc[u][g]);
+                const float mnew = fmaxf(m[g], mx);
+                const float muse = mnew == -INFINITY ? 0.f : mnew;
+                const float alpha = exp2f(m[g] - muse);
+                l[g] *= alpha;
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) acc[g][e] *= alpha;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const float p = exp2f(sc[u][g] - muse);
+                    l[g] += p;
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) acc[g][e] = fmaf(p, vf[u][e], acc[g][e]);
+                }
+                m[g] = mnew;
+            }
+        }
+    }
+
+    // Combine the TPW token groups of the wave (lanes sub, sub+LPT, ...).
+    const int srow = a.prefix_splits * (part == kPartRest) + s;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        float M = m[g];
+#pragma unroll
+        for (int off = LPT; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+        const float muse = M == -INFINITY ? 0.f : M;
+        const float sc = exp2f(m[g] - muse);
+        float lt = l[g] * sc;
+        float o[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) o[e] = acc[g][e] * sc;
+#pragma unroll
+        for (int off = LPT; off < 64; off <<= 1) {
+            lt += __shfl_xor(lt, off, 64);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) o[e] += __shfl_xor(o[e], off, 64);
+        }
+        if (grp == 0) {
+            const int64_t prow = (int64_t)(row0 + g) * a.splits_total + srow;
+            const float inv = lt > 0.f ? 1.f / lt : 0.f;
+            float *dst = a.o_part + prow * D + sub * VEC;
+#pragma unroll
+            for (int e = 0; e < VEC; e += 4) {
+                float4 w = make_float4(o[e] * inv, o[e + 1] * inv, o[e + 2] * inv, o[e + 3] * inv);
+                *(float4 *)(dst + e) = w;
+            }
+            if (sub == 0) a.lse_part[prow] = lt > 0.f ? M + __log2f(lt) : -INFINITY;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Prefix contraction on bf16 MFMA (v_mfma_f32_32x32x16_bf16).
+//
+// Block = W waves; wave w owns 32 query rows (rows of a prefix group are
+// member-major: row = member * G + head-in-group).  Per 32-key tile:
+//   S^T[key, row] = K_tile . Q^T   (A = K rows from LDS, B = Q in registers)
+//   online softmax along keys: each lane holds one query row's 16 scores
+//   O^T[d, row]  += V_tile^T . P^T (A = V columns from LDS, B = P from the
+//                                    S^T accumulators, converted to bf16)
+// MFMA 32x32 operand layout: A[m][k] lives in lane m + 32*(k/8), element
+// k%8; B[k][n] in lane n + 32*(k/8); D[m][n] in lane n + 32*((m/4)%2),
+// register (m/8)*4 + m%4.  K rows are stored in LDS with bits 2 and 3 of the
+// key index swapped, so that accumulator register j of lane l holds key
+// 16*(j/8) + 8*(l/32) + j%8: the P operand for PV is then registers
+// 8*kb .. 8*kb+7 as they stand.  V is read from LDS as NDB = D/32 adjacent
+// columns per key; output row (d) m of block db is column NDB*m + db.
+// ---------------------------------------------------------------------------
+template <int D, int W>
+__global__ __launch_bounds__(64 * W) void prefix_mfma_kernel(Args a) {
+    constexpr int NT = spkv::kPrefixKeyTile;   // 32 keys per tile
+    constexpr int KS = D / 16;                 // MFMA k-steps for Q.K
+    constexpr int NDB = D / 32;                // 32-column blocks of the output
+    constexpr int PITCH = D + 8;               // LDS row pitch (elements)
+    constexpr int PIECES = NT * D / 8;         // 16-byte pieces per tile
+    __shared__ __attribute__((aligned(16))) uint16_t ks[NT * PITCH];
+    __shared__ __attribute__((aligned(16))) uint16_t vs[NT * PITCH];
+
+    const int gz = blockIdx.z;
+    const int g = gz / a.Hkv;
+    const int h = gz % a.Hkv;
+    if (g >= a.ng || !mask_get(a.cascade, g)) return;
+    const int64_t base = a.hot_base[g];
+    const int lp = a.hot_len[g];
+    if (lp <= 0 || base < 0 || base + lp > a.hot_capacity) return;
+    int m0 = a.indptr[g], m1 = a.indptr[g + 1];
+    m0 = max(0, min(m0, a.B));
+    m1 = max(m0, min(m1, a.B));
+    const int M = (m1 - m0) * a.G;
+    const int mt = blockIdx.y;
+    if (mt * 32 * W >= M) return;
+    const int chunk = spkv::chunk_for(lp, a.prefix_tau, spkv::kPrefixSplitCap, NT);
+    const int nsplit = spkv::splits_for(lp, chunk);
+    const int s = blockIdx.x;
+    if (s >= nsplit) return;
+    const int k0 = s * chunk;
+    const int k1 = min(lp, k0 + chunk);
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int half = lane >> 5;
+    const int col = lane & 31;
+
+    // This lane's query row (column of S^T / O^T).
+    const int row = mt * 32 * W + wave * 32 + col;
+    const bool row_ok = row < M;
+    int qb = 0, qj = 0;
+    if (row_ok) {
+        int mb = a.members[m0 + row / a.G];
+        qb = max(0, min(mb, a.B - 1));
+        qj = h * a.G + row % a.G;
+    }
+    bf16x8_t qf[KS];
+    {
+        const uint16_t *qp = (const uint16_t *)a.q + ((int64_t)qb * a.Hq + qj) * D + half * 8;
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+            u32x4_t v = row_ok ? *(const u32x4_t *)(qp + k * 16) : u32x4_t{0, 0, 0, 0};
+            qf[k] = __builtin_bit_cast(bf16x8_t, v);
+        }
+    }
+
+    const uint16_t *kh = (const uint16_t *)a.k_hot + ((int64_t)base * a.Hkv + (int64_t)h * lp) * D;
+    const uint16_t *vh = (const uint16_t *)a.v_hot + ((int64_t)base * a.Hkv + (int64_t)h * lp) * D;
+
+    constexpr int MAXP = PIECES / (64 * W);   // 16-byte pieces per thread per tile
+    static_assert(PIECES % (64 * W) == 0, "tile must split evenly over the block");
+    u32x4_t stk[MAXP], stv[MAXP];
+    constexpr int nthr = 64 * W;
+    auto stage_load = [&](int kt) {
+#pragma unroll
+        for (int i = 0; i < MAXP; ++i) {
+            const int pc = tid + i * nthr;
+            {
+                const int key = pc / (D / 8);
+                const int part = pc % (D / 8);
+                const int kg = kt + key;
+                if (kg < k1) {
+                    stk[i] = *(const u32x4_t *)(kh + (int64_t)kg * D + part * 8);
+                    stv[i] = *(const u32x4_t *)(vh + (int64_t)kg * D + part * 8);
+                } else {
+                    stk[i] = u32x4_t{0, 0, 0, 0};
+                    stv[i] = u32x4_t{0, 0, 0, 0};
+                }
+            }
+        }
+    };
+    auto stage_store = [&]() {
+#pragma unroll
+        for (int i = 0; i < MAXP; ++i) {
+            const int pc = tid + i * nthr;
+            {
+                const int key = pc / (D / 8);
+                const int part = pc % (D / 8);
+                const int krow = (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);  // swap bits 2 and 3
+                *(u32x4_t *)(ks + krow * PITCH + part * 8) = stk[i];
+                *(u32x4_t *)(vs + key * PITCH + part * 8) = stv[i];
+            }
+        }
+    };
+
+    f32x16_t oacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) oacc[db][j] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+
+    stage_load(k0);
+    for (int kt = k0; kt < k1; kt += NT) {
+        __syncthreads();
+        stage_store();
+        __syncthreads();
+        if (kt + NT < k1) stage_load(kt + NT);
+
+        // S^T = K . Q^T
+        f32x16_t sacc;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sacc[j] = 0.f;
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+            bf16x8_t af = *(const bf16x8_t *)(ks + col * PITCH + k * 16 + half * 8);
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[k], sacc, 0, 0, 0);
+        }
+        // Online softmax along keys (one query row per lane, two lane halves).
+        float sv[16];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int key = kt + 16 * (j >> 3) + 8 * half + (j & 7);
+            sv[j] = key < k1 ? sacc[j] * a.scale_log2 : -INFINITY;
+            mx = fmaxf(mx, sv[j]);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mnew = fmaxf(m_run, mx);
+        const float muse = mnew == -INFINITY ? 0.f : mnew;
+        const float alpha = exp2f(m_run - muse);
+        m_run = mnew;
+        float psum = 0.f;
+        uint32_t pk[8];
+#pragma unroll
+        for (int j = 0; j < 16; j += 2) {
+            const float p0 = exp2f(sv[j] - muse);
+            const float p1 = exp2f(sv[j + 1] - muse);
+            psum += p0 + p1;
+            bf16x2_t pp = {(__bf16)p0, (__bf16)p1};   // round to nearest even
+            pk[j >> 1] = __builtin_bit_cast(uint32_t, pp);
+        }
+        l_run = l_run * alpha + psum;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
+
+        // O^T += V^T . P^T, two 16-key steps.
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            uint16_t vcol[NDB][8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int key = 16 * kb + 8 * half + e;
+                const uint16_t *src = vs + key * PITCH + col * NDB;
+                if constexpr (NDB == 4) {
+                    u32x2_t w = *(const u32x2_t *)src;
+                    vcol[0][e] = (uint16_t)(w.x & 0xffff); vcol[1][e] = (uint16_t)(w.x >> 16);
+                    vcol[2][e] = (uint16_t)(w.y & 0xffff); vcol[3][e] = (uint16_t)(w.y >> 16);
+                } else {
+                    uint32_t w = *(const uint32_t *)src;
+                    vcol[0][e] = (uint16_t)(w & 0xffff); vcol[1][e] = (uint16_t)(w >> 16);
+                }
+            }
+            u32x4_t pb = {pk[4 * kb + 0], pk[4 * kb + 1], pk[4 * kb + 2], pk[4 * kb + 3]};
+            const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pb);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                u32x4_t w;
+                w.x = (uint32_t)vcol[db][0] | ((uint32_t)vcol[db][1] << 16);
+                w.y = (uint32_t)vcol[db][2] | ((uint32_t)vcol[db][3] << 16);
+                w.z = (uint32_t)vcol[db][4] | ((uint32_t)vcol[db][5] << 16);
+                w.w = (uint32_t)vcol[db][6] | ((uint32_t)vcol[db][7] << 16);
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w), pf, oacc[db], 0, 0, 0);
+            }
+        }
+    }
+
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    if (!row_ok) return;
+    const int64_t prow = ((int64_t)qb * a.Hq + qj) * a.splits_total + s;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    float *dst = a.o_part + prow * D;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int mrow = (j >> 2) * 8 + half * 4 + (j & 3);
+        if constexpr (NDB == 4) {
+            *(float4 *)(dst + 4 * mrow) = make_float4(oacc[0][j] * inv, oacc[1][j] * inv, oacc[2][j] * inv, oacc[3][j] * inv);
+        } else {
+            *(float2 *)(dst + 2 * mrow) = make_float2(oacc[0][j] * inv, oacc[1][j] * inv);
+        }
+    }
+    if (half == 0) a.lse_part[prow] = l_tot > 0.f ? m_run + __log2f(l_tot) : -INFINITY;
+}
+
+// ---------------------------------------------------------------------------
+// Merge of a row's partial states (Eq. (1) applied across all partials).
+// One wave per (request, query head) row; four rows per block.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void merge_kernel(Args a, float *out, float *lse_out) {
+    constexpr int VPL = D / 64;   // output floats per lane
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+    if (row >= (int64_t)a.B * a.Hq) return;
+    const int b = (int)(row / a.Hq);
+    const Req r = req_geo(a, b);
+    int np = 0;
+    if (r.g >= 0 && r.casc && r.lp > 0)
+        np = spkv::splits_for(r.lp, spkv::chunk_for(r.lp, a.prefix_tau, spkv::kPrefixSplitCap, a.prefix_granule));
+    int lo, hi;
+    flat_range(r, kPartRest, lo, hi);
+    const int L = hi - lo;
+    int nf = spkv::splits_for(L, spkv::chunk_for(L, a.flat_tau, spkv::kFlatSplitCap, spkv::kFlatGranule));
+    np = min(np, a.prefix_splits);   // never read past this row's partial slots
+    nf = min(nf, a.flat_splits);
+    const int n = np + nf;
+    const int64_t prow0 = row * a.splits_total;
+
+    float mx = -INFINITY;
+    for (int k = lane; k < n; k += 64) {
+        const int idx = k < np ? k : a.prefix_splits + (k - np);
+        mx = fmaxf(mx, a.lse_part[prow0 + idx]);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+    const float muse = mx == -INFINITY ? 0.f : mx;
+    float o[VPL];
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) o[e] = 0.f;
+    float wsum = 0.f;
+    for (int k = 0; k < n; ++k) {
+        const int idx = k < np ? k : a.prefix_splits + (k - np);
+        const float lse = a.lse_part[prow0 + idx];
+        const float w = exp2f(lse - muse);
+        wsum += w;
+        const float *src = a.o_part + (prow0 + idx) * D + lane * VPL;
+        if (w > 0.f) {
+#pragma unroll
+            for (int e = 0; e < VPL; ++e) o[e] = fmaf(w, src[e], o[e]);
+        }
+    }
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) out[row * D + lane * VPL + e] = o[e] * inv;
+    if (lse_out && lane == 0) lse_out[row] = wsum > 0.f ? (mx + __log2f(wsum)) * kLn2 : -INFINITY;
+}
+
+// Two-way merge of natural-log partial states, Eq. (1).  head_dim divides the
+// block size, so a row never straddles blocks; all reads of a block finish
+// before any write, which makes in-place use (o == o_a, lse == lse_a) safe.
+__global__ __launch_bounds__(256) void merge2_kernel(const float *oa, const float *la, const float *ob, const float *lb,
+                                                     float *o, float *lse, int64_t rows, int d) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const bool ok = i < rows * d;
+    const int64_t r = ok ? i / d : 0;
+    float wa = 0.f, wb = 0.f, va = 0.f, vb = 0.f, mu = 0.f;
+    if (ok) {
+        const float xa = la[r], xb = lb[r];
+        const float m = fmaxf(xa, xb);
+        mu = m == -INFINITY ? 0.f : m;
+        wa = expf(xa - mu);
+        wb = expf(xb - mu);
+        va = oa[i];
+        vb = ob[i];
+    }
+    __syncthreads();
+    if (!ok) return;
+    const float w = wa + wb;
+    o[i] = w > 0.f ? (wa * va + wb * vb) / w : 0.f;
+    if (lse && i % d == 0) lse[r] = w > 0.f ? mu + logf(w) : -INFINITY;
+}
+
+// ---------------------------------------------------------------------------
+// Cache writes: 16-byte copies.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void hot_write_kernel(const u32x4_t *ksrc, const u32x4_t *vsrc, u32x4_t *khot,
+                                                        u32x4_t *vhot, int64_t base, int64_t lp, int hkv, int pieces_per_row) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t total = lp * hkv * pieces_per_row;
+    if (i >= total) return;
+    const int64_t piece = i % pieces_per_row;
+    const int64_t th = i / pieces_per_row;      // token-major source row: t * hkv + h
+    const int64_t t = th / hkv;
+    const int64_t h = th % hkv;
+    const int64_t dst = ((base * hkv + h * lp) + t) * pieces_per_row + piece;
+    khot[dst] = ksrc[i];
+    vhot[dst] = vsrc[i];
+}
+
+__global__ __launch_bounds__(256) void reshape_and_cache_kernel(const u32x4_t *knew, const u32x4_t *vnew,
+                                                                const int32_t *slots, int n, u32x4_t *kcold,
+                                                                u32x4_t *vcold, int64_t cold_slots, int pieces_per_slot) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (int64_t)n * pieces_per_slot) return;
+    const int64_t tok = i / pieces_per_slot;
+    const int64_t piece = i % pieces_per_slot;
+    const int64_t slot = slots[tok];
+    if (slot < 0 || slot >= cold_slots) return;
+    kcold[slot * pieces_per_slot + piece] = knew[i];
+    vcold[slot * pieces_per_slot + piece] = vnew[i];
+}
+
+__global__ __launch_bounds__(256) void copy_blocks_kernel(const int32_t *pairs, u32x4_t *kcold, u32x4_t *vcold,
+                                                          int num_pages, int64_t pieces_per_page) {
+    const int p = blockIdx.y;
+    const int64_t src = pairs[2 * p], dst = pairs[2 * p + 1];
+    if (src < 0 || src >= num_pages || dst < 0 || dst >= num_pages) return;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < pieces_per_page; i += (int64_t)gridDim.x * blockDim.x) {
+        kcold[dst * pieces_per_page + i] = kcold[src * pieces_per_page + i];
+        vcold[dst * pieces_per_page + i] = vcold[src * pieces_per_page + i];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launch plumbing and optional per-launch timing.
+// ---------------------------------------------------------------------------
+struct Timing {
+    std::mutex mu;
+    bool on = false;
+    struct Rec { int kernel; hipEvent_t a, b; };
+    std::vector<Rec> pending;
+    std::vector<hipEvent_t> pool;
+    double total_ms[SPKV_NUM_KERNELS] = {};
+    int64_t count[SPKV_NUM_KERNELS] = {};
+};
+Timing &timing() {
+    static Timing t;
+    return t;
+}
+
+hipEvent_t take_event(Timing &t) {
+    if (!t.pool.empty()) {
+        hipEvent_t e = t.pool.back();
+        t.pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+struct TimedLaunch {
+    int kernel;
+    hipStream_t st;
+    hipEvent_t a = nullptr, b = nullptr;
+    TimedLaunch(int k, hipStream_t s) : kernel(k), st(s) {
+        Timing &t = timing();
+        std::lock_guard<std::mutex> g(t.mu);
+        if (!t.on) return;
+        a = take_event(t);
+        b = take_event(t);
+        if (a) (void)hipEventRecord(a, st);
+    }
+    ~TimedLaunch() {
+        if (!a || !b) return;
+        (void)hipEventRecord(b, st);
+        Timing &t = timing();
+        std::lock_guard<std::mutex> g(t.mu);
+        t.pending.push_back({kernel, a, b});
+    }
+};
+
+spkv_status check_launch(const char *what) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(SPKV_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+    return SPKV_OK;
+}
+
+template <bool BF16, int D>
+spkv_status launch_flat_d(const Args &a, int part, int splits, hipStream_t st) {
+    const int zb = (a.Hkv + kFlatWavesMax - 1) / kFlatWavesMax;
+    const int waves = a.Hkv < kFlatWavesMax ? a.Hkv : kFlatWavesMax;
+    dim3 grid(splits, a.B, zb), block(64 * waves);
+    TimedLaunch tl(SPKV_KERNEL_FLAT, st);
+    switch (a.G) {
+    case 1: flat_kernel<BF16, D, 1><<<grid, block, 0, st>>>(a, part); break;
+    case 2: flat_kernel<BF16, D, 2><<<grid, block, 0, st>>>(a, part); break;
+    case 3: flat_kernel<BF16, D, 3><<<grid, block, 0, st>>>(a, part); break;
+    case 4: flat_kernel<BF16, D, 4><<<grid, block, 0, st>>>(a, part); break;
+    case 5: flat_kernel<BF16, D, 5><<<grid, block, 0, st>>>(a, part); break;
+    case 6: flat_kernel<BF16, D, 6><<<grid, block, 0, st>>>(a, part); break;
+    case 7: flat_kernel<BF16, D, 7><<<grid, block, 0, st>>>(a, part); break;
+    case 8: flat_kernel<BF16, D, 8><<<grid, block, 0, st>>>(a, part); break;
+    default: return fail(SPKV_E_INVAL, "unsupported GQA group size");
+    }
+    return check_launch("flat_kernel");
+}
+
+spkv_status launch_flat(const Args &a, bool bf16, int d, int part, int splits, hipStream_t st) {
+    if (splits <= 0 || a.B == 0) return SPKV_OK;
+    if (bf16) return d == 128 ? launch_flat_d<true, 128>(a, part, splits, st) : launch_flat_d<true, 64>(a, part, splits, st);
+    return d == 128 ? launch_flat_d<false, 128>(a, part, splits, st) : launch_flat_d<false, 64>(a, part, splits, st);
+}
+
+spkv_status launch_prefix(const Args &a, const Plan &p, int d, hipStream_t st) {
+    if (p.prefix_splits <= 0 || p.prefix_mtiles <= 0) return SPKV_OK;
+    dim3 grid(p.prefix_splits, p.prefix_mtiles, a.ng * a.Hkv), block(64 * p.prefix_waves);
+    TimedLaunch tl(SPKV_KERNEL_PREFIX, st);
+    switch (p.prefix_waves * 1000 + d) {
+    case 1128: prefix_mfma_kernel<128, 1><<<grid, block, 0, st>>>(a); break;
+    case 2128: prefix_mfma_kernel<128, 2><<<grid, block, 0, st>>>(a); break;
+    case 4128: prefix_mfma_kernel<128, 4><<<grid, block, 0, st>>>(a); break;
+    case 1064: prefix_mfma_kernel<64, 1><<<grid, block, 0, st>>>(a); break;
+    case 2064: prefix_mfma_kernel<64, 2><<<grid, block, 0, st>>>(a); break;
+    case 4064: prefix_mfma_kernel<64, 4><<<grid, block, 0, st>>>(a); break;
+    default: return fail(SPKV_E_INVAL, "unsupported prefix tile");
+    }
+    return check_launch("prefix_mfma_kernel");
+}
+
+spkv_status launch_merge(const Args &a, int d, float *out, float *lse, hipStream_t st) {
+    const int64_t rows = (int64_t)a.B * a.Hq;
+    if (rows == 0) return SPKV_OK;
+    dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+    TimedLaunch tl(SPKV_KERNEL_MERGE, st);
+    if (d == 128) merge_kernel<128><<<grid, block, 0, st>>>(a, out, lse);
+    else merge_kernel<64><<<grid, block, 0, st>>>(a, out, lse);
+    return check_launch("merge_kernel");
+}
+
+Args make_args(const spkv_batch *b, const spkv_kv *kv, const Plan &p, void *ws) {
+    Args a;
+    std::memset(&a, 0, sizeof(a));
+    a.q = b->q;
+    a.B = b->batch;
+    a.Hq = b->num_q_heads;
+    a.Hkv = b->num_kv_heads;
+    a.G = b->num_q_heads / b->num_kv_heads;
+    a.scale_log2 = b->scale * kLog2e;
+    a.ng = b->num_groups;
+    a.group_of = b->group_of;
+    a.indptr = b->group_indptr;
+    a.members = b->group_members;
+    a.hot_base = b->hot_base;
+    a.hot_len = b->hot_len;
+    a.page_size = b->page_size;
+    a.max_blocks = b->max_blocks;
+    a.tables = b->block_tables;
+    a.cold_lens = b->cold_lens;
+    a.k_hot = kv->k_hot;
+    a.v_hot = kv->v_hot;
+    a.hot_capacity = kv->hot_capacity;
+    a.k_cold = kv->k_cold;
+    a.v_cold = kv->v_cold;
+    a.cold_slots = kv->cold_slots;
+    const int64_t rows = (int64_t)b->batch * b->num_q_heads;
+    a.o_part = (float *)ws;
+    a.lse_part = (float *)((char *)ws + ((rows * p.splits_total * b->head_dim * 4 + 255) / 256) * 256);
+    a.splits_total = p.splits_total;
+    a.prefix_splits = p.prefix_splits;
+    a.flat_splits = p.flat_splits;
+    a.flat_tau = p.flat_chunk;
+    a.prefix_tau = p.prefix_chunk > 0 ? p.prefix_chunk : 1;
+    a.prefix_granule = p.prefix_as_flat ? spkv::kFlatGranule : spkv::kPrefixKeyTile;
+    a.cascade = p.cascade;
+    return a;
+}
+
+spkv_status run_decode(const spkv_batch *b, const spkv_kv *kv, const int32_t *cascade, float *out, float *lse,
+                       void *ws, size_t ws_bytes, void *stream) {
+    spkv_status st = spkv::validate_batch(b, kv);
+    if (st != SPKV_OK) return st;
+    if (!kv) return fail(SPKV_E_INVAL, "null kv");
+    if (b->batch == 0) return SPKV_OK;
+    if (!out) return fail(SPKV_E_INVAL, "null out");
+    Plan p;
+    st = spkv::make_plan(b, cascade, spkv::kPlanCUs, &p);
+    if (st != SPKV_OK) return st;
+    if (!ws || ws_bytes < (size_t)p.ws_bytes)
+        return fail(SPKV_E_INVAL, "workspace too small: need " + std::to_string(p.ws_bytes) + " bytes");
+    Args a = make_args(b, kv, p, ws);
+    hipStream_t hs = (hipStream_t)stream;
+    const bool bf16 = b->dtype == SPKV_DTYPE_BF16;
+    if (p.run_prefix) {
+        st = bf16 ? launch_prefix(a, p, b->head_dim, hs)
+                  : launch_flat(a, false, b->head_dim, kPartPrefix, p.prefix_splits, hs);
+        if (st != SPKV_OK) return st;
+    }
+    st = launch_flat(a, bf16, b->head_dim, kPartRest, p.flat_splits, hs);
+    if (st != SPKV_OK) return st;
+    return launch_merge(a, b->head_dim, out, lse, hs);
+}
+
+spkv_status check_kv_shape(int32_t hkv, int32_t d, int32_t dtype) {
+    if (hkv < 1 || hkv > spkv::kMaxKvHeads) return fail(SPKV_E_INVAL, "num_kv_heads must be 1..16");
+    if (d != 64 && d != 128) return fail(SPKV_E_INVAL, "head_dim must be 64 or 128");
+    if (dtype != SPKV_DTYPE_BF16 && dtype != SPKV_DTYPE_F32) return fail(SPKV_E_INVAL, "unknown dtype");
+    return SPKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+spkv_status spkv_hot_write(const void *k_src, const void *v_src, int64_t base, int64_t lp, void *k_hot, void *v_hot,
+                           int64_t hot_capacity, int32_t hkv, int32_t d, int32_t dtype, void *stream) {
+    spkv_status st = check_kv_shape(hkv, d, dtype);
+    if (st != SPKV_OK) return st;
+    if (base < 0 || lp < 0 || base + lp > hot_capacity) return fail(SPKV_E_INVAL, "hot_write: slab outside the pool");
+    if (lp == 0) return SPKV_OK;
+    if (!k_src || !v_src || !k_hot || !v_hot) return fail(SPKV_E_INVAL, "hot_write: null pointer");
+    const int esz = dtype == SPKV_DTYPE_BF16 ? 2 : 4;
+    const int ppr = d * esz / 16;
+    const int64_t total = lp * hkv * ppr;
+    TimedLaunch tl(SPKV_KERNEL_CACHE, (hipStream_t)stream);
+    hot_write_kernel<<<(unsigned)((total + 255) / 256), 256, 0, (hipStream_t)stream>>>(
+        (const u32x4_t *)k_src, (const u32x4_t *)v_src, (u32x4_t *)k_hot, (u32x4_t *)v_hot, base, lp, hkv, ppr);
+    return check_launch("hot_write_kernel");
+}
+
+spkv_status spkv_reshape_and_cache(const void *k_new, const void *v_new, const int32_t *slot_mapping, int32_t n,
+                                   void *k_cold, void *v_cold, int64_t cold_slots, int32_t hkv, int32_t d,
+                                   int32_t dtype, void *stream) {
+    spkv_status st = check_kv_shape(hkv, d, dtype);
+    if (st != SPKV_OK) return st;
+    if (n < 0 || cold_slots < 0) return fail(SPKV_E_INVAL, "reshape_and_cache: negative size");
+    if (n == 0) return SPKV_OK;
+    if (!k_new || !v_new || !slot_mapping || !k_cold || !v_cold) return fail(SPKV_E_INVAL, "reshape_and_cache: null pointer");
+    const int esz = dtype == SPKV_DTYPE_BF16 ? 2 : 4;
+    const int pps = hkv * d * esz / 16;
+    const int64_t total = (int64_t)n * pps;
+    TimedLaunch tl(SPKV_KERNEL_CACHE, (hipStream_t)stream);
+    reshape_and_cache_kernel<<<(unsigned)((total + 255) / 256), 256, 0, (hipStream_t)stream>>>(
+        (const u32x4_t *)k_new, (const u32x4_t *)v_new, slot_mapping, n, (u32x4_t *)k_cold, (u32x4_t *)v_cold,
+        cold_slots, pps);
+    return check_launch("reshape_and_cache_kernel");
+}
+
+spkv_status spkv_copy_blocks(const int32_t *pairs, int32_t n, void *k_cold, void *v_cold, int32_t num_pages,
+                             int32_t page_size, int32_t hkv, int32_t d, int32_t dtype, void *stream) {
+    spkv_status st = check_kv_shape(hkv, d, dtype);
+    if (st != SPKV_OK) return st;
+    if (n < 0 || num_pages < 0 || page_size < 1) return fail(SPKV_E_INVAL, "copy_blocks: bad size");
+    if (n == 0) return SPKV_OK;
+    if (n > 65535) return fail(SPKV_E_INVAL, "copy_blocks: at most 65535 pairs per call");
+    if (!pairs || !k_cold || !v_cold) return fail(SPKV_E_INVAL, "copy_blocks: null pointer");
+    const int esz = dtype == SPKV_DTYPE_BF16 ? 2 : 4;
+    const int64_t ppp = (int64_t)page_size * hkv * d * esz / 16;
+    const unsigned gx = (unsigned)std::min<int64_t>(64, (ppp + 255) / 256);
+    TimedLaunch tl(SPKV_KERNEL_CACHE, (hipStream_t)stream);
+    copy_blocks_kernel<<<dim3(gx, (unsigned)n), 256, 0, (hipStream_t)stream>>>(pairs, (u32x4_t *)k_cold,
+                                                                                (u32x4_t *)v_cold, num_pages, ppp);
+    return check_launch("copy_blocks_kernel");
+}
+
+spkv_status spkv_cascade_decode(const spkv_batch *batch, const spkv_kv *kv, float *out, float *lse, void *ws,
+                                size_t ws_bytes, void *stream) {
+    return run_decode(batch, kv, nullptr, out, lse, ws, ws_bytes, stream);
+}
+
+spkv_status spkv_dense_decode(const spkv_batch *batch, const spkv_kv *kv, float *out, float *lse, void *ws,
+                              size_t ws_bytes, void *stream) {
+    spkv_status st = spkv::validate_batch(batch, kv);
+    if (st != SPKV_OK) return st;
+    std::vector<int32_t> none((size_t)std::max(1, batch->num_groups), 0);
+    return run_decode(batch, kv, none.data(), out, lse, ws, ws_bytes, stream);
+}
+
+spkv_status spkv_decode_step(const spkv_batch *batch, const spkv_kv *kv, const spkv_dispatch_params *params,
+                             float *out, float *lse, void *ws, size_t ws_bytes, void *stream, int32_t *cascade_out) {
+    spkv_status st = spkv::validate_batch(batch, kv);
+    if (st != SPKV_OK) return st;
+    std::vector<int32_t> choice((size_t)std::max(1, batch->num_groups), 0);
+    st = spkv_dispatch(batch, params, choice.data());
+    if (st != SPKV_OK) return st;
+    if (cascade_out)
+        for (int g = 0; g < batch->num_groups; ++g) cascade_out[g] = choice[(size_t)g];
+    return run_decode(batch, kv, choice.data(), out, lse, ws, ws_bytes, stream);
+}
+
+spkv_status spkv_merge_states(const float *o_a, const float *lse_a, const float *o_b, const float *lse_b, float *o,
+                              float *lse, int64_t rows, int32_t head_dim, void *stream) {
+    if (rows < 0 || head_dim <= 0) return fail(SPKV_E_INVAL, "merge_states: bad size");
+    if (rows == 0) return SPKV_OK;
+    if (!o_a || !lse_a || !o_b || !lse_b || !o) return fail(SPKV_E_INVAL, "merge_states: null pointer");
+    if (head_dim > 256 || 256 % head_dim) return fail(SPKV_E_INVAL, "merge_states: head_dim must divide 256");
+    const int64_t total = rows * head_dim;
+    TimedLaunch tl(SPKV_KERNEL_MERGE, (hipStream_t)stream);
+    merge2_kernel<<<(unsigned)((total + 255) / 256), 256, 0, (hipStream_t)stream>>>(o_a, lse_a, o_b, lse_b, o, lse,
+                                                                                    rows, head_dim);
+    return check_launch("merge2_kernel");
+}
+
+spkv_status spkv_timing_enable(int32_t on) {
+    Timing &t = timing();
+    std::lock_guard<std::mutex> g(t.mu);
+    t.on = on != 0;
+    return SPKV_OK;
+}
+
+spkv_status spkv_timing_read(int32_t kernel, double *total_ms, int64_t *launches) {
+    if (kernel < 0 || kernel >= SPKV_NUM_KERNELS || !total_ms || !launches)
+        return fail(SPKV_E_INVAL, "timing_read: bad argument");
+    Timing &t = timing();
+    std::lock_guard<std::mutex> g(t.mu);
+    for (auto &r : t.pending) {
+        if (hipEventSynchronize(r.b) != hipSuccess) return fail(SPKV_E_HIP, "timing_read: event wait failed");
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) return fail(SPKV_E_HIP, "timing_read: elapsed time failed");
+        t.total_ms[r.kernel] += ms;
+        t.count[r.kernel] += 1;
+        t.pool.push_back(r.a);
+        t.pool.push_back(r.b);
+    }
+    t.pending.clear();
+    *total_ms = t.total_ms[kernel];
+    *launches = t.count[kernel];
+    return SPKV_OK;
+}
+
+spkv_status spkv_timing_reset(void) {
+    Timing &t = timing();
+    std::lock_guard<std::mutex> g(t.mu);
+    for (auto &r : t.pending) {
+        (void)hipEventSynchronize(r.b);
+        t.pool.push_back(r.a);
+        t.pool.push_back(r.b);
+    }
+    t.pending.clear();
+    for (int k = 0; k < SPKV_NUM_KERNELS; ++k) {
+        t.total_ms[k] = 0;
+        t.count[k] = 0;
+    }
+    return SPKV_OK;
+}
+
+spkv_status spkv_device_cus(int32_t *cus_out) {
+    if (!cus_out) return fail(SPKV_E_INVAL, "device_cus: null out");
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(SPKV_E_HIP, "device_cus: no device");
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return fail(SPKV_E_HIP, "device_cus: attribute query failed");
+    *cus_out = n;
+    return SPKV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,303 @@
+// Host runtime: error state, batch validation, the per-call split plan and the
+// per-step dispatcher.
+//
+// Split plan: the static partition of Tangram's Algorithm 1 (Section 4.3),
+// applied to decode requests instead of head groups - a per-split budget
+// tau = max(1, ceil(total / target_items)) and max(1, ceil(len / tau)) splits
+// per request; here tau also has a floor (partial states cost traffic) and
+// the splits per row are capped (workspace bound).  Partials of every split
+// are combined by the log-sum-exp merge of the GraniKV paper's Eq. (1).
+//
+// Dispatcher: GraniKV paper, Section 3.6 - a thin per-step wrapper owning both
+// backends over the same pools decides from the step's realized batch
+// (M_eff = B_step * n_q/kv, its Eq. (2)) with a constant fitted to the GPU.
+// Here the decision is cascade vs flat per prefix group, from a cost model
+// whose constants are data.
+#include <algorithm>
+#include <cmath>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+namespace spkv {
+
+namespace {
+thread_local std::string g_last_error;
+}
+
+spkv_status fail(spkv_status code, const std::string &msg) {
+    g_last_error = msg;
+    return code;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+static int elem_bytes(int32_t dtype) { return dtype == SPKV_DTYPE_BF16 ? 2 : 4; }
+
+spkv_status validate_batch(const spkv_batch *b, const spkv_kv *kv) {
+    if (!b) return fail(SPKV_E_INVAL, "null batch");
+    if (b->batch < 0) return fail(SPKV_E_INVAL, "negative batch");
+    if (b->num_kv_heads < 1 || b->num_kv_heads > kMaxKvHeads) return fail(SPKV_E_INVAL, "num_kv_heads must be 1..16");
+    if (b->num_q_heads < b->num_kv_heads || b->num_q_heads % b->num_kv_heads)
+        return fail(SPKV_E_INVAL, "num_q_heads must be a multiple of num_kv_heads");
+    if (b->num_q_heads / b->num_kv_heads > kMaxGqa) return fail(SPKV_E_INVAL, "GQA group size must be <= 8");
+    if (b->head_dim != 64 && b->head_dim != 128) return fail(SPKV_E_INVAL, "head_dim must be 64 or 128");
+    if (b->dtype != SPKV_DTYPE_BF16 && b->dtype != SPKV_DTYPE_F32) return fail(SPKV_E_INVAL, "unknown dtype");
+    if (!std::isfinite(b->scale)) return fail(SPKV_E_INVAL, "scale must be finite");
+    if (b->num_groups < 0 || b->num_groups > kMaxGroups) return fail(SPKV_E_INVAL, "num_groups must be 0..512");
+    if (b->page_size < 1 || b->max_blocks < 0) return fail(SPKV_E_INVAL, "bad page_size/max_blocks");
+    const int B = b->batch, ng = b->num_groups;
+    if (B > 0 && (!b->q || !b->group_of || !b->cold_lens || !b->host_cold_lens))
+        return fail(SPKV_E_INVAL, "q, group_of, cold_lens and host_cold_lens are required");
+    if (B > 0 && b->max_blocks > 0 && !b->block_tables) return fail(SPKV_E_INVAL, "block_tables is required");
+    if (ng > 0 && (!b->group_indptr || !b->group_members || !b->hot_base || !b->hot_len ||
+                   !b->host_group_indptr || !b->host_hot_base || !b->host_hot_len))
+        return fail(SPKV_E_INVAL, "group arrays (device and host) are required when num_groups > 0");
+    if (ng > 0) {
+        if (b->host_group_indptr[0] != 0) return fail(SPKV_E_INVAL, "group_indptr[0] must be 0");
+        for (int g = 0; g < ng; ++g) {
+            if (b->host_group_indptr[g + 1] < b->host_group_indptr[g])
+                return fail(SPKV_E_INVAL, "group_indptr must be non-decreasing");
+            if (b->host_hot_len[g] < 0 || b->host_hot_base[g] < 0) return fail(SPKV_E_INVAL, "negative hot_base/hot_len");
+            if (kv && b->host_hot_base[g] + b->host_hot_len[g] > kv->hot_capacity)
+                return fail(SPKV_E_INVAL, "group " + std::to_string(g) + " slab exceeds the HOT capacity");
+        }
+        if (b->host_group_indptr[ng] > B) return fail(SPKV_E_INVAL, "more group members than requests");
+    }
+    const int64_t cap_tokens = (int64_t)b->max_blocks * b->page_size;
+    for (int i = 0; i < B; ++i) {
+        if (b->host_cold_lens[i] < 0 || b->host_cold_lens[i] > cap_tokens)
+            return fail(SPKV_E_INVAL, "cold_lens[" + std::to_string(i) + "] outside [0, max_blocks*page_size]");
+    }
+    if (kv) {
+        if (kv->hot_capacity < 0 || kv->cold_slots < 0) return fail(SPKV_E_INVAL, "negative pool size");
+        if (kv->hot_capacity * b->num_kv_heads >= (int64_t(1) << 31) || kv->cold_slots * b->num_kv_heads >= (int64_t(1) << 31))
+            return fail(SPKV_E_INVAL, "pools limited to 2^31 rows (slots x KV heads)");
+        if (B > 0 && kv->cold_slots > 0 && (!kv->k_cold || !kv->v_cold)) return fail(SPKV_E_INVAL, "null COLD pool");
+        if (ng > 0 && kv->hot_capacity > 0 && (!kv->k_hot || !kv->v_hot)) return fail(SPKV_E_INVAL, "null HOT pool");
+        if (kv->cold_slots % b->page_size) return fail(SPKV_E_INVAL, "cold_slots must be a multiple of page_size");
+    }
+    return SPKV_OK;
+}
+
+static inline bool mask_get(const GroupMask &m, int g) { return (m.bits[g >> 5] >> (g & 31)) & 1u; }
+
+spkv_status make_plan(const spkv_batch *b, const int32_t *cascade, int32_t num_cus, Plan *p) {
+    *p = Plan{};
+    const int B = b->batch, ng = b->num_groups, Hkv = b->num_kv_heads, D = b->head_dim;
+    const int G = b->num_q_heads / Hkv;
+    p->num_groups = ng;
+    for (int g = 0; g < ng; ++g)
+        if (!cascade || cascade[g]) p->cascade.bits[g >> 5] |= 1u << (g & 31);
+
+    // Member ids are device-only; sizing needs only per-group counts and
+    // lengths plus the COLD lengths.
+    const bool bf16 = b->dtype == SPKV_DTYPE_BF16;
+    int64_t flat_total = 0;
+    int64_t flat_max_len = 0;
+    for (int i = 0; i < B; ++i) {
+        flat_total += b->host_cold_lens[i];
+        flat_max_len = std::max<int64_t>(flat_max_len, b->host_cold_lens[i]);
+    }
+    int64_t prefix_work = 0;        // bf16: (row tiles x keys) units; f32: request-prefix tokens
+    int64_t max_m = 0, max_lp_c = 0;
+    for (int g = 0; g < ng; ++g) {
+        const int64_t n = b->host_group_indptr[g + 1] - b->host_group_indptr[g];
+        const int64_t lp = b->host_hot_len[g];
+        if (n == 0 || lp == 0) continue;
+        if (mask_get(p->cascade, g)) {
+            max_m = std::max<int64_t>(max_m, n * G);
+            max_lp_c = std::max<int64_t>(max_lp_c, lp);
+        } else {
+            flat_total += n * lp;
+        }
+    }
+    // Per-request maximum of the flat length: a dense-mode member carries Lp + Ls.
+    {
+        // Bound from the host lists: the longest COLD length plus the longest dense-mode Lp.
+        int64_t max_dense_lp = 0;
+        for (int g = 0; g < ng; ++g) {
+            const int64_t n = b->host_group_indptr[g + 1] - b->host_group_indptr[g];
+            if (n > 0 && !mask_get(p->cascade, g)) max_dense_lp = std::max<int64_t>(max_dense_lp, b->host_hot_len[g]);
+        }
+        flat_max_len += max_dense_lp;
+    }
+
+    // ---- flat pass --------------------------------------------------------
+    const int hpb = std::min(Hkv, 4);                 // KV heads (waves) per flat block
+    const int64_t blocks_per_item = (Hkv + hpb - 1) / hpb;
+    const int64_t target_items = std::max<int64_t>(1, (int64_t)num_cus * 8 / blocks_per_item);
+    int64_t tau = (flat_total + target_items - 1) / target_items;
+    tau = std::max<int64_t>(tau, 128);
+    tau = (tau + kFlatGranule - 1) / kFlatGranule * kFlatGranule;
+    p->flat_chunk = (int32_t)std::min<int64_t>(tau, 1 << 20);
+    // Every request's chunk is >= flat_chunk, so ceil(max_len / flat_chunk) (capped) bounds its splits.
+    p->flat_splits = std::min<int32_t>(kFlatSplitCap, splits_for(flat_max_len, p->flat_chunk));
+
+    // ---- prefix pass ------------------------------------------------------
+    p->prefix_as_flat = !bf16;
+    p->run_prefix = max_lp_c > 0;
+    if (p->run_prefix && bf16) {
+        int w = (int)std::min<int64_t>(4, (max_m + 31) / 32);
+        p->prefix_waves = std::max(1, w);
+        const int64_t mt = 32 * p->prefix_waves;
+        p->prefix_mtiles = (int32_t)((max_m + mt - 1) / mt);
+        for (int g = 0; g < ng; ++g) {
+            const int64_t n = b->host_group_indptr[g + 1] - b->host_group_indptr[g];
+            const int64_t lp = b->host_hot_len[g];
+            if (n == 0 || lp == 0 || !mask_get(p->cascade, g)) continue;
+            prefix_work += Hkv * ((n * G + mt - 1) / mt) * lp;
+        }
+        const int64_t target = std::max<int64_t>(1, (int64_t)num_cus * 2);
+        int64_t pt = (prefix_work + target - 1) / target;
+        pt = std::max<int64_t>(pt, 256);
+        pt = (pt + kPrefixKeyTile - 1) / kPrefixKeyTile * kPrefixKeyTile;
+        p->prefix_chunk = (int32_t)std::min<int64_t>(pt, 1 << 20);
+        p->prefix_splits = std::min<int32_t>(kPrefixSplitCap, splits_for(max_lp_c, p->prefix_chunk));
+    } else if (p->run_prefix) {
+        // float32: prefix part of cascade groups runs as a per-request pass over the slab.
+        int64_t total = 0;
+        for (int g = 0; g < ng; ++g) {
+            const int64_t n = b->host_group_indptr[g + 1] - b->host_group_indptr[g];
+            if (mask_get(p->cascade, g)) total += n * b->host_hot_len[g];
+        }
+        int64_t pt = (total + target_items - 1) / target_items;
+        pt = std::max<int64_t>(pt, 128);
+        pt = (pt + kFlatGranule - 1) / kFlatGranule * kFlatGranule;
+        p->prefix_chunk = (int32_t)std::min<int64_t>(pt, 1 << 20);
+        p->prefix_splits = std::min<int32_t>(kPrefixSplitCap, splits_for(max_lp_c, p->prefix_chunk));
+        p->prefix_waves = 0;
+        p->prefix_mtiles = 0;
+    }
+    p->splits_total = p->prefix_splits + p->flat_splits;
+
+    // Item counts (informational).
+    p->flat_items = 0;
+    p->prefix_items = 0;
+    for (int i = 0; i < B; ++i) {
+        // cascade members have only their COLD tokens in the flat pass; dense members add Lp,
+        // which the host cannot attribute without member ids, so count COLD-only here.
+        p->flat_items += splits_for(b->host_cold_lens[i], chunk_for(b->host_cold_lens[i], p->flat_chunk, kFlatSplitCap, kFlatGranule));
+    }
+    for (int g = 0; g < ng; ++g) {
+        const int64_t n = b->host_group_indptr[g + 1] - b->host_group_indptr[g];
+        const int64_t lp = b->host_hot_len[g];
+        if (n == 0 || lp == 0) continue;
+        if (mask_get(p->cascade, g)) {
+            if (bf16) {
+                const int64_t mt = 32 * p->prefix_waves;
+                p->prefix_items += Hkv * ((n * G + mt - 1) / mt) *
+                                   splits_for(lp, chunk_for(lp, p->prefix_chunk, kPrefixSplitCap, kPrefixKeyTile));
+            } else {
+                p->prefix_items += n * splits_for(lp, chunk_for(lp, p->prefix_chunk, kPrefixSplitCap, kFlatGranule));
+            }
+        } else {
+            p->flat_items += n * splits_for(lp, chunk_for(lp, p->flat_chunk, kFlatSplitCap, kFlatGranule));
+        }
+    }
+    const int64_t rows = (int64_t)B * b->num_q_heads;
+    p->ws_bytes = rows * p->splits_total * (int64_t)(D + 1) * 4 + 256;
+    (void)elem_bytes;
+    return SPKV_OK;
+}
+
+size_t workspace_bound(const spkv_batch *b) {
+    const int64_t rows = (int64_t)b->batch * b->num_q_heads;
+    return (size_t)(rows * (kPrefixSplitCap + kFlatSplitCap) * (int64_t)(b->head_dim + 1) * 4 + 256);
+}
+
+}  // namespace spkv
+
+using namespace spkv;
+
+extern "C" {
+
+const char *spkv_last_error(void) {
+    static thread_local std::string copy;
+    copy = spkv::g_last_error;
+    return copy.c_str();
+}
+
+const char *spkv_version(void) { return "spkv 0.1 (gfx950)"; }
+
+size_t spkv_workspace_size(const spkv_batch *batch) {
+    if (validate_batch(batch, nullptr) != SPKV_OK) return 0;
+    return workspace_bound(batch);
+}
+
+spkv_status spkv_plan_query(const spkv_batch *batch, const int32_t *cascade, spkv_plan_info *out) {
+    if (!out) return fail(SPKV_E_INVAL, "plan_query: null out");
+    spkv_status st = validate_batch(batch, nullptr);
+    if (st != SPKV_OK) return st;
+    Plan p;
+    st = make_plan(batch, cascade, kPlanCUs, &p);
+    if (st != SPKV_OK) return st;
+    out->flat_chunk = p.flat_chunk;
+    out->flat_splits = p.flat_splits;
+    out->prefix_chunk = p.prefix_chunk;
+    out->prefix_splits = p.prefix_splits;
+    out->prefix_waves = p.prefix_waves;
+    out->prefix_mtiles = p.prefix_mtiles;
+    out->flat_items = p.flat_items;
+    out->prefix_items = p.prefix_items;
+    out->workspace_bytes = p.ws_bytes;
+    return SPKV_OK;
+}
+
+void spkv_dispatch_params_default(spkv_dispatch_params *p) {
+    if (!p) return;
+    p->mode = SPKV_MODE_PER_GROUP;
+    p->min_group_requests = 2;
+    p->fixed_cost_us = 8.0;
+    p->flat_gbps = 4000.0;
+    p->prefix_gbps = 4000.0;
+    p->prefix_tflops = 400.0;
+}
+
+spkv_status spkv_dispatch(const spkv_batch *b, const spkv_dispatch_params *prm, int32_t *cascade_out) {
+    spkv_status st = validate_batch(b, nullptr);
+    if (st != SPKV_OK) return st;
+    if (!prm || (b->num_groups > 0 && !cascade_out)) return fail(SPKV_E_INVAL, "dispatch: null argument");
+    const int ng = b->num_groups;
+    const int G = b->num_q_heads / b->num_kv_heads;
+    const double kvb = 2.0 * b->num_kv_heads * b->head_dim * elem_bytes(b->dtype);
+    switch (prm->mode) {
+    case SPKV_MODE_FORCE_CASCADE:
+        for (int g = 0; g < ng; ++g) cascade_out[g] = 1;
+        return SPKV_OK;
+    case SPKV_MODE_FORCE_DENSE:
+        for (int g = 0; g < ng; ++g) cascade_out[g] = 0;
+        return SPKV_OK;
+    case SPKV_MODE_BATCH_GLOBAL: {
+        // One batch-wide shared level: only when every request shares group 0's prefix.
+        const bool all_one = ng == 1 && b->host_group_indptr[1] == b->batch && b->batch > 0;
+        for (int g = 0; g < ng; ++g) cascade_out[g] = all_one ? 1 : 0;
+        return SPKV_OK;
+    }
+    case SPKV_MODE_PER_GROUP:
+        break;
+    default:
+        return fail(SPKV_E_INVAL, "dispatch: unknown mode");
+    }
+    if (prm->flat_gbps <= 0 || prm->prefix_gbps <= 0 || prm->prefix_tflops <= 0)
+        return fail(SPKV_E_INVAL, "dispatch: rates must be positive");
+    for (int g = 0; g < ng; ++g) {
+        const int64_t n = b->host_group_indptr[g + 1] - b->host_group_indptr[g];
+        const double lp = (double)b->host_hot_len[g];
+        if (n < prm->min_group_requests || lp <= 0 || b->dtype != SPKV_DTYPE_BF16) {
+            cascade_out[g] = 0;
+            continue;
+        }
+        // Effective M of the group's prefix contraction (Eq. (2) per group).
+        const double m_eff = (double)n * G;
+        const double t_flat = n * lp * kvb / (prm->flat_gbps * 1e3);                    // us
+        const double t_bytes = lp * kvb / (prm->prefix_gbps * 1e3);
+        const double t_flops = 4.0 * m_eff * lp * b->head_dim * b->num_kv_heads / (prm->prefix_tflops * 1e6);
+        const double t_casc = std::max(t_bytes, t_flops) + prm->fixed_cost_us;
+        cascade_out[g] = t_casc < t_flat ? 1 : 0;
+    }
+    return SPKV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,208 @@
+"""HIP path vs the CPU oracle, through the C ABI (needs an MI355X).
+
+Allocator outputs (slots, copy-on-write pairs, block tables) and pool
+contents are compared bit for bit; attention outputs within the fp32 bound
+(max abs 2e-3) plus tighter LSE / relative-error discriminators.
+"""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle.attention import decode_reference
+from oracle.driver import run_single_step
+from shared_prefix_paged_amd import runtime as R
+from shared_prefix_paged_amd import _abi as A
+from hip_setup import setup_single_step, errors, pool_bytes
+
+pytestmark = pytest.mark.gpu
+
+TOL_O, TOL_LSE, TOL_REL = 2e-3, 1e-3, 1e-2
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def small_cases():
+    return {
+        "c0": lambda: W.make_workload(W.CONFIGS["C0"]),
+        "bf16_d128_g4_multi": lambda: W.make_custom(
+            batch=7, num_q_heads=8, num_kv_heads=2, head_dim=128, dtype="bf16", group_prefix_len=[40, 17],
+            group_of=[0, 0, 1, -1, 1, 0, 1], suffix_len=[5, 1, 33, 9, 16, 17, 2], seed=11),
+        "bf16_d64_g2": lambda: W.make_custom(
+            batch=5, num_q_heads=6, num_kv_heads=3, head_dim=64, dtype="bf16", group_prefix_len=[129],
+            group_of=[0, 0, 0, 0, 0], suffix_len=[1, 64, 65, 200, 3], seed=12),
+        "bf16_d128_g5_tail": lambda: W.make_custom(
+            batch=9, num_q_heads=10, num_kv_heads=2, head_dim=128, dtype="bf16", group_prefix_len=[300],
+            group_of=[0] * 9, suffix_len=[7, 300, 1, 45, 130, 2, 99, 64, 17], seed=13),
+        "bf16_d128_g8": lambda: W.make_custom(
+            batch=6, num_q_heads=8, num_kv_heads=1, head_dim=128, dtype="bf16", group_prefix_len=[77, 500],
+            group_of=[1, 1, 0, 1, 0, -1], suffix_len=[3, 8, 1, 250, 31, 12], seed=14),
+        "bf16_d128_mha": lambda: W.make_custom(
+            batch=4, num_q_heads=4, num_kv_heads=4, head_dim=128, dtype="bf16", group_prefix_len=[64],
+            group_of=[0, 0, 0, 0], suffix_len=[9, 10, 11, 12], seed=15),
+        "f32_d128_g3": lambda: W.make_custom(
+            batch=5, num_q_heads=6, num_kv_heads=2, head_dim=128, dtype="f32", group_prefix_len=[90],
+            group_of=[0, 0, -1, 0, 0], suffix_len=[4, 70, 5, 1, 33], seed=16),
+        "bf16_many_tiles": lambda: W.make_custom(
+            batch=40, num_q_heads=32, num_kv_heads=8, head_dim=128, dtype="bf16", group_prefix_len=[1000],
+            group_of=[0] * 40, suffix_len=list(np.random.default_rng(5).integers(1, 3000, 40)), seed=17),
+        "bf16_hkv16": lambda: W.make_custom(
+            batch=3, num_q_heads=16, num_kv_heads=16, head_dim=64, dtype="bf16", group_prefix_len=[33],
+            group_of=[0, 0, 0], suffix_len=[5, 6, 400], seed=18),
+    }
+
+
+CASES = small_cases()
+
+
+@pytest.fixture(scope="module", params=sorted(CASES))
+def case(request):
+    note(f"[setup] case={request.param}")
+    wl = CASES[request.param]()
+    ref = decode_reference(wl)
+    return request.param, wl, ref
+
+
+def test_allocator_outputs_bit_exact(case):
+    name, wl, _ = case
+    st_o = run_single_step(wl, with_mirror=False)
+    note(f"[gpu] setup {name}")
+    st = setup_single_step(wl)
+    torch.cuda.synchronize()
+    assert list(st.setup_slots) == st_o.setup_slots
+    assert list(st.step_slots) == st_o.step_slots
+    assert st.step_cows == st_o.step_cows
+    assert st.bases == st_o.bases
+    for b in range(wl.batch):
+        n = len(st_o.tables[b])
+        assert list(st.tables[b, :n]) == st_o.tables[b] and np.all(st.tables[b, n:] == -1)
+        assert st.lens[b] == st_o.lens[b]
+    assert st.cold.state() == st_o.cold.state()
+    assert st.hot.state() == st_o.hot.state()
+
+
+def test_pools_byte_exact(case):
+    name, wl, _ = case
+    st_o = run_single_step(wl)
+    note(f"[gpu] pools {name}")
+    st = setup_single_step(wl)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(pool_bytes(st.pools.k_hot)[:st_o.mirror.k_hot.size], st_o.mirror.k_hot)
+    np.testing.assert_array_equal(pool_bytes(st.pools.v_hot)[:st_o.mirror.v_hot.size], st_o.mirror.v_hot)
+    np.testing.assert_array_equal(pool_bytes(st.pools.k_cold), st_o.mirror.k_cold)
+    np.testing.assert_array_equal(pool_bytes(st.pools.v_cold), st_o.mirror.v_cold)
+
+
+@pytest.mark.parametrize("mode", ["cascade", "dense", "step_per_group", "step_batch_global"])
+def test_attention_matches_oracle(case, mode):
+    name, wl, (ref_o, ref_l) = case
+    note(f"[gpu] attention {name} {mode}")
+    st = setup_single_step(wl)
+    ws = R.workspace(st.batch)
+    if mode == "cascade":
+        out, lse = R.cascade_decode(st.batch, st.pools, ws)
+    elif mode == "dense":
+        out, lse = R.dense_decode(st.batch, st.pools, ws)
+    else:
+        m = A.SPKV_MODE_PER_GROUP if mode == "step_per_group" else A.SPKV_MODE_BATCH_GLOBAL
+        out, lse, _ = R.decode_step(st.batch, st.pools, R.default_params(m), ws)
+    torch.cuda.synchronize()
+    e_o, e_l, rel = errors(out, lse, ref_o, ref_l)
+    note(f"    max_abs={e_o:.3e} lse={e_l:.3e} rel={rel:.3e}")
+    assert e_o <= TOL_O and e_l <= TOL_LSE and rel <= TOL_REL
+
+
+def test_cascade_deterministic(case):
+    name, wl, _ = case
+    note(f"[gpu] determinism {name}")
+    st = setup_single_step(wl)
+    ws = R.workspace(st.batch)
+    o1, l1 = R.cascade_decode(st.batch, st.pools, ws)
+    o1, l1 = o1.clone(), l1.clone()
+    o2, l2 = R.cascade_decode(st.batch, st.pools, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_page_size_16_and_reshuffle_match():
+    wl = CASES["bf16_d128_g4_multi"]()
+    ref_o, ref_l = decode_reference(wl)
+    outs = []
+    for P, fo in [(1, None), (16, None), (16, "perm"), (4, "perm")]:
+        w = W.make_custom(batch=7, num_q_heads=8, num_kv_heads=2, head_dim=128, dtype="bf16",
+                          group_prefix_len=[40, 17], group_of=[0, 0, 1, -1, 1, 0, 1],
+                          suffix_len=[5, 1, 33, 9, 16, 17, 2], seed=11, page_size=P)
+        order = None if fo is None else np.random.default_rng(P).permutation(w.num_cold_pages).astype(np.int32)
+        note(f"[gpu] page size {P} order={fo}")
+        st = setup_single_step(w, page_size=P, free_order=order)
+        ws = R.workspace(st.batch)
+        out, lse = R.cascade_decode(st.batch, st.pools, ws)
+        torch.cuda.synchronize()
+        e_o, e_l, _ = errors(out, lse, ref_o, ref_l)
+        assert e_o <= TOL_O and e_l <= TOL_LSE
+        outs.append(out.cpu())
+    # the same logical tokens in a different physical order give the same reduction order here
+    for o in outs[1:]:
+        assert torch.allclose(o, outs[0], atol=1e-6, rtol=0)
+
+
+def test_merge_states_kernel():
+    rng = np.random.default_rng(4)
+    rows, d = 37, 128
+    oa, ob = rng.standard_normal((rows, d)), rng.standard_normal((rows, d))
+    la, lb = rng.standard_normal(rows) * 3, rng.standard_normal(rows) * 3
+    la[3] = -np.inf
+    la[5] = lb[5] = -np.inf
+    from oracle.attention import merge
+    ro, rl = merge(oa, la, ob, lb)
+    t = lambda x: torch.tensor(x, dtype=torch.float32, device="cuda")
+    note("[gpu] merge_states")
+    o, l = R.merge_states(t(oa), t(la), t(ob), t(lb))
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(o.cpu().numpy(), ro, atol=1e-5)
+    lg = l.cpu().numpy()
+    assert np.isneginf(lg[5]) and np.allclose(lg[np.isfinite(rl)], rl[np.isfinite(rl)], atol=1e-5)
+
+
+def test_empty_batch_and_no_groups():
+    wl = W.make_custom(batch=3, num_q_heads=4, num_kv_heads=1, head_dim=64, dtype="bf16", group_prefix_len=[],
+                       group_of=[-1, -1, -1], suffix_len=[1, 2, 300], seed=21)
+    ref_o, ref_l = decode_reference(wl)
+    note("[gpu] no groups")
+    st = setup_single_step(wl)
+    ws = R.workspace(st.batch)
+    out, lse = R.cascade_decode(st.batch, st.pools, ws)
+    torch.cuda.synchronize()
+    e_o, e_l, _ = errors(out, lse, ref_o, ref_l)
+    assert e_o <= TOL_O and e_l <= TOL_LSE
+
+
+# ---------------------------------------------------------------- full-size configs (sampled rows)
+
+def full_size(name, **kw):
+    return W.make_workload(W.CONFIGS[name], **kw)
+
+
+@pytest.mark.parametrize("name,lp", [("C1", None), ("C2", None), ("C3", 4096), ("C3", 32768)])
+def test_full_size_sampled(name, lp):
+    wl = full_size(name, prefix_len=lp)
+    rng = np.random.default_rng(0)
+    rows = sorted({0, wl.batch - 1, *rng.integers(0, wl.batch, 3).tolist()})
+    ref_o, ref_l = decode_reference(wl, rows=rows)
+    note(f"[gpu] full size {name} lp={lp} rows={rows}")
+    st = setup_single_step(wl)
+    ws = R.workspace(st.batch)
+    for fn in (R.cascade_decode, R.dense_decode):
+        out, lse = fn(st.batch, st.pools, ws)
+        torch.cuda.synchronize()
+        e_o, e_l, rel = errors(out, lse, ref_o, ref_l, rows=rows)
+        note(f"    {fn.__name__}: max_abs={e_o:.3e} lse={e_l:.3e} rel={rel:.3e}")
+        assert e_o <= TOL_O and e_l <= TOL_LSE and rel <= TOL_REL
+        # closed-form property at any size: every output row is a convex combination of V rows
+        assert torch.isfinite(out).all() and torch.isfinite(lse).all()
