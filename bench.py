@@ -1,0 +1,275 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of HOT/COLD cascade attention on one MI355X.
+
+One step = the whole hot path over one batch: one COLD append per request
+(host allocator), upload of the slot mapping, copy-on-write page copies (none
+without forks), reshape_and_cache of the step's K/V, device block-table
+append, per-step dispatch, then cascade attention (bf16 MFMA prefix
+contraction over the HOT slab, paged suffix pass over COLD, log-sum-exp
+merge).  Inputs are seeded synthetic tensors already resident in HBM.
+
+Default workload: the Llama-3.1-8B-shaped layer (B = 64, Hq = 32, Hkv = 8,
+d = 128, bf16, Lp = 16384, Ls ~ U[256, 2048] growing by one token per step,
+COLD page size 1 with shuffled slots).
+
+Prints one JSON line.  ``--gpus N`` with N > 1 is refused: this build runs on
+one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+sys.path.insert(0, os.path.join(ROOT, "tests"))
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+METRIC = "cascade decode-attn KV-tokens/s per step + % HBM roofline, Lp=16K 8B shape"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="C1", choices=["C0", "C1", "C2", "C3", "C4"])
+    ap.add_argument("--lp", type=int, default=None, help="override the prefix length (C3 sweep)")
+    ap.add_argument("--mode", default="step", choices=["step", "cascade", "dense"],
+                    help="step: dispatcher decides (default); cascade/dense: force a backend")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle timing sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def kv_bytes_per_token(hkv, d, esz):
+    return 2 * hkv * d * esz
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
+              "this build has no multi-GPU path.", file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    import workloads as W
+    from shared_prefix_paged_amd import runtime as R
+    from shared_prefix_paged_amd import _abi as A
+    from hip_setup import setup_single_step, to_device
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    cfg = W.CONFIGS[args.config]
+    total_steps = args.warmup + 2 * args.steps + 1
+    wl = W.make_workload(cfg, prefix_len=args.lp, extra_steps=max(32, total_steps + 1))
+    cfg = wl.cfg
+    B, Hq, Hkv, d, P = wl.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.page_size
+    esz = 2 if cfg.dtype == "bf16" else 4
+    kvb = kv_bytes_per_token(Hkv, d, esz)
+    max_len0 = int(wl.suffix_len.max())
+    st = setup_single_step(wl, device=dev, max_blocks=(max_len0 + total_steps + P - 1) // P + 1)
+    batch, pools, cold = st.batch, st.pools, st.cold
+    mb = batch.max_blocks
+    print(f"[bench] {cfg.name}: B={B} Hq={Hq} Hkv={Hkv} d={d} {cfg.dtype} Lp={list(wl.group_prefix_len)} "
+          f"sum(Ls)={int(wl.suffix_len.sum())} P={P}", file=sys.stderr, flush=True)
+
+    # Per-step inputs (fresh K/V of the decoded token, fresh Q), resident on the device.
+    k_steps, v_steps, q_steps = [], [], []
+    for s in range(total_steps):
+        dr = W.step_draws(cfg, s, B)
+        k_steps.append(to_device(dr.k_new, cfg.dtype, dev))
+        v_steps.append(to_device(dr.v_new, cfg.dtype, dev))
+        q_steps.append(to_device(dr.q, cfg.dtype, dev))
+    slots_pin = torch.zeros((total_steps, B), dtype=torch.int32).pin_memory()
+    slots_dev = torch.zeros((total_steps, B), dtype=torch.int32, device=dev)
+    rows_dev = torch.arange(B, dtype=torch.int32, device=dev)
+    seqs = np.asarray(st.seqs, dtype=np.int32)
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    ws = torch.empty(batch.workspace_size(), dtype=torch.uint8, device=dev)
+    mode = {"step": A.SPKV_MODE_PER_GROUP, "cascade": A.SPKV_MODE_FORCE_CASCADE,
+            "dense": A.SPKV_MODE_FORCE_DENSE}[args.mode]
+    params = R.default_params(mode)
+    lp_of = np.array([wl.prefix_len_of(b) for b in range(B)], dtype=np.int64)
+    state = {"i": 0, "choice": None}
+
+    def one_step():
+        i = state["i"]
+        slots, cows = cold.append_batch(seqs)                       # host allocator
+        slots_pin[i].copy_(torch.from_numpy(slots))
+        slots_dev[i].copy_(slots_pin[i], non_blocking=True)         # slot mapping upload
+        if cows:
+            R.copy_blocks(torch.tensor(cows, dtype=torch.int32, device=dev), pools.k_cold, pools.v_cold,
+                          cold.num_pages, P, Hkv, d)
+        R.reshape_and_cache(k_steps[i], v_steps[i], slots_dev[i], pools.k_cold, pools.v_cold, pools.cold_slots,
+                            Hkv, d)
+        R.block_table_append(batch.tables, mb, batch.lens, rows_dev, slots_dev[i], P)
+        batch.lens_h += 1                                            # host mirror of the lengths
+        batch.struct.q = q_steps[i].data_ptr()
+        _, _, choice = R.decode_step(batch, pools, params, ws, out, lse)
+        state["choice"] = choice
+        state["i"] = i + 1
+        return int(np.sum(lp_of + batch.lens_h))                     # logical KV tokens attended
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly `steps` steps --------------------------------
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    tokens = 0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        tokens += one_step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = 1e3 * wall / args.steps
+    value = tokens / wall
+
+    # ---- per-kernel durations from HIP events on the launch stream ----------
+    lens_before = batch.lens_h.copy()
+    with R.KernelTimer() as kt:
+        tok2 = 0
+        for _ in range(args.steps):
+            tok2 += one_step()
+        torch.cuda.synchronize()
+    kt_ms = {k: kt.read(k) for k in (A.SPKV_KERNEL_PREFIX, A.SPKV_KERNEL_FLAT, A.SPKV_KERNEL_MERGE,
+                                     A.SPKV_KERNEL_CACHE)}
+    choice = state["choice"]
+    cascade = bool(len(choice) and choice[0])
+    plan = batch.plan(list(map(int, choice)) if len(choice) else None)
+
+    # Algorithmic bytes / FLOPs of one launch, averaged over the profiled steps
+    # (the lengths grow by one token per step).
+    def chunk_for(n, tau, cap, gran):
+        c = max(tau, -(-n // cap))
+        return -(-c // gran) * gran
+
+    def splits_for(n, c):
+        return 0 if n <= 0 else -(-n // c)
+
+    rows = B * Hq
+    steps_lens = [lens_before + j + 1 for j in range(args.steps)]
+    lp_dense = np.zeros(B, np.int64) if cascade else lp_of
+    flat_bytes, flat_partial_bytes = [], 0.0
+    for L in steps_lens:
+        Lf = L + lp_dense
+        nf = sum(splits_for(int(x), chunk_for(int(x), plan.flat_chunk, plan.flat_split_cap, plan.flat_granule))
+                 for x in Lf)
+        flat_bytes.append(int(Lf.sum()) * kvb + 4 * int(np.sum(-(-L // P))) + rows * d * esz
+                          + Hq * nf * (d + 1) * 4)
+        flat_partial_bytes += Hq * nf * (d + 1) * 4 / len(steps_lens)
+    flat_bytes = float(np.mean(flat_bytes))
+    prefix_partial_bytes = 0.0
+    groups = [(int(lp), int(np.sum(wl.group_of == g))) for g, lp in enumerate(wl.group_prefix_len)]
+    prefix_bytes = prefix_flops = 0.0
+    if cascade:
+        for lp, n in groups:
+            npf = splits_for(lp, chunk_for(lp, plan.prefix_chunk, plan.prefix_split_cap, plan.prefix_granule))
+            prefix_bytes += lp * kvb + n * Hq * d * esz + n * Hq * npf * (d + 1) * 4
+            prefix_partial_bytes += n * Hq * npf * (d + 1) * 4
+            prefix_flops += 4.0 * n * Hq * lp * d
+    # merge: reads every partial state written by the two passes, writes O and LSE
+    merge_bytes = (flat_partial_bytes + prefix_partial_bytes) + rows * (d + 1) * 4
+
+    kernels = {}
+    for name, kid, nbytes, flops in (("prefix_mfma", A.SPKV_KERNEL_PREFIX, prefix_bytes, prefix_flops),
+                                     ("flat_paged", A.SPKV_KERNEL_FLAT, flat_bytes, 0.0),
+                                     ("merge", A.SPKV_KERNEL_MERGE, merge_bytes, 0.0)):
+        ms, n = kt_ms[kid]
+        if n == 0:
+            continue
+        avg_us = 1e3 * ms / n
+        kernels[name] = {"avg_us": round(avg_us, 3), "launches": n,
+                         "alg_bytes": int(nbytes), "gbps": round(nbytes / avg_us / 1e3, 1)}
+        if flops:
+            kernels[name]["tflops"] = round(flops / avg_us / 1e6, 2)
+            kernels[name]["mfma_frac"] = round(flops / avg_us / 1e6 / BF16_PEAK_TFLOPS, 4)
+    dom = max(kernels, key=lambda k: kernels[k]["avg_us"])
+    dk = kernels[dom]
+    if dom == "prefix_mfma" and prefix_flops / (dk["avg_us"] * 1e6) / BF16_PEAK_TFLOPS > \
+            (prefix_bytes / dk["avg_us"] / 1e3) / HBM_PEAK_GBPS:
+        roofline = {"bound": "mfma", "achieved": dk["tflops"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(dk["tflops"] / BF16_PEAK_TFLOPS, 4), "traffic": None}
+    else:
+        roofline = {"bound": "hbm", "achieved": dk["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(dk["gbps"] / HBM_PEAK_GBPS, 4), "traffic": None}
+    roofline["kernel"] = dom
+    attn_us = sum(k["avg_us"] for k in kernels.values())
+
+    # ---- oracle on the host cores, bounded sample ---------------------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "KV-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: one decode step, B={B}, Hq={Hq}, Hkv={Hkv}, d={d}, {cfg.dtype}, "
+                        f"Lp={list(map(int, wl.group_prefix_len))}, Ls~U{list(cfg.suffix_range)} (+1 per step), "
+                        f"COLD page size {P}, shuffled slots",
+            "batch": B, "prefix_len": [int(x) for x in wl.group_prefix_len], "page_size": P,
+            "backend": ("cascade" if cascade else "dense"), "mode": args.mode,
+        },
+        "gpu_ms_per_step": round(gpu_ms / args.steps, 4),
+        "attention_us_per_step": round(attn_us, 2),
+        "kv_tokens_per_s_attention": round(tokens / args.steps / (attn_us * 1e-6), 1),
+        "kernels": kernels,
+        "plan": {f: int(getattr(plan, f)) for f, _ in plan._fields_},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def cpu_baseline(wl, budget_s: float):
+    """The oracle, untuned, on the host cores: fp64 attention per request until the budget is spent."""
+    import numpy as np
+    from oracle.attention import decode_reference
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    cores = min(threads, len(os.sched_getaffinity(0)))
+    done, tokens, t0 = 0, 0, time.perf_counter()
+    order = list(range(wl.batch))
+    while done < len(order) and time.perf_counter() - t0 < budget_s:
+        b = order[done]
+        decode_reference(wl, rows=[b])
+        tokens += wl.prefix_len_of(b) + int(wl.suffix_len[b])
+        done += 1
+    el = time.perf_counter() - t0
+    return {"value": round(tokens / el, 1), "unit": "KV-tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} of {wl.batch} requests of the same workload (all query heads, "
+                      f"prefix + suffix), fp64 numpy, {el:.1f} s"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

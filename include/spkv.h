@@ -188,6 +188,18 @@ spkv_status spkv_copy_blocks(const int32_t *pairs, int32_t n, void *k_cold, void
                              int32_t num_pages, int32_t page_size,
                              int32_t num_kv_heads, int32_t head_dim, int32_t dtype, void *stream);
 
+/* Device-side mirror of one append per request ([PKV] How it works, steps 2
+ * and 3: the new token's page enters the block table the attention kernel
+ * reads).  For i in 0..n-1 with r = rows[i]:
+ *     tables[r * max_blocks + lens[r] / P] = slots[i] / P;  lens[r] += 1
+ * which covers a fresh page, a copy-on-write replacement and an append into
+ * the current page alike.  tables, lens, rows and slots are device memory;
+ * rows must be distinct within one call.  Rows outside [0, num_rows) and
+ * entries that would land beyond max_blocks are skipped. */
+spkv_status spkv_block_table_append(int32_t *tables, int32_t max_blocks, int32_t *lens, int32_t num_rows,
+                                    const int32_t *rows, const int32_t *slots, int32_t n, int32_t page_size,
+                                    void *stream);
+
 /* ======================================================================
  * Decode attention.
  * ==================================================================== */
@@ -306,6 +318,10 @@ typedef struct spkv_plan_info {
     int64_t flat_items;            /* non-empty flat work items */
     int64_t prefix_items;          /* non-empty prefix work items */
     int64_t workspace_bytes;       /* bytes this plan uses */
+    int32_t flat_split_cap;        /* per request: chunk = roundup(max(flat_chunk, ceil(L / cap)), granule) */
+    int32_t flat_granule;
+    int32_t prefix_split_cap;      /* per group: same rule with prefix_chunk */
+    int32_t prefix_granule;
 } spkv_plan_info;
 
 /* Plan the launch for a given per-group choice (host [ng]; NULL = all cascade). */

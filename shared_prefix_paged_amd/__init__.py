@@ -24,7 +24,7 @@ except ImportError:  # host-only use (allocators) works without torch
 
 _LIB_PATH = _os.path.join(_os.path.dirname(_os.path.abspath(__file__)), "libspkv.so")
 if not _os.path.exists(_LIB_PATH):
-    raise ImportError(f"{_LIB_PATH} is not built; run `python -m shared_prefix_paged_amd.build` "
+    raise ImportError(f"{_LIB_PATH} is not built; run `python shared_prefix_paged_amd/build.py` "
                       "(or __graft_entry__.build()) first")
 lib = _C.CDLL(_LIB_PATH)
 _abi.declare(lib)

@@ -45,7 +45,8 @@ class spkv_dispatch_params(C.Structure):
 class spkv_plan_info(C.Structure):
     _fields_ = [("flat_chunk", c_i32), ("flat_splits", c_i32), ("prefix_chunk", c_i32), ("prefix_splits", c_i32),
                 ("prefix_waves", c_i32), ("prefix_mtiles", c_i32), ("flat_items", c_i64),
-                ("prefix_items", c_i64), ("workspace_bytes", c_i64)]
+                ("prefix_items", c_i64), ("workspace_bytes", c_i64), ("flat_split_cap", c_i32),
+                ("flat_granule", c_i32), ("prefix_split_cap", c_i32), ("prefix_granule", c_i32)]
 
 
 P_batch, P_kv, P_params = C.POINTER(spkv_batch), C.POINTER(spkv_kv), C.POINTER(spkv_dispatch_params)
@@ -77,6 +78,7 @@ SIGNATURES = {
     "spkv_hot_write": (c_i32, [c_vp, c_vp, c_i64, c_i64, c_vp, c_vp, c_i64, c_i32, c_i32, c_i32, c_vp]),
     "spkv_reshape_and_cache": (c_i32, [c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i64, c_i32, c_i32, c_i32, c_vp]),
     "spkv_copy_blocks": (c_i32, [c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp]),
+    "spkv_block_table_append": (c_i32, [c_vp, c_i32, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_vp]),
     "spkv_workspace_size": (c_sz, [P_batch]),
     "spkv_cascade_decode": (c_i32, [P_batch, P_kv, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "spkv_dense_decode": (c_i32, [P_batch, P_kv, c_vp, c_vp, c_vp, c_sz, c_vp]),

@@ -1,6 +1,6 @@
 """Builds libspkv.so for gfx950 in-tree.
 
-    python -m shared_prefix_paged_amd.build        (or: python shared_prefix_paged_amd/build.py)
+    python shared_prefix_paged_amd/build.py   (runs without importing the package)
 
 Host sources are compiled with g++ (no HIP dependency); the HIP sources with
 hipcc for gfx950 only, with packed-fp32 code generation disabled; everything

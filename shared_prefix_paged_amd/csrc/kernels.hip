@@ -662,6 +662,20 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(const int32_t *pairs, 
     }
 }
 
+__global__ __launch_bounds__(256) void block_table_append_kernel(int32_t *tables, int max_blocks, int32_t *lens,
+                                                                 int num_rows, const int32_t *rows,
+                                                                 const int32_t *slots, int n, int page_size) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const int r = rows[i];
+    if (r < 0 || r >= num_rows) return;
+    const int len = lens[r];
+    const int blk = len / page_size;
+    if (len < 0 || blk >= max_blocks) return;
+    tables[(int64_t)r * max_blocks + blk] = slots[i] / page_size;
+    lens[r] = len + 1;
+}
+
 // ---------------------------------------------------------------------------
 // Launch plumbing and optional per-launch timing.
 // ---------------------------------------------------------------------------
@@ -892,6 +906,18 @@ spkv_status spkv_copy_blocks(const int32_t *pairs, int32_t n, void *k_cold, void
     copy_blocks_kernel<<<dim3(gx, (unsigned)n), 256, 0, (hipStream_t)stream>>>(pairs, (u32x4_t *)k_cold,
                                                                                 (u32x4_t *)v_cold, num_pages, ppp);
     return check_launch("copy_blocks_kernel");
+}
+
+spkv_status spkv_block_table_append(int32_t *tables, int32_t max_blocks, int32_t *lens, int32_t num_rows,
+                                    const int32_t *rows, const int32_t *slots, int32_t n, int32_t page_size,
+                                    void *stream) {
+    if (n < 0 || max_blocks < 0 || num_rows < 0 || page_size < 1) return fail(SPKV_E_INVAL, "block_table_append: bad size");
+    if (n == 0) return SPKV_OK;
+    if (!tables || !lens || !rows || !slots) return fail(SPKV_E_INVAL, "block_table_append: null pointer");
+    TimedLaunch tl(SPKV_KERNEL_CACHE, (hipStream_t)stream);
+    block_table_append_kernel<<<(unsigned)((n + 255) / 256), 256, 0, (hipStream_t)stream>>>(
+        tables, max_blocks, lens, num_rows, rows, slots, n, page_size);
+    return check_launch("block_table_append_kernel");
 }
 
 spkv_status spkv_cascade_decode(const spkv_batch *batch, const spkv_kv *kv, float *out, float *lse, void *ws,

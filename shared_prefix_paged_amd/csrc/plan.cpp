@@ -242,6 +242,10 @@ spkv_status spkv_plan_query(const spkv_batch *batch, const int32_t *cascade, spk
     out->flat_items = p.flat_items;
     out->prefix_items = p.prefix_items;
     out->workspace_bytes = p.ws_bytes;
+    out->flat_split_cap = kFlatSplitCap;
+    out->flat_granule = kFlatGranule;
+    out->prefix_split_cap = kPrefixSplitCap;
+    out->prefix_granule = p.prefix_as_flat ? kFlatGranule : kPrefixKeyTile;
     return SPKV_OK;
 }
 

@@ -218,6 +218,12 @@ def copy_blocks(pairs, k_cold, v_cold, num_pages: int, page_size: int, num_kv_he
                                stream_handle(stream)))
 
 
+def block_table_append(tables, max_blocks: int, lens, rows, slots, page_size: int, stream=None):
+    """Device tables/lens follow one append per listed row (spkv_block_table_append)."""
+    check(lib.spkv_block_table_append(_dp(tables), int(max_blocks), _dp(lens), int(lens.numel()), _dp(rows),
+                                      _dp(slots), int(rows.numel()), int(page_size), stream_handle(stream)))
+
+
 class KVPools:
     """Caller-owned device pools; ``struct`` is the spkv_kv describing them."""
 
