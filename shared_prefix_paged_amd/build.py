@@ -53,6 +53,8 @@ def build(verbose: bool = False) -> str:
         obj = os.path.join(BUILD, src + ".o")
         _run([hipcc, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}",
               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+              # MFMA accumulators in ordinary VGPRs: the softmax rescales them in place
+              "-mllvm", "-amdgpu-mfma-vgpr-form=1",
               "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     tmp = LIB + ".tmp"

@@ -27,6 +27,7 @@ constexpr int kFlatSplitCap = 64;      // partials per row from the flat pass
 constexpr int kPrefixSplitCap = 64;    // partials per row from the prefix pass
 constexpr int kPrefixKeyTile = 32;     // keys per MFMA tile in the prefix kernel
 constexpr int kFlatGranule = 16;       // flat chunks are multiples of this many tokens
+constexpr int kSplitPBelow = 256;      // prefixes shorter than this carry P as bf16 hi + lo
 
 // Per-group cascade bitmask passed to kernels by value.
 struct GroupMask {
@@ -48,6 +49,7 @@ struct Plan {
     int64_t prefix_items;
     int64_t ws_bytes;
     bool run_prefix;          // some cascade group has Lp > 0 (bf16)
+    bool prefix_split_p;      // some cascade group is short: carry P as bf16 hi + lo
     bool prefix_as_flat;      // float32 pools: prefix part via a per-request pass
 };
 

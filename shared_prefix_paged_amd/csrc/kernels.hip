@@ -337,25 +337,93 @@ __global__ __launch_bounds__(256) void flat_kernel(Args a, int part) {
 // member-major: row = member * G + head-in-group).  Per 32-key tile:
 //   S^T[key, row] = K_tile . Q^T   (A = K rows from LDS, B = Q in registers)
 //   online softmax along keys: each lane holds one query row's 16 scores
-//   O^T[d, row]  += V_tile^T . P^T (A = V columns from LDS, B = P from the
-//                                    S^T accumulators, converted to bf16)
+//   O^T[d, row]  += V_tile^T . P^T (A = V from LDS by transposing reads,
+//                                    B = P from the S^T accumulators in bf16)
 // MFMA 32x32 operand layout: A[m][k] lives in lane m + 32*(k/8), element
 // k%8; B[k][n] in lane n + 32*(k/8); D[m][n] in lane n + 32*((m/4)%2),
-// register (m/8)*4 + m%4.  K rows are stored in LDS with bits 2 and 3 of the
-// key index swapped, so that accumulator register j of lane l holds key
-// 16*(j/8) + 8*(l/32) + j%8: the P operand for PV is then registers
-// 8*kb .. 8*kb+7 as they stand.  V is read from LDS as NDB = D/32 adjacent
-// columns per key; output row (d) m of block db is column NDB*m + db.
+// register (m/8)*4 + m%4.  K rows are placed in LDS with bits 2 and 3 of the
+// key index swapped, so accumulator register j of lane l holds key
+// 16*(j/8) + 8*(l/32) + j%8, and registers 8*kb..8*kb+7 are already the P
+// operand of the kb-th 16-key step.
+//
+// K/V tiles stream through a ring of LDS stages filled by global->LDS DMA
+// (global_load_lds_dwordx4: lane l of a wave-wide load lands at base + 16*l),
+// several tiles ahead of the MFMAs.  The 16-byte chunks of each LDS row are
+// XOR-swizzled by row so that the K reads (16 B, 32 rows) and the transposing
+// V reads (ds_read_b64_tr_b16: within 16 lanes, lane i receives element e of
+// the 4x16-bit chunk addressed by lane 4e + i/4, component i%4) hit distinct
+// banks.
 // ---------------------------------------------------------------------------
-template <int D, int W>
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char_t;
+
+__device__ __forceinline__ uint32_t lds_offset(const void *p) {
+    return (uint32_t)(uintptr_t)(const lds_char_t *)p;
+}
+
+// One wave-wide global->LDS copy: this lane's 16 bytes (at gbase + voff) land
+// at lds_base + 16 * lane.  gbase and lds_base must be wave-uniform.  M0 (the
+// LDS base of the copy) is saved and restored around the instruction; the
+// s_nop covers the M0-write hazard.
+__device__ __forceinline__ void dma16(const void *gbase, uint32_t voff, uint32_t lds_base) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(gbase), "s"(lds_base)
+        : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ int swap_bits23(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
+
+// V tile chunk placement.  Logical 16-byte chunk c of LDS row r sits at
+// physical chunk vchunk_phys(r, c); the transposing reads of one 16-lane group
+// touch 4 consecutive rows x one 32-byte chunk pair, and the two groups read
+// in the same cycle use pairs of opposite parity.  With 8 pairs per row
+// (d = 128) the pair is rotated by 2 * (r % 4), so the 8 (row, pair)
+// combinations of a cycle land on 8 distinct bank groups; with 4 pairs
+// (d = 64) it is XOR-ed with r % 4.
+template <int CPR>
+__device__ __forceinline__ int vchunk_phys(int r, int c) {
+    constexpr int NP = CPR / 2;
+    const int m = c >> 1;
+    const int pm = NP == 8 ? ((m + 2 * (r & 3)) & 7) : (m ^ (r & (NP - 1)));
+    return 2 * pm + (c & 1);
+}
+template <int CPR>
+__device__ __forceinline__ int vchunk_logical(int r, int p) {
+    constexpr int NP = CPR / 2;
+    const int pm = p >> 1;
+    const int m = NP == 8 ? ((pm - 2 * (r & 3)) & 7) : (pm ^ (r & (NP - 1)));
+    return 2 * m + (p & 1);
+}
+
+// SPLIT_P: P is rounded to bf16 for the P.V MFMA.  Its relative rounding error
+// (2^-8) averages out over long prefixes; for short ones (few keys per row)
+// P is carried as two bf16 terms, hi + lo, and P.V takes two MFMA passes.
+template <int D, int W, bool SPLIT_P>
 __global__ __launch_bounds__(64 * W) void prefix_mfma_kernel(Args a) {
     constexpr int NT = spkv::kPrefixKeyTile;   // 32 keys per tile
+    constexpr int STAGES = 4;
     constexpr int KS = D / 16;                 // MFMA k-steps for Q.K
     constexpr int NDB = D / 32;                // 32-column blocks of the output
-    constexpr int PITCH = D + 8;               // LDS row pitch (elements)
-    constexpr int PIECES = NT * D / 8;         // 16-byte pieces per tile
-    __shared__ __attribute__((aligned(16))) uint16_t ks[NT * PITCH];
-    __shared__ __attribute__((aligned(16))) uint16_t vs[NT * PITCH];
+    constexpr int ROWB = D * 2;                // bytes per K/V row
+    constexpr int TILEB = NT * ROWB;           // bytes per K (or V) tile
+    constexpr int CPR = ROWB / 16;             // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;              // rows per wave-wide DMA
+    constexpr int IPW = NT / RPI / W;          // DMAs per wave per tile per operand
+    static_assert(IPW >= 1 && (NT / RPI) % W == 0, "tile must split evenly over the waves");
+    constexpr int AHEAD = (STAGES - 2) * 2 * IPW;   // DMAs issued after a tile's own
+    __shared__ __attribute__((aligned(1024))) char smem[STAGES * 2 * TILEB];
 
     const int gz = blockIdx.z;
     const int g = gz / a.Hkv;
@@ -376,6 +444,7 @@ __global__ __launch_bounds__(64 * W) void prefix_mfma_kernel(Args a) {
     if (s >= nsplit) return;
     const int k0 = s * chunk;
     const int k1 = min(lp, k0 + chunk);
+    const int ntiles = (k1 - k0 + NT - 1) / NT;
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -383,12 +452,60 @@ __global__ __launch_bounds__(64 * W) void prefix_mfma_kernel(Args a) {
     const int half = lane >> 5;
     const int col = lane & 31;
 
+    const char *kh = (const char *)a.k_hot + ((int64_t)base * a.Hkv + (int64_t)h * lp) * ROWB;
+    const char *vh = (const char *)a.v_hot + ((int64_t)base * a.Hkv + (int64_t)h * lp) * ROWB;
+    // kh / vh are wave-uniform (kernel arguments and block indices only), so
+    // they live in SGPRs as the DMA's "s" operand requires.  (The readfirstlane
+    // builtin is 32-bit and must not be applied to these 64-bit pointers.)
+    const uint32_t smem0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_offset(smem));
+
+    // Per-lane source rows and LDS placement of the DMAs.  K row r holds key
+    // swap_bits23(r); chunk c of a row sits at vchunk/kchunk-swizzled positions.
+    int koff[IPW], voff[IPW];
+    uint32_t wdst[IPW];
+    {
+        const int p = lane % CPR;
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) {
+            const int r0 = (wave * IPW + i) * RPI;
+            const int r = r0 + lane / CPR;
+            koff[i] = swap_bits23(r);
+            voff[i] = r;
+            // physical chunk p of row r holds logical chunk kc / vc
+            const int kc = p ^ (r % CPR);
+            const int vc = vchunk_logical<CPR>(r, p);
+            koff[i] = (koff[i] << 16) | (kc << 4);
+            voff[i] = (voff[i] << 16) | (vc << 4);
+            wdst[i] = (uint32_t)__builtin_amdgcn_readfirstlane((int)(r0 * ROWB));
+        }
+    }
+    auto issue = [&](int t) {
+        const int kt = k0 + t * NT;
+        const uint32_t kst = smem0 + (uint32_t)((t % STAGES) * 2 * TILEB);
+        const uint32_t vst = kst + TILEB;
+        const bool tail = kt + NT > k1;
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) {
+            int kr = kt + (koff[i] >> 16), vr = kt + (voff[i] >> 16);
+            if (tail) {   // rows past the key range read the last valid key (in bounds; masked later)
+                kr = min(kr, k1 - 1);
+                vr = min(vr, k1 - 1);
+            }
+            dma16(kh, (uint32_t)(kr * ROWB + (koff[i] & 0xffff)), kst + wdst[i]);
+            dma16(vh, (uint32_t)(vr * ROWB + (voff[i] & 0xffff)), vst + wdst[i]);
+        }
+    };
+
+#pragma unroll
+    for (int t = 0; t < STAGES - 1; ++t)
+        if (t < ntiles) issue(t);
+
     // This lane's query row (column of S^T / O^T).
     const int row = mt * 32 * W + wave * 32 + col;
     const bool row_ok = row < M;
     int qb = 0, qj = 0;
     if (row_ok) {
-        int mb = a.members[m0 + row / a.G];
+        const int mb = a.members[m0 + row / a.G];
         qb = max(0, min(mb, a.B - 1));
         qj = h * a.G + row % a.G;
     }
@@ -400,60 +517,38 @@ __global__ __launch_bounds__(64 * W) void prefix_mfma_kernel(Args a) {
             u32x4_t v = row_ok ? *(const u32x4_t *)(qp + k * 16) : u32x4_t{0, 0, 0, 0};
             qf[k] = __builtin_bit_cast(bf16x8_t, v);
         }
+        // Consume Q here so the compiler waits for its loads once, before the
+        // loop, and not inside it (where the tile DMAs are still in flight).
+#pragma unroll
+        for (int k = 0; k < KS; ++k) asm volatile("" ::"v"(__builtin_bit_cast(u32x4_t, qf[k])));
     }
-
-    const uint16_t *kh = (const uint16_t *)a.k_hot + ((int64_t)base * a.Hkv + (int64_t)h * lp) * D;
-    const uint16_t *vh = (const uint16_t *)a.v_hot + ((int64_t)base * a.Hkv + (int64_t)h * lp) * D;
-
-    constexpr int MAXP = PIECES / (64 * W);   // 16-byte pieces per thread per tile
-    static_assert(PIECES % (64 * W) == 0, "tile must split evenly over the block");
-    u32x4_t stk[MAXP], stv[MAXP];
-    constexpr int nthr = 64 * W;
-    auto stage_load = [&](int kt) {
-#pragma unroll
-        for (int i = 0; i < MAXP; ++i) {
-            const int pc = tid + i * nthr;
-            {
-                const int key = pc / (D / 8);
-                const int part = pc % (D / 8);
-                const int kg = kt + key;
-                if (kg < k1) {
-                    stk[i] = *(const u32x4_t *)(kh + (int64_t)kg * D + part * 8);
-                    stv[i] = *(const u32x4_t *)(vh + (int64_t)kg * D + part * 8);
-                } else {
-                    stk[i] = u32x4_t{0, 0, 0, 0};
-                    stv[i] = u32x4_t{0, 0, 0, 0};
-                }
-            }
-        }
-    };
-    auto stage_store = [&]() {
-#pragma unroll
-        for (int i = 0; i < MAXP; ++i) {
-            const int pc = tid + i * nthr;
-            {
-                const int key = pc / (D / 8);
-                const int part = pc % (D / 8);
-                const int krow = (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);  // swap bits 2 and 3
-                *(u32x4_t *)(ks + krow * PITCH + part * 8) = stk[i];
-                *(u32x4_t *)(vs + key * PITCH + part * 8) = stv[i];
-            }
-        }
-    };
 
     f32x16_t oacc[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int j = 0; j < 16; ++j) oacc[db][j] = 0.f;
+    // Running reference max (log2 units) and normaliser.  The reference only
+    // moves when a row's max grows by more than kRescaleSlack: any reference
+    // gives the same O = sum 2^(s-m) v / sum 2^(s-m), and the slack bounds the
+    // un-normalised terms by 2^kRescaleSlack.
+    constexpr float kRescaleSlack = 8.f;
     float m_run = -INFINITY, l_run = 0.f;
+    const float c2 = a.scale_log2;
 
-    stage_load(k0);
-    for (int kt = k0; kt < k1; kt += NT) {
-        __syncthreads();
-        stage_store();
-        __syncthreads();
-        if (kt + NT < k1) stage_load(kt + NT);
+    const int krow_off = col * ROWB;
+    const int g16 = lane >> 4, j16 = lane & 15;
+
+    for (int t = 0; t < ntiles; ++t) {
+        if (t + STAGES - 2 < ntiles) wait_vmcnt<AHEAD>();
+        else wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();          // tile t visible; every wave is done with tile t-1
+        asm volatile("" ::: "memory");
+        if (t + STAGES - 1 < ntiles) issue(t + STAGES - 1);
+
+        const char *ks = smem + (t % STAGES) * 2 * TILEB;
+        const char *vs = ks + TILEB;
+        const int kt = k0 + t * NT;
 
         // S^T = K . Q^T
         f32x16_t sacc;
@@ -461,66 +556,76 @@ __global__ __launch_bounds__(64 * W) void prefix_mfma_kernel(Args a) {
         for (int j = 0; j < 16; ++j) sacc[j] = 0.f;
 #pragma unroll
         for (int k = 0; k < KS; ++k) {
-            bf16x8_t af = *(const bf16x8_t *)(ks + col * PITCH + k * 16 + half * 8);
+            const int c = 2 * k + half;
+            const bf16x8_t af = *(const bf16x8_t *)(ks + krow_off + ((c ^ (col % CPR)) << 4));
             sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[k], sacc, 0, 0, 0);
         }
-        // Online softmax along keys (one query row per lane, two lane halves).
-        float sv[16];
-        float mx = -INFINITY;
+        if (kt + NT > k1) {   // last tile of the range: mask keys past its end
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int key = kt + 16 * (j >> 3) + 8 * half + (j & 7);
-            sv[j] = key < k1 ? sacc[j] * a.scale_log2 : -INFINITY;
-            mx = fmaxf(mx, sv[j]);
+            for (int j = 0; j < 16; ++j)
+                if (kt + 16 * (j >> 3) + 8 * half + (j & 7) >= k1) sacc[j] = -INFINITY;
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float mnew = fmaxf(m_run, mx);
-        const float muse = mnew == -INFINITY ? 0.f : mnew;
-        const float alpha = exp2f(m_run - muse);
-        m_run = mnew;
+        // Online softmax along keys (one query row per lane, two lane halves).
+        float mx = fmaxf(fmaxf(sacc[0], sacc[1]), sacc[2]);
+#pragma unroll
+        for (int j = 3; j < 16; j += 2) mx = fmaxf(fmaxf(mx, sacc[j]), sacc[j + 1 < 16 ? j + 1 : j]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c2;
+        const bool grow = mx > m_run + kRescaleSlack;
+        if (__any(grow)) {
+            const float mnew = grow ? mx : m_run;
+            const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
+            m_run = mnew;
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
+        }
+        const float nm = -m_run;
         float psum = 0.f;
-        uint32_t pk[8];
+        uint32_t pk[8], pl[8];
 #pragma unroll
         for (int j = 0; j < 16; j += 2) {
-            const float p0 = exp2f(sv[j] - muse);
-            const float p1 = exp2f(sv[j + 1] - muse);
-            psum += p0 + p1;
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[j], c2, nm));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[j + 1], c2, nm));
             bf16x2_t pp = {(__bf16)p0, (__bf16)p1};   // round to nearest even
-            pk[j >> 1] = __builtin_bit_cast(uint32_t, pp);
+            const uint32_t w = __builtin_bit_cast(uint32_t, pp);
+            pk[j >> 1] = w;
+            const float h0 = bf16lo(w), h1 = bf16hi(w);
+            if constexpr (SPLIT_P) {
+                bf16x2_t ll = {(__bf16)(p0 - h0), (__bf16)(p1 - h1)};
+                pl[j >> 1] = __builtin_bit_cast(uint32_t, ll);
+                psum += p0 + p1;
+            } else {
+                // Normalise by the weights the MFMA actually uses, so the
+                // output stays a convex combination of V rows.
+                psum += h0 + h1;
+            }
         }
-        l_run = l_run * alpha + psum;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
+        l_run += psum;
 
-        // O^T += V^T . P^T, two 16-key steps.
+        // O^T += V^T . P^T, two 16-key steps; V^T operands by transposing reads.
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            uint16_t vcol[NDB][8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int key = 16 * kb + 8 * half + e;
-                const uint16_t *src = vs + key * PITCH + col * NDB;
-                if constexpr (NDB == 4) {
-                    u32x2_t w = *(const u32x2_t *)src;
-                    vcol[0][e] = (uint16_t)(w.x & 0xffff); vcol[1][e] = (uint16_t)(w.x >> 16);
-                    vcol[2][e] = (uint16_t)(w.y & 0xffff); vcol[3][e] = (uint16_t)(w.y >> 16);
-                } else {
-                    uint32_t w = *(const uint32_t *)src;
-                    vcol[0][e] = (uint16_t)(w & 0xffff); vcol[1][e] = (uint16_t)(w >> 16);
-                }
-            }
-            u32x4_t pb = {pk[4 * kb + 0], pk[4 * kb + 1], pk[4 * kb + 2], pk[4 * kb + 3]};
+            const u32x4_t pb = {pk[4 * kb + 0], pk[4 * kb + 1], pk[4 * kb + 2], pk[4 * kb + 3]};
             const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pb);
+            const u32x4_t plb = {pl[4 * kb + 0], pl[4 * kb + 1], pl[4 * kb + 2], pl[4 * kb + 3]};
+            const bf16x8_t pfl = __builtin_bit_cast(bf16x8_t, plb);
+            const int r1 = 16 * kb + 8 * (g16 >> 1) + (j16 >> 2);   // key row of the first read
+            const int r2 = r1 + 4;
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                u32x4_t w;
-                w.x = (uint32_t)vcol[db][0] | ((uint32_t)vcol[db][1] << 16);
-                w.y = (uint32_t)vcol[db][2] | ((uint32_t)vcol[db][3] << 16);
-                w.z = (uint32_t)vcol[db][4] | ((uint32_t)vcol[db][5] << 16);
-                w.w = (uint32_t)vcol[db][6] | ((uint32_t)vcol[db][7] << 16);
+                const int dpiece = 32 * db + 16 * (g16 & 1) + 4 * (j16 & 3);
+                const int c = dpiece >> 3, inner = (dpiece & 7) * 2;
+                const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (v4i16_t __attribute__((address_space(3))) *)(lds_char_t *)(vs + r1 * ROWB + (vchunk_phys<CPR>(r1, c) << 4) + inner));
+                const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (v4i16_t __attribute__((address_space(3))) *)(lds_char_t *)(vs + r2 * ROWB + (vchunk_phys<CPR>(r2, c) << 4) + inner));
+                const u32x4_t w = {__builtin_bit_cast(u32x2_t, lo).x, __builtin_bit_cast(u32x2_t, lo).y,
+                                   __builtin_bit_cast(u32x2_t, hi).x, __builtin_bit_cast(u32x2_t, hi).y};
                 oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w), pf, oacc[db], 0, 0, 0);
+                if constexpr (SPLIT_P)
+                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w), pfl, oacc[db], 0, 0, 0);
             }
         }
     }
@@ -531,24 +636,27 @@ __global__ __launch_bounds__(64 * W) void prefix_mfma_kernel(Args a) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     float *dst = a.o_part + prow * D;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const int mrow = (j >> 2) * 8 + half * 4 + (j & 3);
-        if constexpr (NDB == 4) {
-            *(float4 *)(dst + 4 * mrow) = make_float4(oacc[0][j] * inv, oacc[1][j] * inv, oacc[2][j] * inv, oacc[3][j] * inv);
-        } else {
-            *(float2 *)(dst + 2 * mrow) = make_float2(oacc[0][j] * inv, oacc[1][j] * inv);
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; j += 4) {
+            const int d = 32 * db + 8 * (j >> 2) + 4 * half;
+            *(float4 *)(dst + d) = make_float4(oacc[db][j] * inv, oacc[db][j + 1] * inv, oacc[db][j + 2] * inv,
+                                               oacc[db][j + 3] * inv);
         }
-    }
     if (half == 0) a.lse_part[prow] = l_tot > 0.f ? m_run + __log2f(l_tot) : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
 // Merge of a row's partial states (Eq. (1) applied across all partials).
-// One wave per (request, query head) row; four rows per block.
+// One wave per (request, query head) row; four rows per block.  Lane k first
+// holds partial k's weight exp2(lse_k - max); then each wave-wide load brings
+// PPW partial rows (LPP lanes x 16 bytes each), several loads in flight.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(Args a, float *out, float *lse_out) {
-    constexpr int VPL = D / 64;   // output floats per lane
+    constexpr int LPP = D / 4;      // lanes per partial row (float4 each)
+    constexpr int PPW = 64 / LPP;   // partial rows per wave-wide load
+    constexpr int UNR = 4;          // loads in flight per lane
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + wave;
@@ -564,35 +672,55 @@ __global__ __launch_bounds__(256) void merge_kernel(Args a, float *out, float *l
     int nf = spkv::splits_for(L, spkv::chunk_for(L, a.flat_tau, spkv::kFlatSplitCap, spkv::kFlatGranule));
     np = min(np, a.prefix_splits);   // never read past this row's partial slots
     nf = min(nf, a.flat_splits);
-    const int n = np + nf;
+    const int n = np + nf;           // <= 128
     const int64_t prow0 = row * a.splits_total;
+    auto slot_of = [&](int k) { return k < np ? k : a.prefix_splits + (k - np); };
 
-    float mx = -INFINITY;
-    for (int k = lane; k < n; k += 64) {
-        const int idx = k < np ? k : a.prefix_splits + (k - np);
-        mx = fmaxf(mx, a.lse_part[prow0 + idx]);
-    }
+    // Weights: lane k holds partials k and k + 64.
+    const float l0 = lane < n ? a.lse_part[prow0 + slot_of(lane)] : -INFINITY;
+    const float l1 = lane + 64 < n ? a.lse_part[prow0 + slot_of(lane + 64)] : -INFINITY;
+    float mx = fmaxf(l0, l1);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
     const float muse = mx == -INFINITY ? 0.f : mx;
-    float o[VPL];
+    const float w0 = exp2f(l0 - muse), w1 = exp2f(l1 - muse);
+    float wsum = w0 + w1;
 #pragma unroll
-    for (int e = 0; e < VPL; ++e) o[e] = 0.f;
-    float wsum = 0.f;
-    for (int k = 0; k < n; ++k) {
-        const int idx = k < np ? k : a.prefix_splits + (k - np);
-        const float lse = a.lse_part[prow0 + idx];
-        const float w = exp2f(lse - muse);
-        wsum += w;
-        const float *src = a.o_part + (prow0 + idx) * D + lane * VPL;
-        if (w > 0.f) {
+    for (int off = 32; off > 0; off >>= 1) wsum += __shfl_xor(wsum, off, 64);
+
+    const int sub = lane % LPP;      // float4 column of the row
+    const int which = lane / LPP;    // partial within a wave-wide load
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k0 = 0; k0 < n; k0 += PPW * UNR) {
+        float4 v[UNR];
+        float w[UNR];
 #pragma unroll
-            for (int e = 0; e < VPL; ++e) o[e] = fmaf(w, src[e], o[e]);
+        for (int u = 0; u < UNR; ++u) {
+            const int k = k0 + u * PPW + which;
+            const int kk = k < n ? k : 0;
+            const float wa = __shfl(w0, kk & 63, 64), wb = __shfl(w1, kk & 63, 64);
+            w[u] = k < n ? (kk < 64 ? wa : wb) : 0.f;
+            v[u] = k < n ? *(const float4 *)(a.o_part + (prow0 + slot_of(kk)) * D + sub * 4)
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+            acc.x = fmaf(w[u], v[u].x, acc.x);
+            acc.y = fmaf(w[u], v[u].y, acc.y);
+            acc.z = fmaf(w[u], v[u].z, acc.z);
+            acc.w = fmaf(w[u], v[u].w, acc.w);
         }
     }
-    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
 #pragma unroll
-    for (int e = 0; e < VPL; ++e) out[row * D + lane * VPL + e] = o[e] * inv;
+    for (int off = LPP; off < 64; off <<= 1) {
+        acc.x += __shfl_xor(acc.x, off, 64);
+        acc.y += __shfl_xor(acc.y, off, 64);
+        acc.z += __shfl_xor(acc.z, off, 64);
+        acc.w += __shfl_xor(acc.w, off, 64);
+    }
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    if (which == 0)
+        *(float4 *)(out + row * D + sub * 4) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
     if (lse_out && lane == 0) lse_out[row] = wsum > 0.f ? (mx + __log2f(wsum)) * kLn2 : -INFINITY;
 }
 
@@ -761,13 +889,20 @@ spkv_status launch_prefix(const Args &a, const Plan &p, int d, hipStream_t st) {
     if (p.prefix_splits <= 0 || p.prefix_mtiles <= 0) return SPKV_OK;
     dim3 grid(p.prefix_splits, p.prefix_mtiles, a.ng * a.Hkv), block(64 * p.prefix_waves);
     TimedLaunch tl(SPKV_KERNEL_PREFIX, st);
-    switch (p.prefix_waves * 1000 + d) {
-    case 1128: prefix_mfma_kernel<128, 1><<<grid, block, 0, st>>>(a); break;
-    case 2128: prefix_mfma_kernel<128, 2><<<grid, block, 0, st>>>(a); break;
-    case 4128: prefix_mfma_kernel<128, 4><<<grid, block, 0, st>>>(a); break;
-    case 1064: prefix_mfma_kernel<64, 1><<<grid, block, 0, st>>>(a); break;
-    case 2064: prefix_mfma_kernel<64, 2><<<grid, block, 0, st>>>(a); break;
-    case 4064: prefix_mfma_kernel<64, 4><<<grid, block, 0, st>>>(a); break;
+    const int key = p.prefix_waves * 1000 + d + (p.prefix_split_p ? 10000 : 0);
+    switch (key) {
+    case 1128: prefix_mfma_kernel<128, 1, false><<<grid, block, 0, st>>>(a); break;
+    case 2128: prefix_mfma_kernel<128, 2, false><<<grid, block, 0, st>>>(a); break;
+    case 4128: prefix_mfma_kernel<128, 4, false><<<grid, block, 0, st>>>(a); break;
+    case 1064: prefix_mfma_kernel<64, 1, false><<<grid, block, 0, st>>>(a); break;
+    case 2064: prefix_mfma_kernel<64, 2, false><<<grid, block, 0, st>>>(a); break;
+    case 4064: prefix_mfma_kernel<64, 4, false><<<grid, block, 0, st>>>(a); break;
+    case 11128: prefix_mfma_kernel<128, 1, true><<<grid, block, 0, st>>>(a); break;
+    case 12128: prefix_mfma_kernel<128, 2, true><<<grid, block, 0, st>>>(a); break;
+    case 14128: prefix_mfma_kernel<128, 4, true><<<grid, block, 0, st>>>(a); break;
+    case 11064: prefix_mfma_kernel<64, 1, true><<<grid, block, 0, st>>>(a); break;
+    case 12064: prefix_mfma_kernel<64, 2, true><<<grid, block, 0, st>>>(a); break;
+    case 14064: prefix_mfma_kernel<64, 4, true><<<grid, block, 0, st>>>(a); break;
     default: return fail(SPKV_E_INVAL, "unsupported prefix tile");
     }
     return check_launch("prefix_mfma_kernel");

@@ -109,6 +109,7 @@ spkv_status make_plan(const spkv_batch *b, const int32_t *cascade, int32_t num_c
         if (mask_get(p->cascade, g)) {
             max_m = std::max<int64_t>(max_m, n * G);
             max_lp_c = std::max<int64_t>(max_lp_c, lp);
+            if (lp < kSplitPBelow) p->prefix_split_p = true;
         } else {
             flat_total += n * lp;
         }
