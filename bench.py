@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--lp", type=int, default=None, help="override the prefix length (C3 sweep)")
     ap.add_argument("--mode", default="step", choices=["step", "cascade", "dense"],
                     help="step: dispatcher decides (default); cascade/dense: force a backend")
+    ap.add_argument("--page-size", type=int, default=None, help="override the COLD page size")
+    ap.add_argument("--contiguous", action="store_true", help="COLD pages handed out in order (no shuffle)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle timing sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
@@ -71,7 +73,9 @@ def main():
     dev = torch.device("cuda:0")
     cfg = W.CONFIGS[args.config]
     total_steps = args.warmup + 2 * args.steps + 1
-    wl = W.make_workload(cfg, prefix_len=args.lp, extra_steps=max(32, total_steps + 1))
+    wl = W.make_workload(cfg, prefix_len=args.lp, page_size=args.page_size, extra_steps=max(32, total_steps + 1))
+    if args.contiguous:
+        wl.free_order = None
     cfg = wl.cfg
     B, Hq, Hkv, d, P = wl.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.page_size
     esz = 2 if cfg.dtype == "bf16" else 4
@@ -232,8 +236,9 @@ def main():
         "config": {
             "workload": f"{cfg.name}: one decode step, B={B}, Hq={Hq}, Hkv={Hkv}, d={d}, {cfg.dtype}, "
                         f"Lp={list(map(int, wl.group_prefix_len))}, Ls~U{list(cfg.suffix_range)} (+1 per step), "
-                        f"COLD page size {P}, shuffled slots",
+                        f"COLD page size {P}, {'contiguous' if args.contiguous else 'shuffled'} slots",
             "batch": B, "prefix_len": [int(x) for x in wl.group_prefix_len], "page_size": P,
+            "slots": "contiguous" if args.contiguous else "shuffled",
             "backend": ("cascade" if cascade else "dense"), "mode": args.mode,
         },
         "gpu_ms_per_step": round(gpu_ms / args.steps, 4),

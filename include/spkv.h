@@ -214,7 +214,7 @@ typedef struct spkv_batch {
     int32_t num_kv_heads;          /* Hkv, 1..16 */
     int32_t head_dim;              /* d: 64 or 128 */
     int32_t dtype;                 /* SPKV_DTYPE_* of q and of every K/V pool */
-    float   scale;                 /* softmax scale applied to q.k (usually 1/sqrt(d)) */
+    float   scale;                 /* softmax scale applied to q.k, > 0 (usually 1/sqrt(d)) */
     const void *q;                 /* device [B, Hq, d] */
 
     int32_t num_groups;            /* ng, 0..512 */
@@ -223,7 +223,8 @@ typedef struct spkv_batch {
     const int32_t *group_members;  /* device: request ids; request b appears once, in group group_of[b] */
     const int64_t *hot_base;       /* device [ng]: slab base (token slot) */
     const int32_t *hot_len;        /* device [ng]: prefix length Lp_g >= 0 */
-    const int32_t *host_group_indptr; /* host copies of the three group arrays above */
+    const int32_t *host_group_of;     /* host copies of group_of and of the three group arrays above */
+    const int32_t *host_group_indptr;
     const int64_t *host_hot_base;
     const int32_t *host_hot_len;
 

@@ -27,7 +27,8 @@ class spkv_batch(C.Structure):
                 ("dtype", c_i32), ("scale", c_f32), ("q", c_vp),
                 ("num_groups", c_i32), ("group_of", c_vp), ("group_indptr", c_vp), ("group_members", c_vp),
                 ("hot_base", c_vp), ("hot_len", c_vp),
-                ("host_group_indptr", c_vp), ("host_hot_base", c_vp), ("host_hot_len", c_vp),
+                ("host_group_of", c_vp), ("host_group_indptr", c_vp), ("host_hot_base", c_vp),
+                ("host_hot_len", c_vp),
                 ("page_size", c_i32), ("max_blocks", c_i32), ("block_tables", c_vp), ("cold_lens", c_vp),
                 ("host_cold_lens", c_vp)]
 

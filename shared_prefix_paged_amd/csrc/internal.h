@@ -4,6 +4,7 @@
 #include <cstdint>
 #include <cstddef>
 #include <string>
+#include <vector>
 
 #include "spkv.h"
 
@@ -27,6 +28,9 @@ constexpr int kFlatSplitCap = 64;      // partials per row from the flat pass
 constexpr int kPrefixSplitCap = 64;    // partials per row from the prefix pass
 constexpr int kPrefixKeyTile = 32;     // keys per MFMA tile in the prefix kernel
 constexpr int kFlatGranule = 16;       // flat chunks are multiples of this many tokens
+constexpr int kFlatWaves = 4;          // KV heads (one wave each) per flat block
+constexpr int kFlatMinTokens = 64;     // shortest flat range per block
+constexpr int kFlatWaveSlots = 16;     // resident flat waves per CU (128 VGPRs)
 constexpr int kSplitPBelow = 256;      // prefixes shorter than this carry P as bf16 hi + lo
 
 // Per-group cascade bitmask passed to kernels by value.
@@ -34,12 +38,29 @@ struct GroupMask {
     uint32_t bits[kMaxGroups / 32];
 };
 
+// One launch of the paged (flat) pass over a sub-batch of at most
+// kFlatArgReqs requests.  Its tokens - every request's range of
+// [HOT prefix ; COLD suffix] concatenated in request order - are cut into
+// `blocks` equal ranges per group of up to kFlatWaves KV heads (stream-K), so
+// every block carries the same number of tokens whatever the request lengths.
+// Passed by value as a kernel argument: blocks find their requests with a few
+// scalar loads and no index pass.
+constexpr int kFlatArgReqs = 256;
+struct FlatLaunch {
+    int32_t b0;                        // first request of the sub-batch
+    int32_t nreq;                      // requests in it
+    int32_t blocks;                    // ranges per head group (grid x)
+    int32_t max_parts;                 // bound on partial states per request
+    int64_t total;                     // tokens of the sub-batch
+    int32_t offs[kFlatArgReqs + 1];    // exclusive prefix sums of the request lengths
+};
+
 // The launch plan of one decode call (host-computed, deterministic).
 struct Plan {
     GroupMask cascade;        // bit g set: group g takes the prefix contraction
     int32_t num_groups;
-    int32_t flat_chunk;       // base tau for the flat pass
-    int32_t flat_splits;      // grid x of the flat kernel (max partials per row)
+    int32_t flat_chunk;       // tokens per flat block (largest sub-batch)
+    int32_t flat_splits;      // partial slots per row reserved for the flat pass
     int32_t prefix_chunk;     // base tau for the prefix pass (multiple of kPrefixKeyTile)
     int32_t prefix_splits;    // grid x of the prefix kernel
     int32_t prefix_waves;     // waves per prefix block (32 rows each)
@@ -48,6 +69,9 @@ struct Plan {
     int64_t flat_items;
     int64_t prefix_items;
     int64_t ws_bytes;
+    std::vector<FlatLaunch> flat;    // paged pass (suffix, or whole context for flat-mode groups)
+    std::vector<FlatLaunch> pflat;   // float32 cascade: the prefix part as a paged pass
+    int32_t flat_head_groups;        // grid y of the paged pass
     bool run_prefix;          // some cascade group has Lp > 0 (bf16)
     bool prefix_split_p;      // some cascade group is short: carry P as bf16 hi + lo
     bool prefix_as_flat;      // float32 pools: prefix part via a per-request pass

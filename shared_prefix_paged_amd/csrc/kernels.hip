@@ -21,6 +21,7 @@
 #include "internal.h"
 
 using spkv::fail;
+using spkv::FlatLaunch;
 using spkv::GroupMask;
 using spkv::Plan;
 
@@ -63,6 +64,7 @@ struct Args {
     int32_t prefix_splits;  // offset of the flat partials inside a row
     int32_t flat_splits;    // flat partial slots per row
     int32_t flat_tau, prefix_tau, prefix_granule;
+    int32_t prefix_mode;    // 0: no prefix partials; 1: MFMA split rule; 2: paged prefix pass
     GroupMask cascade;
 };
 
@@ -147,41 +149,102 @@ __device__ __forceinline__ float fdot2(uint32_t a, uint32_t b, float c) {
 // one wave per head.  Inside a wave, LPT lanes hold one token's K (or V) row
 // as 16-byte pieces, so a wave-wide load covers TPW tokens; each group of LPT
 // lanes keeps its own online-softmax state, combined once at the end.
-// Row addresses (HOT slab row or COLD slot row) are computed once per 64
-// tokens, one per lane, and fetched with a lane permute.
+//
+// Memory pipeline: the loads of the next TPI tokens are issued before the
+// current TPI tokens are computed (two register stages), and the row codes
+// (HOT slab row or COLD slot row, one per lane for 64 tokens) of the next
+// 64-token block are fetched one block ahead, so a wave always has a full
+// iteration of K/V loads in flight.
 // ---------------------------------------------------------------------------
+
+// Rows of TPI tokens (U wave-wide loads of K and V) held in registers.
+template <int U>
+struct KVStage {
+    u32x4_t k[U], v[U];
+    bool valid[U];
+};
+
+// Occupancy: 4 waves per SIMD (<= 128 VGPRs) for group sizes up to 5.
+// Range (block) index containing token x when T tokens are cut into nb
+// ranges [floor(k*T/nb), floor((k+1)*T/nb)).
+__device__ __forceinline__ int range_of(int64_t x, int64_t T, int nb) {
+    int k = (int)((x * nb) / T);
+    if (k + 1 < nb && (T * (k + 1)) / nb <= x) ++k;
+    return k;
+}
+
+// Partial states written for request i of a flat launch, and the first range.
+__device__ __forceinline__ int flat_parts(const FlatLaunch &f, int i, int *first) {
+    const int64_t o0 = f.offs[i], o1 = f.offs[i + 1];
+    if (f.blocks <= 0 || o1 <= o0) {
+        *first = 0;
+        return 0;
+    }
+    const int k0 = range_of(o0, f.total, f.blocks);
+    *first = k0;
+    return range_of(o1 - 1, f.total, f.blocks) - k0 + 1;
+}
+
+// Online softmax of the G query rows of KV head h over tokens [t0, t1) of
+// request b; the normalised partial state goes to partial slot `slot`.
 template <bool BF16, int D, int G>
-__global__ __launch_bounds__(256) void flat_kernel(Args a, int part) {
+__device__ __forceinline__ void attend_range(const Args &a, const Req &r, int b, int h, int t0, int t1, int slot,
+                                             int lane) {
     constexpr int ESZ = BF16 ? 2 : 4;
     constexpr int VEC = 16 / ESZ;            // elements per 16-byte piece
     constexpr int LPT = D / VEC;             // lanes per token row
     constexpr int TPW = 64 / LPT;            // tokens per wave-wide load
-    constexpr int U = (G <= 4) ? 4 : 2;      // loads in flight per operand
+    constexpr int U = (G <= 4) ? 2 : 1;      // wave-wide loads per operand per iteration (two stages in flight)
     constexpr int TPI = TPW * U;             // tokens per iteration
+    constexpr int IPB = 64 / TPI;            // iterations per 64-token block
     static_assert(64 % TPI == 0, "iteration must divide 64 tokens");
-
-    const int s = blockIdx.x;
-    const int b = blockIdx.y;
-    const int wave = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63;
-    const int h = blockIdx.z * kFlatWavesMax + wave;
-    if (h >= a.Hkv) return;
-
-    const Req r = req_geo(a, b);
-    int lo, hi;
-    flat_range(r, part, lo, hi);
-    const int L = hi - lo;
-    const int tau = part == kPartPrefix ? a.prefix_tau : a.flat_tau;
-    const int chunk = spkv::chunk_for(L, tau, part == kPartPrefix ? spkv::kPrefixSplitCap : spkv::kFlatSplitCap,
-                                      part == kPartPrefix ? a.prefix_granule : spkv::kFlatGranule);
-    const int nsplit = spkv::splits_for(L, chunk);
-    if (s >= nsplit) return;
-    const int t0 = lo + s * chunk;
-    const int t1 = min(hi, t0 + chunk);
+    static_assert(IPB % 2 == 0, "iterations of a 64-token block come in pairs (two stages)");
+    constexpr float kRescaleSlack = 8.f;     // see the prefix kernel: exact for any reference
 
     const int sub = lane % LPT;              // 16-byte piece of the row
     const int grp = lane / LPT;              // token group inside the wave
     const int row0 = b * a.Hq + h * G;       // first query row of this head
+
+    const char *khot = (const char *)a.k_hot;
+    const char *vhot = (const char *)a.v_hot;
+    const char *kcold = (const char *)a.k_cold;
+    const char *vcold = (const char *)a.v_cold;
+    const int32_t *table = a.tables + (int64_t)b * a.max_blocks;
+    const int64_t num_pages = a.cold_slots / a.page_size;
+    const uint32_t hot_row0 = (uint32_t)(r.base * a.Hkv + (int64_t)h * r.lp);
+
+    // Row code of token blk + lane: bit 31 = HOT, low bits = row index.  Built
+    // in two steps so the block-table load can be issued a 64-token block
+    // before its value is needed: a load consumed right away would make the
+    // wave wait for every K/V load issued before it (vmcnt retires in order).
+    auto table_entry = [&](int blk) -> int32_t {
+        const int t = min(blk + lane, t1 - 1);
+        return t < r.lp ? 0 : table[(t - r.lp) / a.page_size];
+    };
+    auto row_code = [&](int blk, int32_t entry) -> uint32_t {
+        const int t = min(blk + lane, t1 - 1);
+        if (t < r.lp) return 0x80000000u | (hot_row0 + (uint32_t)t);
+        const int tc = t - r.lp;
+        int64_t page = entry;
+        page = page < 0 ? 0 : (page >= num_pages ? num_pages - 1 : page);
+        return (uint32_t)((page * a.page_size + tc % a.page_size) * a.Hkv + h);
+    };
+    // Issue the loads of iteration j (tokens t0 + j*TPI ...) with the row codes of its 64-block.
+    auto issue = [&](KVStage<U> &st, int j, uint32_t code) {
+        const int base = (j % IPB) * TPI;
+        const int nblk = min(64, t1 - (t0 + (j / IPB) * 64));
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int ti = base + u * TPW + grp;            // token index inside the 64-block
+            st.valid[u] = ti < nblk;
+            // lane ti of `code` already holds the row of min(token, t1 - 1)
+            const uint32_t c = (uint32_t)__shfl((int)code, ti, 64);
+            const bool hot = c >> 31;
+            const int64_t off = ((int64_t)(c & 0x7fffffffu) * D + sub * VEC) * ESZ;
+            st.k[u] = *(const u32x4_t *)((hot ? khot : kcold) + off);
+            st.v[u] = *(const u32x4_t *)((hot ? vhot : vcold) + off);
+        }
+    };
 
     // Query rows in registers.
     uint32_t qw[G][4];
@@ -202,110 +265,105 @@ __global__ __launch_bounds__(256) void flat_kernel(Args a, int part) {
 #pragma unroll
         for (int e = 0; e < VEC; ++e) acc[g][e] = 0.f;
     }
+    const float c2 = a.scale_log2;
 
-    const char *khot = (const char *)a.k_hot;
-    const char *vhot = (const char *)a.v_hot;
-    const char *kcold = (const char *)a.k_cold;
-    const char *vcold = (const char *)a.v_cold;
-    const int32_t *table = a.tables + (int64_t)b * a.max_blocks;
-    const int64_t num_pages = a.cold_slots / a.page_size;
-    const uint32_t hot_row0 = (uint32_t)(r.base * a.Hkv + (int64_t)h * r.lp);
-
-    for (int blk = t0; blk < t1; blk += 64) {
-        // Row code of token blk + lane: bit 31 = HOT, low bits = row index.
-        uint32_t code;
-        {
-            int t = min(blk + lane, t1 - 1);
-            if (t < r.lp) {
-                code = 0x80000000u | (hot_row0 + (uint32_t)t);
-            } else {
-                int tc = t - r.lp;
-                int64_t page = table[tc / a.page_size];
-                page = page < 0 ? 0 : (page >= num_pages ? num_pages - 1 : page);
-                int64_t slot = page * a.page_size + tc % a.page_size;
-                code = (uint32_t)(slot * a.Hkv + h);
-            }
-        }
-        const int nblk = min(64, t1 - blk);
-        for (int it = 0; it < nblk; it += TPI) {
-            u32x4_t kv[U], vv[U];
-            bool valid[U];
+    auto compute = [&](const KVStage<U> &st) {
+        float sc[U][G];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int ti = it + u * TPW + grp;          // token index inside the 64-block
-                valid[u] = ti < nblk;
-                const uint32_t c = (uint32_t)__shfl((int)code, min(ti, nblk - 1), 64);
-                const bool hot = c >> 31;
-                const int64_t off = ((int64_t)(c & 0x7fffffffu) * D + sub * VEC) * ESZ;
-                kv[u] = *(const u32x4_t *)((hot ? khot : kcold) + off);
-                vv[u] = *(const u32x4_t *)((hot ? vhot : vcold) + off);
-            }
-            float sc[U][G];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-#pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    float d;
-                    if constexpr (BF16) {
-                        d = fdot2(qw[g][0], kv[u].x, 0.f);
-                        d = fdot2(qw[g][1], kv[u].y, d);
-                        d = fdot2(qw[g][2], kv[u].z, d);
-                        d = fdot2(qw[g][3], kv[u].w, d);
-                    } else {
-                        d = __uint_as_float(qw[g][0]) * __uint_as_float(kv[u].x);
-                        d = fmaf(__uint_as_float(qw[g][1]), __uint_as_float(kv[u].y), d);
-                        d = fmaf(__uint_as_float(qw[g][2]), __uint_as_float(kv[u].z), d);
-                        d = fmaf(__uint_as_float(qw[g][3]), __uint_as_float(kv[u].w), d);
-                    }
-                    d = dpp_sum<LPT>(d);
-                    sc[u][g] = valid[u] ? d * a.scale_log2 : -INFINITY;
-                }
-            }
-            float vf[U][VEC];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                if constexpr (BF16) {
-                    vf[u][0] = bf16lo(vv[u].x); vf[u][1] = bf16hi(vv[u].x);
-                    vf[u][2] = bf16lo(vv[u].y); vf[u][3] = bf16hi(vv[u].y);
-                    vf[u][4] = bf16lo(vv[u].z); vf[u][5] = bf16hi(vv[u].z);
-                    vf[u][6] = bf16lo(vv[u].w); vf[u][7] = bf16hi(vv[u].w);
-                } else {
-                    vf[u][0] = __uint_as_float(vv[u].x); vf[u][1] = __uint_as_float(vv[u].y);
-                    vf[u][2] = __uint_as_float(vv[u].z); vf[u][3] = __uint_as_float(vv[u].w);
-                }
-            }
+        for (int u = 0; u < U; ++u) {
 #pragma unroll
             for (int g = 0; g < G; ++g) {
-                float mx = sc[0][g];
+                float d;
+                if constexpr (BF16) {
+                    d = fdot2(qw[g][0], st.k[u].x, 0.f);
+                    d = fdot2(qw[g][1], st.k[u].y, d);
+                    d = fdot2(qw[g][2], st.k[u].z, d);
+                    d = fdot2(qw[g][3], st.k[u].w, d);
+                } else {
+                    d = __uint_as_float(qw[g][0]) * __uint_as_float(st.k[u].x);
+                    d = fmaf(__uint_as_float(qw[g][1]), __uint_as_float(st.k[u].y), d);
+                    d = fmaf(__uint_as_float(qw[g][2]), __uint_as_float(st.k[u].z), d);
+                    d = fmaf(__uint_as_float(qw[g][3]), __uint_as_float(st.k[u].w), d);
+                }
+                d = dpp_sum<LPT>(d);
+                sc[u][g] = st.valid[u] ? d : -INFINITY;   // raw q.k; scale folded below
+            }
+        }
 #pragma unroll
-                for (int u = 1; u < U; ++u) mx = fmaxf(mx, sc[u][g]);
-                const float mnew = fmaxf(m[g], mx);
-                const float muse = mnew == -INFINITY ? 0.f : mnew;
-                const float alpha = exp2f(m[g] - muse);
+        for (int g = 0; g < G; ++g) {
+            float mx = sc[0][g];
+#pragma unroll
+            for (int u = 1; u < U; ++u) mx = fmaxf(mx, sc[u][g]);
+            mx *= c2;
+            if (mx > m[g] + kRescaleSlack) {     // rare after the first tokens
+                const float alpha = __builtin_amdgcn_exp2f(m[g] - mx);
+                m[g] = mx;
                 l[g] *= alpha;
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) acc[g][e] *= alpha;
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const float p = exp2f(sc[u][g] - muse);
-                    l[g] += p;
-#pragma unroll
-                    for (int e = 0; e < VEC; ++e) acc[g][e] = fmaf(p, vf[u][e], acc[g][e]);
-                }
-                m[g] = mnew;
             }
+            // m = -inf only while every token seen is masked (then p = 0, not NaN)
+            const float nm = m[g] == -INFINITY ? 0.f : -m[g];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                sc[u][g] = __builtin_amdgcn_exp2f(fmaf(sc[u][g], c2, nm));   // now the weight p
+                l[g] += sc[u][g];
+            }
+        }
+        // P.V with each value element widened once and used by all G rows.
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const uint32_t w = st.v[u][BF16 ? e / 2 : e];
+                const float v = BF16 ? ((e & 1) ? bf16hi(w) : bf16lo(w)) : __uint_as_float(w);
+#pragma unroll
+                for (int g = 0; g < G; ++g) acc[g][e] = fmaf(sc[u][g], v, acc[g][e]);
+            }
+        }
+    };
+
+    // Steady state without data-dependent branches between a load and its use:
+    // the waitcnt the compiler places before each compute then only covers the
+    // stage being computed (vmcnt = loads of the other stage), not every load in
+    // flight.  Loads are issued for whole 64-token blocks; iterations past t1
+    // read the clamped last row and are masked, and the row codes / table
+    // entries of blocks past t1 are clamped to the last token, so every address
+    // stays inside the request.
+    const int n_it = (t1 - t0 + TPI - 1) / TPI;
+    uint32_t code = row_code(t0, table_entry(t0));   // row codes of the block being issued
+    int32_t entry_nxt = table_entry(t0 + 64);        // table entries of the block after it
+    KVStage<U> sa, sb;
+    issue(sa, 0, code);
+    bool live = true;
+    for (int blk = 0; live; ++blk) {
+#pragma unroll
+        for (int i = 0; i < IPB; i += 2) {
+            const int j = blk * IPB + i;
+            if (j >= n_it) {
+                live = false;
+                break;
+            }
+            issue(sb, j + 1, code);
+            compute(sa);
+            if (i + 2 == IPB) {
+                code = row_code(t0 + (blk + 1) * 64, entry_nxt);
+                entry_nxt = table_entry(t0 + (blk + 2) * 64);
+            }
+            issue(sa, j + 2, code);
+            compute(sb);
         }
     }
 
     // Combine the TPW token groups of the wave (lanes sub, sub+LPT, ...).
-    const int srow = a.prefix_splits * (part == kPartRest) + s;
+    const int srow = slot;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         float M = m[g];
 #pragma unroll
         for (int off = LPT; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
         const float muse = M == -INFINITY ? 0.f : M;
-        const float sc = exp2f(m[g] - muse);
+        const float sc = __builtin_amdgcn_exp2f(m[g] - muse);
         float lt = l[g] * sc;
         float o[VEC];
 #pragma unroll
@@ -327,6 +385,43 @@ __global__ __launch_bounds__(256) void flat_kernel(Args a, int part) {
             }
             if (sub == 0) a.lse_part[prow] = lt > 0.f ? M + __log2f(lt) : -INFINITY;
         }
+    }
+}
+
+// Occupancy: 4 waves per SIMD (<= 128 VGPRs) for group sizes up to 5.
+template <bool BF16, int D, int G>
+__global__ __launch_bounds__(256, (G <= 5 ? 4 : 2)) void flat_kernel(Args a, int part, FlatLaunch fl) {
+    const int k = blockIdx.x;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int h = blockIdx.y * kFlatWavesMax + wave;
+    if (h >= a.Hkv) return;
+    const int64_t T = fl.total;
+    const int nb = fl.blocks;
+    const int64_t s0 = (T * k) / nb, s1 = (T * (k + 1)) / nb;
+    if (s0 >= s1) return;
+    int i = 0, hi_i = fl.nreq;          // first request whose tokens reach past s0
+    while (i < hi_i) {
+        const int mid = (i + hi_i) >> 1;
+        if (fl.offs[mid + 1] > s0) hi_i = mid;
+        else i = mid + 1;
+    }
+    const int slot0 = part == kPartRest ? a.prefix_splits : 0;
+    for (; i < fl.nreq; ++i) {
+        const int64_t o0 = fl.offs[i], o1 = fl.offs[i + 1];
+        if (o0 >= s1) break;
+        const int64_t lo_s = s0 > o0 ? s0 : o0, hi_s = s1 < o1 ? s1 : o1;
+        if (hi_s <= lo_s) continue;
+        const int slot = k - range_of(o0, T, nb);
+        if (slot < 0 || slot >= fl.max_parts) continue;   // cannot happen for a consistent plan
+        const int b = fl.b0 + i;
+        const Req r = req_geo(a, b);
+        int lo, hi;
+        flat_range(r, part, lo, hi);
+        const int t0 = lo + (int)(lo_s - o0);
+        const int t1 = min(hi, lo + (int)(hi_s - o0));   // device data shorter than the plan: clamp
+        if (t1 <= t0) continue;
+        attend_range<BF16, D, G>(a, r, b, h, t0, t1, slot0 + slot, lane);
     }
 }
 
@@ -653,25 +748,28 @@ __global__ __launch_bounds__(64 * W) void prefix_mfma_kernel(Args a) {
 // PPW partial rows (LPP lanes x 16 bytes each), several loads in flight.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void merge_kernel(Args a, float *out, float *lse_out) {
+__global__ __launch_bounds__(256) void merge_kernel(Args a, float *out, float *lse_out, FlatLaunch fr,
+                                                    FlatLaunch fp) {
     constexpr int LPP = D / 4;      // lanes per partial row (float4 each)
     constexpr int PPW = 64 / LPP;   // partial rows per wave-wide load
     constexpr int UNR = 4;          // loads in flight per lane
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + wave;
-    if (row >= (int64_t)a.B * a.Hq) return;
+    const int64_t row = (int64_t)fr.b0 * a.Hq + (int64_t)blockIdx.x * 4 + wave;
+    if (row >= (int64_t)(fr.b0 + fr.nreq) * a.Hq) return;
     const int b = (int)(row / a.Hq);
-    const Req r = req_geo(a, b);
-    int np = 0;
-    if (r.g >= 0 && r.casc && r.lp > 0)
-        np = spkv::splits_for(r.lp, spkv::chunk_for(r.lp, a.prefix_tau, spkv::kPrefixSplitCap, a.prefix_granule));
-    int lo, hi;
-    flat_range(r, kPartRest, lo, hi);
-    const int L = hi - lo;
-    int nf = spkv::splits_for(L, spkv::chunk_for(L, a.flat_tau, spkv::kFlatSplitCap, spkv::kFlatGranule));
-    np = min(np, a.prefix_splits);   // never read past this row's partial slots
-    nf = min(nf, a.flat_splits);
+    const int i = b - fr.b0;
+    int np = 0, first;
+    if (a.prefix_mode == 1) {
+        const Req r = req_geo(a, b);
+        if (r.g >= 0 && r.casc && r.lp > 0)
+            np = spkv::splits_for(r.lp, spkv::chunk_for(r.lp, a.prefix_tau, spkv::kPrefixSplitCap, a.prefix_granule));
+    } else if (a.prefix_mode == 2) {
+        np = flat_parts(fp, i, &first);
+    }
+    int nf = flat_parts(fr, i, &first);
+    np = max(0, min(np, a.prefix_splits));   // never read past this row's partial slots
+    nf = max(0, min(nf, a.flat_splits));
     const int n = np + nf;           // <= 128
     const int64_t prow0 = row * a.splits_total;
     auto slot_of = [&](int k) { return k < np ? k : a.prefix_splits + (k - np); };
@@ -860,29 +958,31 @@ spkv_status check_launch(const char *what) {
 }
 
 template <bool BF16, int D>
-spkv_status launch_flat_d(const Args &a, int part, int splits, hipStream_t st) {
-    const int zb = (a.Hkv + kFlatWavesMax - 1) / kFlatWavesMax;
+spkv_status launch_flat_d(const Args &a, int part, const FlatLaunch &f, int head_groups, hipStream_t st) {
     const int waves = a.Hkv < kFlatWavesMax ? a.Hkv : kFlatWavesMax;
-    dim3 grid(splits, a.B, zb), block(64 * waves);
+    dim3 grid(f.blocks, head_groups), block(64 * waves);
     TimedLaunch tl(SPKV_KERNEL_FLAT, st);
     switch (a.G) {
-    case 1: flat_kernel<BF16, D, 1><<<grid, block, 0, st>>>(a, part); break;
-    case 2: flat_kernel<BF16, D, 2><<<grid, block, 0, st>>>(a, part); break;
-    case 3: flat_kernel<BF16, D, 3><<<grid, block, 0, st>>>(a, part); break;
-    case 4: flat_kernel<BF16, D, 4><<<grid, block, 0, st>>>(a, part); break;
-    case 5: flat_kernel<BF16, D, 5><<<grid, block, 0, st>>>(a, part); break;
-    case 6: flat_kernel<BF16, D, 6><<<grid, block, 0, st>>>(a, part); break;
-    case 7: flat_kernel<BF16, D, 7><<<grid, block, 0, st>>>(a, part); break;
-    case 8: flat_kernel<BF16, D, 8><<<grid, block, 0, st>>>(a, part); break;
+    case 1: flat_kernel<BF16, D, 1><<<grid, block, 0, st>>>(a, part, f); break;
+    case 2: flat_kernel<BF16, D, 2><<<grid, block, 0, st>>>(a, part, f); break;
+    case 3: flat_kernel<BF16, D, 3><<<grid, block, 0, st>>>(a, part, f); break;
+    case 4: flat_kernel<BF16, D, 4><<<grid, block, 0, st>>>(a, part, f); break;
+    case 5: flat_kernel<BF16, D, 5><<<grid, block, 0, st>>>(a, part, f); break;
+    case 6: flat_kernel<BF16, D, 6><<<grid, block, 0, st>>>(a, part, f); break;
+    case 7: flat_kernel<BF16, D, 7><<<grid, block, 0, st>>>(a, part, f); break;
+    case 8: flat_kernel<BF16, D, 8><<<grid, block, 0, st>>>(a, part, f); break;
     default: return fail(SPKV_E_INVAL, "unsupported GQA group size");
     }
     return check_launch("flat_kernel");
 }
 
-spkv_status launch_flat(const Args &a, bool bf16, int d, int part, int splits, hipStream_t st) {
-    if (splits <= 0 || a.B == 0) return SPKV_OK;
-    if (bf16) return d == 128 ? launch_flat_d<true, 128>(a, part, splits, st) : launch_flat_d<true, 64>(a, part, splits, st);
-    return d == 128 ? launch_flat_d<false, 128>(a, part, splits, st) : launch_flat_d<false, 64>(a, part, splits, st);
+spkv_status launch_flat(const Args &a, bool bf16, int d, int part, const FlatLaunch &f, int head_groups,
+                        hipStream_t st) {
+    if (f.blocks <= 0 || a.B == 0) return SPKV_OK;
+    if (bf16) return d == 128 ? launch_flat_d<true, 128>(a, part, f, head_groups, st)
+                              : launch_flat_d<true, 64>(a, part, f, head_groups, st);
+    return d == 128 ? launch_flat_d<false, 128>(a, part, f, head_groups, st)
+                    : launch_flat_d<false, 64>(a, part, f, head_groups, st);
 }
 
 spkv_status launch_prefix(const Args &a, const Plan &p, int d, hipStream_t st) {
@@ -908,13 +1008,14 @@ spkv_status launch_prefix(const Args &a, const Plan &p, int d, hipStream_t st) {
     return check_launch("prefix_mfma_kernel");
 }
 
-spkv_status launch_merge(const Args &a, int d, float *out, float *lse, hipStream_t st) {
-    const int64_t rows = (int64_t)a.B * a.Hq;
+spkv_status launch_merge(const Args &a, int d, float *out, float *lse, const FlatLaunch &fr, const FlatLaunch &fp,
+                         hipStream_t st) {
+    const int64_t rows = (int64_t)fr.nreq * a.Hq;
     if (rows == 0) return SPKV_OK;
     dim3 grid((unsigned)((rows + 3) / 4)), block(256);
     TimedLaunch tl(SPKV_KERNEL_MERGE, st);
-    if (d == 128) merge_kernel<128><<<grid, block, 0, st>>>(a, out, lse);
-    else merge_kernel<64><<<grid, block, 0, st>>>(a, out, lse);
+    if (d == 128) merge_kernel<128><<<grid, block, 0, st>>>(a, out, lse, fr, fp);
+    else merge_kernel<64><<<grid, block, 0, st>>>(a, out, lse, fr, fp);
     return check_launch("merge_kernel");
 }
 
@@ -952,6 +1053,7 @@ Args make_args(const spkv_batch *b, const spkv_kv *kv, const Plan &p, void *ws) 
     a.flat_tau = p.flat_chunk;
     a.prefix_tau = p.prefix_chunk > 0 ? p.prefix_chunk : 1;
     a.prefix_granule = p.prefix_as_flat ? spkv::kFlatGranule : spkv::kPrefixKeyTile;
+    a.prefix_mode = !p.run_prefix ? 0 : (p.prefix_as_flat ? 2 : 1);
     a.cascade = p.cascade;
     return a;
 }
@@ -971,14 +1073,25 @@ spkv_status run_decode(const spkv_batch *b, const spkv_kv *kv, const int32_t *ca
     Args a = make_args(b, kv, p, ws);
     hipStream_t hs = (hipStream_t)stream;
     const bool bf16 = b->dtype == SPKV_DTYPE_BF16;
-    if (p.run_prefix) {
-        st = bf16 ? launch_prefix(a, p, b->head_dim, hs)
-                  : launch_flat(a, false, b->head_dim, kPartPrefix, p.prefix_splits, hs);
+    if (p.run_prefix && bf16) {
+        st = launch_prefix(a, p, b->head_dim, hs);
         if (st != SPKV_OK) return st;
     }
-    st = launch_flat(a, bf16, b->head_dim, kPartRest, p.flat_splits, hs);
-    if (st != SPKV_OK) return st;
-    return launch_merge(a, b->head_dim, out, lse, hs);
+    // Sub-batch i is entry i of both paged passes.
+    for (size_t i = 0; i < p.flat.size(); ++i) {
+        if (p.run_prefix && !bf16) {
+            st = launch_flat(a, false, b->head_dim, kPartPrefix, p.pflat[i], p.flat_head_groups, hs);
+            if (st != SPKV_OK) return st;
+        }
+        st = launch_flat(a, bf16, b->head_dim, kPartRest, p.flat[i], p.flat_head_groups, hs);
+        if (st != SPKV_OK) return st;
+    }
+    static const FlatLaunch kNone{};
+    for (size_t i = 0; i < p.flat.size(); ++i) {
+        st = launch_merge(a, b->head_dim, out, lse, p.flat[i], p.prefix_as_flat && p.run_prefix ? p.pflat[i] : kNone, hs);
+        if (st != SPKV_OK) return st;
+    }
+    return SPKV_OK;
 }
 
 spkv_status check_kv_shape(int32_t hkv, int32_t d, int32_t dtype) {

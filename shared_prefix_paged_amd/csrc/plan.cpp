@@ -44,12 +44,12 @@ spkv_status validate_batch(const spkv_batch *b, const spkv_kv *kv) {
     if (b->num_q_heads / b->num_kv_heads > kMaxGqa) return fail(SPKV_E_INVAL, "GQA group size must be <= 8");
     if (b->head_dim != 64 && b->head_dim != 128) return fail(SPKV_E_INVAL, "head_dim must be 64 or 128");
     if (b->dtype != SPKV_DTYPE_BF16 && b->dtype != SPKV_DTYPE_F32) return fail(SPKV_E_INVAL, "unknown dtype");
-    if (!std::isfinite(b->scale)) return fail(SPKV_E_INVAL, "scale must be finite");
+    if (!std::isfinite(b->scale) || !(b->scale > 0.f)) return fail(SPKV_E_INVAL, "scale must be finite and positive");
     if (b->num_groups < 0 || b->num_groups > kMaxGroups) return fail(SPKV_E_INVAL, "num_groups must be 0..512");
     if (b->page_size < 1 || b->max_blocks < 0) return fail(SPKV_E_INVAL, "bad page_size/max_blocks");
     const int B = b->batch, ng = b->num_groups;
-    if (B > 0 && (!b->q || !b->group_of || !b->cold_lens || !b->host_cold_lens))
-        return fail(SPKV_E_INVAL, "q, group_of, cold_lens and host_cold_lens are required");
+    if (B > 0 && (!b->q || !b->group_of || !b->cold_lens || !b->host_cold_lens || !b->host_group_of))
+        return fail(SPKV_E_INVAL, "q, group_of, cold_lens and their host copies are required");
     if (B > 0 && b->max_blocks > 0 && !b->block_tables) return fail(SPKV_E_INVAL, "block_tables is required");
     if (ng > 0 && (!b->group_indptr || !b->group_members || !b->hot_base || !b->hot_len ||
                    !b->host_group_indptr || !b->host_hot_base || !b->host_hot_len))
@@ -64,6 +64,10 @@ spkv_status validate_batch(const spkv_batch *b, const spkv_kv *kv) {
                 return fail(SPKV_E_INVAL, "group " + std::to_string(g) + " slab exceeds the HOT capacity");
         }
         if (b->host_group_indptr[ng] > B) return fail(SPKV_E_INVAL, "more group members than requests");
+    }
+    for (int i = 0; i < B; ++i) {
+        if (b->host_group_of[i] < -1 || b->host_group_of[i] >= ng)
+            return fail(SPKV_E_INVAL, "group_of[" + std::to_string(i) + "] outside [-1, num_groups)");
     }
     const int64_t cap_tokens = (int64_t)b->max_blocks * b->page_size;
     for (int i = 0; i < B; ++i) {
@@ -83,6 +87,42 @@ spkv_status validate_batch(const spkv_batch *b, const spkv_kv *kv) {
 
 static inline bool mask_get(const GroupMask &m, int g) { return (m.bits[g >> 5] >> (g & 31)) & 1u; }
 
+// Stream-K launches of one paged pass over per-request lengths L (sub-batches
+// of at most kFlatArgReqs requests).  Each launch gets as many equal token
+// ranges per head group as one full round of resident blocks, no shorter than
+// kFlatMinTokens, and few enough that no request spans more than
+// kFlatSplitCap ranges.
+static std::vector<FlatLaunch> plan_flat(const std::vector<int64_t> &L, int head_groups, int hpb, int32_t num_cus) {
+    std::vector<FlatLaunch> out;
+    const int B = (int)L.size();
+    const int64_t resident = std::max<int64_t>(1, (int64_t)num_cus * kFlatWaveSlots / hpb / head_groups);
+    for (int b0 = 0; b0 < B; b0 += kFlatArgReqs) {
+        FlatLaunch f{};
+        f.b0 = b0;
+        f.nreq = std::min(kFlatArgReqs, B - b0);
+        int64_t T = 0, max_len = 0;
+        for (int i = 0; i < f.nreq; ++i) {
+            f.offs[i] = (int32_t)T;
+            T += L[(size_t)(b0 + i)];
+            max_len = std::max<int64_t>(max_len, L[(size_t)(b0 + i)]);
+        }
+        f.offs[f.nreq] = (int32_t)T;
+        f.total = T;
+        if (T == 0) {            // kept (blocks = 0) so sub-batch i is entry i of every pass
+            out.push_back(f);
+            continue;
+        }
+        int64_t nb = std::min<int64_t>(resident, (T + kFlatMinTokens - 1) / kFlatMinTokens);
+        nb = std::max<int64_t>(nb, 1);
+        auto parts = [&](int64_t n) { return (max_len + T / n - 1) / (T / n) + 1; };
+        while (nb > 1 && parts(nb) > kFlatSplitCap) nb = std::max<int64_t>(1, nb * 3 / 4);
+        f.blocks = (int32_t)nb;
+        f.max_parts = (int32_t)std::min<int64_t>(kFlatSplitCap, parts(nb));
+        out.push_back(f);
+    }
+    return out;
+}
+
 spkv_status make_plan(const spkv_batch *b, const int32_t *cascade, int32_t num_cus, Plan *p) {
     *p = Plan{};
     const int B = b->batch, ng = b->num_groups, Hkv = b->num_kv_heads, D = b->head_dim;
@@ -91,51 +131,36 @@ spkv_status make_plan(const spkv_batch *b, const int32_t *cascade, int32_t num_c
     for (int g = 0; g < ng; ++g)
         if (!cascade || cascade[g]) p->cascade.bits[g >> 5] |= 1u << (g & 31);
 
-    // Member ids are device-only; sizing needs only per-group counts and
-    // lengths plus the COLD lengths.
     const bool bf16 = b->dtype == SPKV_DTYPE_BF16;
-    int64_t flat_total = 0;
-    int64_t flat_max_len = 0;
-    for (int i = 0; i < B; ++i) {
-        flat_total += b->host_cold_lens[i];
-        flat_max_len = std::max<int64_t>(flat_max_len, b->host_cold_lens[i]);
-    }
-    int64_t prefix_work = 0;        // bf16: (row tiles x keys) units; f32: request-prefix tokens
+    int64_t prefix_work = 0;        // row tiles x keys of the MFMA prefix pass
     int64_t max_m = 0, max_lp_c = 0;
     for (int g = 0; g < ng; ++g) {
         const int64_t n = b->host_group_indptr[g + 1] - b->host_group_indptr[g];
         const int64_t lp = b->host_hot_len[g];
-        if (n == 0 || lp == 0) continue;
-        if (mask_get(p->cascade, g)) {
-            max_m = std::max<int64_t>(max_m, n * G);
-            max_lp_c = std::max<int64_t>(max_lp_c, lp);
-            if (lp < kSplitPBelow) p->prefix_split_p = true;
-        } else {
-            flat_total += n * lp;
-        }
+        if (n == 0 || lp == 0 || !mask_get(p->cascade, g)) continue;
+        max_m = std::max<int64_t>(max_m, n * G);
+        max_lp_c = std::max<int64_t>(max_lp_c, lp);
+        if (lp < kSplitPBelow) p->prefix_split_p = true;
     }
-    // Per-request maximum of the flat length: a dense-mode member carries Lp + Ls.
+
+    // ---- flat pass (stream-K over each sub-batch's concatenated tokens) -----
+    const int hpb = std::min(Hkv, kFlatWaves);
+    p->flat_head_groups = (Hkv + hpb - 1) / hpb;
     {
-        // Bound from the host lists: the longest COLD length plus the longest dense-mode Lp.
-        int64_t max_dense_lp = 0;
-        for (int g = 0; g < ng; ++g) {
-            const int64_t n = b->host_group_indptr[g + 1] - b->host_group_indptr[g];
-            if (n > 0 && !mask_get(p->cascade, g)) max_dense_lp = std::max<int64_t>(max_dense_lp, b->host_hot_len[g]);
+        std::vector<int64_t> L((size_t)B);
+        for (int i = 0; i < B; ++i) {
+            const int g = b->host_group_of[i];
+            const bool dense_member = g >= 0 && !mask_get(p->cascade, g);
+            L[(size_t)i] = b->host_cold_lens[i] + (dense_member ? b->host_hot_len[g] : 0);
         }
-        flat_max_len += max_dense_lp;
+        p->flat = plan_flat(L, p->flat_head_groups, hpb, num_cus);
     }
-
-    // ---- flat pass --------------------------------------------------------
-    const int hpb = std::min(Hkv, 4);                 // KV heads (waves) per flat block
-    const int64_t blocks_per_item = (Hkv + hpb - 1) / hpb;
-    const int64_t target_items = std::max<int64_t>(1, (int64_t)num_cus * 8 / blocks_per_item);
-    int64_t tau = (flat_total + target_items - 1) / target_items;
-    tau = std::max<int64_t>(tau, 128);
-    tau = (tau + kFlatGranule - 1) / kFlatGranule * kFlatGranule;
-    p->flat_chunk = (int32_t)std::min<int64_t>(tau, 1 << 20);
-    // Every request's chunk is >= flat_chunk, so ceil(max_len / flat_chunk) (capped) bounds its splits.
-    p->flat_splits = std::min<int32_t>(kFlatSplitCap, splits_for(flat_max_len, p->flat_chunk));
-
+    p->flat_splits = 0;
+    p->flat_chunk = 0;
+    for (const auto &f : p->flat) {
+        p->flat_splits = std::max(p->flat_splits, f.max_parts);
+        if (f.blocks > 0) p->flat_chunk = std::max<int32_t>(p->flat_chunk, (int32_t)(f.total / f.blocks));
+    }
     // ---- prefix pass ------------------------------------------------------
     p->prefix_as_flat = !bf16;
     p->run_prefix = max_lp_c > 0;
@@ -157,17 +182,21 @@ spkv_status make_plan(const spkv_batch *b, const int32_t *cascade, int32_t num_c
         p->prefix_chunk = (int32_t)std::min<int64_t>(pt, 1 << 20);
         p->prefix_splits = std::min<int32_t>(kPrefixSplitCap, splits_for(max_lp_c, p->prefix_chunk));
     } else if (p->run_prefix) {
-        // float32: prefix part of cascade groups runs as a per-request pass over the slab.
-        int64_t total = 0;
-        for (int g = 0; g < ng; ++g) {
-            const int64_t n = b->host_group_indptr[g + 1] - b->host_group_indptr[g];
-            if (mask_get(p->cascade, g)) total += n * b->host_hot_len[g];
+        // float32: the prefix part of cascade groups runs as a paged pass over the slab.
+        std::vector<int64_t> L((size_t)B);
+        for (int i = 0; i < B; ++i) {
+            const int g = b->host_group_of[i];
+            L[(size_t)i] = (g >= 0 && mask_get(p->cascade, g)) ? b->host_hot_len[g] : 0;
         }
-        int64_t pt = (total + target_items - 1) / target_items;
-        pt = std::max<int64_t>(pt, 128);
-        pt = (pt + kFlatGranule - 1) / kFlatGranule * kFlatGranule;
-        p->prefix_chunk = (int32_t)std::min<int64_t>(pt, 1 << 20);
-        p->prefix_splits = std::min<int32_t>(kPrefixSplitCap, splits_for(max_lp_c, p->prefix_chunk));
+        p->pflat = plan_flat(L, p->flat_head_groups, hpb, num_cus);
+        p->prefix_splits = 0;
+        p->prefix_chunk = 0;
+        for (const auto &f : p->pflat) {
+            p->prefix_splits = std::max(p->prefix_splits, f.max_parts);
+            if (f.blocks > 0) p->prefix_chunk = std::max<int32_t>(p->prefix_chunk, (int32_t)(f.total / f.blocks));
+        }
+        p->run_prefix = false;
+        for (const auto &f : p->pflat) p->run_prefix = p->run_prefix || f.blocks > 0;
         p->prefix_waves = 0;
         p->prefix_mtiles = 0;
     }
@@ -176,11 +205,8 @@ spkv_status make_plan(const spkv_batch *b, const int32_t *cascade, int32_t num_c
     // Item counts (informational).
     p->flat_items = 0;
     p->prefix_items = 0;
-    for (int i = 0; i < B; ++i) {
-        // cascade members have only their COLD tokens in the flat pass; dense members add Lp,
-        // which the host cannot attribute without member ids, so count COLD-only here.
-        p->flat_items += splits_for(b->host_cold_lens[i], chunk_for(b->host_cold_lens[i], p->flat_chunk, kFlatSplitCap, kFlatGranule));
-    }
+    for (const auto &f : p->flat) p->flat_items += (int64_t)f.blocks * p->flat_head_groups;
+    for (const auto &f : p->pflat) p->prefix_items += (int64_t)f.blocks * p->flat_head_groups;
     for (int g = 0; g < ng; ++g) {
         const int64_t n = b->host_group_indptr[g + 1] - b->host_group_indptr[g];
         const int64_t lp = b->host_hot_len[g];
@@ -190,11 +216,7 @@ spkv_status make_plan(const spkv_batch *b, const int32_t *cascade, int32_t num_c
                 const int64_t mt = 32 * p->prefix_waves;
                 p->prefix_items += Hkv * ((n * G + mt - 1) / mt) *
                                    splits_for(lp, chunk_for(lp, p->prefix_chunk, kPrefixSplitCap, kPrefixKeyTile));
-            } else {
-                p->prefix_items += n * splits_for(lp, chunk_for(lp, p->prefix_chunk, kPrefixSplitCap, kFlatGranule));
             }
-        } else {
-            p->flat_items += n * splits_for(lp, chunk_for(lp, p->flat_chunk, kFlatSplitCap, kFlatGranule));
         }
     }
     const int64_t rows = (int64_t)B * b->num_q_heads;

@@ -281,6 +281,7 @@ class DecodeBatch:
         self.struct = A.spkv_batch(
             int(B), int(Hq), int(num_kv_heads), int(d), dtype_code(q), sc, _dp(self.q),
             ng, _dp(self.group_of), _dp(self.indptr), _dp(self.members), _dp(self.base), _dp(self.len),
+            self.group_of_h.ctypes.data if B else None,
             self.indptr_h.ctypes.data if ng else None, self.base_h.ctypes.data if ng else None,
             self.len_h.ctypes.data if ng else None,
             int(page_size), self.max_blocks, _dp(self.tables), _dp(self.lens), self.lens_h.ctypes.data)
