@@ -222,7 +222,8 @@ typedef struct spkv_batch {
     const int32_t *group_indptr;   /* device [ng+1]: members of g are group_members[indptr[g] .. indptr[g+1]) */
     const int32_t *group_members;  /* device: request ids; request b appears once, in group group_of[b] */
     const int64_t *hot_base;       /* device [ng]: slab base (token slot) */
-    const int32_t *hot_len;        /* device [ng]: prefix length Lp_g >= 0 */
+    const int32_t *hot_len;        /* device [ng]: prefix length Lp_g >= 0; one head's slab
+                                      (Lp_g * d * element size) must stay below 4 GiB */
     const int32_t *host_group_of;     /* host copies of group_of and of the three group arrays above */
     const int32_t *host_group_indptr;
     const int64_t *host_hot_base;

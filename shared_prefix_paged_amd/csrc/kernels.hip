@@ -145,26 +145,108 @@ __device__ __forceinline__ float fdot2(uint32_t a, uint32_t b, float c) {
 }
 
 // ---------------------------------------------------------------------------
-// Flat paged pass.  One block = one (chunk, request) and up to 4 KV heads,
-// one wave per head.  Inside a wave, LPT lanes hold one token's K (or V) row
-// as 16-byte pieces, so a wave-wide load covers TPW tokens; each group of LPT
-// lanes keeps its own online-softmax state, combined once at the end.
-//
-// Memory pipeline: the loads of the next TPI tokens are issued before the
-// current TPI tokens are computed (two register stages), and the row codes
-// (HOT slab row or COLD slot row, one per lane for 64 tokens) of the next
-// 64-token block are fetched one block ahead, so a wave always has a full
-// iteration of K/V loads in flight.
+// Global->LDS DMA (global_load_lds_*): lane l's bytes land at M0 + size * l.
+// The compiler does not track these loads, so every wait on them is an
+// explicit s_waitcnt; loads the compiler does track are only ever counted
+// conservatively by it (extra loads in flight make its waits stricter).
 // ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) char lds_char_t;
 
-// Rows of TPI tokens (U wave-wide loads of K and V) held in registers.
-template <int U>
-struct KVStage {
-    u32x4_t k[U], v[U];
-    bool valid[U];
+__device__ __forceinline__ uint32_t lds_offset(const void *p) {
+    return (uint32_t)(uintptr_t)(const lds_char_t *)p;
+}
+
+// One wave-wide global->LDS copy: this lane's 16 bytes (at gbase + voff) land
+// at lds_base + 16 * lane.  gbase and lds_base must be wave-uniform.  M0 (the
+// LDS base of the copy) is saved and restored around the instruction; the
+// s_nop covers the M0-write hazard.
+__device__ __forceinline__ void dma16(const void *gbase, uint32_t voff, uint32_t lds_base) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(gbase), "s"(lds_base)
+        : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Same with a 64-bit address per lane (any pool size).
+__device__ __forceinline__ void dma16_at(const void *addr, uint32_t lds_base) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(addr), "s"(lds_base)
+        : "memory");
+}
+
+// 4 bytes per lane: lane l's dword (at gbase + voff) lands at lds_base + 4 * l.
+__device__ __forceinline__ void dma4(const void *gbase, uint32_t voff, uint32_t lds_base) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(gbase), "s"(lds_base)
+        : "memory");
+}
+
+// Wait until at most N vector-memory loads of this wave are in flight and
+// every LDS access it issued has completed.
+template <int N>
+__device__ __forceinline__ void wait_vm_lds() {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
+}
+
+// ---------------------------------------------------------------------------
+// Flat paged pass.  A block takes one token range of a stream-K split (see
+// FlatLaunch) for up to 4 KV heads, one wave per head.  LPT lanes hold one
+// token's K (or V) row as 16-byte pieces, so one wave-wide access covers TPW
+// tokens; each group of LPT lanes keeps its own online-softmax state, and the
+// groups are combined once per range.
+//
+// Memory pipeline: K/V rows are gathered straight into LDS by DMA (one 64-bit
+// address per lane), through a ring of kFlatStages stages per wave that runs
+// kFlatStages-1 stages ahead of the compute, so data in flight occupies no
+// VGPRs.  A stage is one wave-wide DMA of K and one of V (TPW tokens, 2 KB).
+// Row codes (HOT slab row or COLD slot row, bit 31 = HOT) are built per
+// 64-token block, one token per lane; the block-table entries of the next
+// block are DMA'd into LDS a block ahead, so nothing in the loop waits on a
+// load the compiler tracks and all waits are explicit vmcnt counts.
+// ---------------------------------------------------------------------------
+constexpr int kFlatStages = 4;
+
+template <bool BF16, int D>
+struct FlatGeom {
+    static constexpr int ESZ = BF16 ? 2 : 4;
+    static constexpr int VEC = 16 / ESZ;         // elements per 16-byte piece
+    static constexpr int LPT = D / VEC;          // lanes per token row
+    static constexpr int TPW = 64 / LPT;         // tokens per stage
+    static constexpr int SPB = 64 / TPW;         // stages per 64-token block
+    static constexpr int ROWB = D * ESZ;         // bytes per K/V row
+    static constexpr int STAGEB = 2048;          // K (1 KB) then V (1 KB)
+    static constexpr int TABB = 256;             // 64 block-table entries
+    static constexpr int WAVEB = kFlatStages * STAGEB + TABB;
+    static_assert(TPW * ROWB == 1024, "a stage operand is one 1 KB wave-wide DMA");
+    static_assert(kFlatStages - 1 < SPB, "prologue stays inside the first 64-token block");
+    static_assert((kFlatStages & (kFlatStages - 1)) == 0, "ring index is a mask");
 };
 
-// Occupancy: 4 waves per SIMD (<= 128 VGPRs) for group sizes up to 5.
 // Range (block) index containing token x when T tokens are cut into nb
 // ranges [floor(k*T/nb), floor((k+1)*T/nb)).
 __device__ __forceinline__ int range_of(int64_t x, int64_t T, int nb) {
@@ -187,18 +269,14 @@ __device__ __forceinline__ int flat_parts(const FlatLaunch &f, int i, int *first
 
 // Online softmax of the G query rows of KV head h over tokens [t0, t1) of
 // request b; the normalised partial state goes to partial slot `slot`.
+// `ring` is this wave's LDS area (FlatGeom::WAVEB bytes), `ring_off` its LDS
+// address.
 template <bool BF16, int D, int G>
 __device__ __forceinline__ void attend_range(const Args &a, const Req &r, int b, int h, int t0, int t1, int slot,
-                                             int lane) {
-    constexpr int ESZ = BF16 ? 2 : 4;
-    constexpr int VEC = 16 / ESZ;            // elements per 16-byte piece
-    constexpr int LPT = D / VEC;             // lanes per token row
-    constexpr int TPW = 64 / LPT;            // tokens per wave-wide load
-    constexpr int U = (G <= 4) ? 2 : 1;      // wave-wide loads per operand per iteration (two stages in flight)
-    constexpr int TPI = TPW * U;             // tokens per iteration
-    constexpr int IPB = 64 / TPI;            // iterations per 64-token block
-    static_assert(64 % TPI == 0, "iteration must divide 64 tokens");
-    static_assert(IPB % 2 == 0, "iterations of a 64-token block come in pairs (two stages)");
+                                             int lane, char *ring, uint32_t ring_off) {
+    using FG = FlatGeom<BF16, D>;
+    constexpr int S = kFlatStages;
+    constexpr int VEC = FG::VEC, LPT = FG::LPT, TPW = FG::TPW, SPB = FG::SPB;
     constexpr float kRescaleSlack = 8.f;     // see the prefix kernel: exact for any reference
 
     const int sub = lane % LPT;              // 16-byte piece of the row
@@ -212,50 +290,65 @@ __device__ __forceinline__ void attend_range(const Args &a, const Req &r, int b,
     const int32_t *table = a.tables + (int64_t)b * a.max_blocks;
     const int64_t num_pages = a.cold_slots / a.page_size;
     const uint32_t hot_row0 = (uint32_t)(r.base * a.Hkv + (int64_t)h * r.lp);
+    const int32_t *tab_lds = (const int32_t *)(ring + S * FG::STAGEB);
+    const uint32_t tab_off = ring_off + S * FG::STAGEB;
 
-    // Row code of token blk + lane: bit 31 = HOT, low bits = row index.  Built
-    // in two steps so the block-table load can be issued a 64-token block
-    // before its value is needed: a load consumed right away would make the
-    // wave wait for every K/V load issued before it (vmcnt retires in order).
-    auto table_entry = [&](int blk) -> int32_t {
-        const int t = min(blk + lane, t1 - 1);
-        return t < r.lp ? 0 : table[(t - r.lp) / a.page_size];
-    };
-    auto row_code = [&](int blk, int32_t entry) -> uint32_t {
-        const int t = min(blk + lane, t1 - 1);
+    // Token of 64-block n taken by this lane (clamped into the range), and the
+    // first block-table index the block needs.
+    auto lane_token = [&](int n) { return min(t0 + 64 * n + lane, t1 - 1); };
+    auto first_entry = [&](int n) { return (max(t0 + 64 * n, r.lp) - r.lp) / a.page_size; };
+    auto block_has_cold = [&](int n) { return t0 + 64 * n < t1 && t0 + 64 * n + 63 >= r.lp; };
+    auto code_of = [&](int t, int32_t entry) -> uint32_t {
         if (t < r.lp) return 0x80000000u | (hot_row0 + (uint32_t)t);
-        const int tc = t - r.lp;
         int64_t page = entry;
         page = page < 0 ? 0 : (page >= num_pages ? num_pages - 1 : page);
-        return (uint32_t)((page * a.page_size + tc % a.page_size) * a.Hkv + h);
+        return (uint32_t)((page * a.page_size + (t - r.lp) % a.page_size) * a.Hkv + h);
     };
-    // Issue the loads of iteration j (tokens t0 + j*TPI ...) with the row codes of its 64-block.
-    auto issue = [&](KVStage<U> &st, int j, uint32_t code) {
-        const int base = (j % IPB) * TPI;
-        const int nblk = min(64, t1 - (t0 + (j / IPB) * 64));
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int ti = base + u * TPW + grp;            // token index inside the 64-block
-            st.valid[u] = ti < nblk;
-            // lane ti of `code` already holds the row of min(token, t1 - 1)
-            const uint32_t c = (uint32_t)__shfl((int)code, ti, 64);
-            const bool hot = c >> 31;
-            const int64_t off = ((int64_t)(c & 0x7fffffffu) * D + sub * VEC) * ESZ;
-            st.k[u] = *(const u32x4_t *)((hot ? khot : kcold) + off);
-            st.v[u] = *(const u32x4_t *)((hot ? vhot : vcold) + off);
-        }
+    // Table entries e0 .. e0+63 of block n into the LDS table area.
+    auto table_dma = [&](int n) {
+        const int e = max(0, min(first_entry(n) + lane, a.max_blocks - 1));
+        dma4(table, (uint32_t)e * 4u, tab_off);
+    };
+    // Row codes of block n from the LDS table (its DMA has landed).
+    auto code_from_lds = [&](int n) -> uint32_t {
+        const int t = lane_token(n);
+        int32_t entry = 0;
+        if (t >= r.lp) entry = tab_lds[max(0, min((t - r.lp) / a.page_size - first_entry(n), 63))];
+        return code_of(t, entry);
     };
 
-    // Query rows in registers.
+    // Query rows in registers, and the row codes of block 0, loaded (and
+    // consumed) before any DMA is in flight.
     uint32_t qw[G][4];
     {
-        const char *qb = (const char *)a.q + ((int64_t)row0 * D + sub * VEC) * ESZ;
+        const char *qb = (const char *)a.q + ((int64_t)row0 * D + sub * VEC) * FG::ESZ;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            u32x4_t v = *(const u32x4_t *)(qb + (int64_t)g * D * ESZ);
+            u32x4_t v = *(const u32x4_t *)(qb + (int64_t)g * D * FG::ESZ);
             qw[g][0] = v.x; qw[g][1] = v.y; qw[g][2] = v.z; qw[g][3] = v.w;
         }
     }
+    uint32_t code;
+    {
+        const int t = lane_token(0);
+        int32_t entry = 0;
+        if (t >= r.lp) entry = table[max(0, min((t - r.lp) / a.page_size, a.max_blocks - 1))];
+        code = code_of(t, entry);
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) asm volatile("" ::"v"(qw[g][0]), "v"(qw[g][1]), "v"(qw[g][2]), "v"(qw[g][3]));
+    asm volatile("" ::"v"(code));
+
+    // Stage j: tokens t0 + j*TPW + grp, LDS slot j % S.
+    auto issue = [&](int j) {
+        const int ti = (j % SPB) * TPW + grp;    // token inside its 64-block; lane ti holds its code
+        const uint32_t c = (uint32_t)__shfl((int)code, ti, 64);
+        const bool hot = c >> 31;
+        const int64_t off = (int64_t)(c & 0x7fffffffu) * FG::ROWB + sub * 16;
+        const uint32_t dst = ring_off + (uint32_t)((j & (S - 1)) * FG::STAGEB);
+        dma16_at((hot ? khot : kcold) + off, dst);
+        dma16_at((hot ? vhot : vcold) + off, dst + 1024);
+    };
 
     float m[G], l[G], acc[G][VEC];
 #pragma unroll
@@ -267,95 +360,75 @@ __device__ __forceinline__ void attend_range(const Args &a, const Req &r, int b,
     }
     const float c2 = a.scale_log2;
 
-    auto compute = [&](const KVStage<U> &st) {
-        float sc[U][G];
+    auto compute = [&](int j) {
+        const char *st = ring + (j & (S - 1)) * FG::STAGEB + lane * 16;
+        const u32x4_t kk = *(const u32x4_t *)st;
+        const u32x4_t vv = *(const u32x4_t *)(st + 1024);
+        const bool valid = j * TPW + grp < t1 - t0;
+        float sc[G];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                float d;
-                if constexpr (BF16) {
-                    d = fdot2(qw[g][0], st.k[u].x, 0.f);
-                    d = fdot2(qw[g][1], st.k[u].y, d);
-                    d = fdot2(qw[g][2], st.k[u].z, d);
-                    d = fdot2(qw[g][3], st.k[u].w, d);
-                } else {
-                    d = __uint_as_float(qw[g][0]) * __uint_as_float(st.k[u].x);
-                    d = fmaf(__uint_as_float(qw[g][1]), __uint_as_float(st.k[u].y), d);
-                    d = fmaf(__uint_as_float(qw[g][2]), __uint_as_float(st.k[u].z), d);
-                    d = fmaf(__uint_as_float(qw[g][3]), __uint_as_float(st.k[u].w), d);
-                }
-                d = dpp_sum<LPT>(d);
-                sc[u][g] = st.valid[u] ? d : -INFINITY;   // raw q.k; scale folded below
+        for (int g = 0; g < G; ++g) {
+            float d;
+            if constexpr (BF16) {
+                d = fdot2(qw[g][0], kk.x, 0.f);
+                d = fdot2(qw[g][1], kk.y, d);
+                d = fdot2(qw[g][2], kk.z, d);
+                d = fdot2(qw[g][3], kk.w, d);
+            } else {
+                d = __uint_as_float(qw[g][0]) * __uint_as_float(kk.x);
+                d = fmaf(__uint_as_float(qw[g][1]), __uint_as_float(kk.y), d);
+                d = fmaf(__uint_as_float(qw[g][2]), __uint_as_float(kk.z), d);
+                d = fmaf(__uint_as_float(qw[g][3]), __uint_as_float(kk.w), d);
             }
+            d = dpp_sum<LPT>(d);
+            sc[g] = valid ? d * c2 : -INFINITY;   // log2 units
         }
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            float mx = sc[0][g];
-#pragma unroll
-            for (int u = 1; u < U; ++u) mx = fmaxf(mx, sc[u][g]);
-            mx *= c2;
-            if (mx > m[g] + kRescaleSlack) {     // rare after the first tokens
-                const float alpha = __builtin_amdgcn_exp2f(m[g] - mx);
-                m[g] = mx;
+            if (sc[g] > m[g] + kRescaleSlack) {     // rare after the first tokens
+                const float alpha = __builtin_amdgcn_exp2f(m[g] - sc[g]);
+                m[g] = sc[g];
                 l[g] *= alpha;
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) acc[g][e] *= alpha;
             }
             // m = -inf only while every token seen is masked (then p = 0, not NaN)
-            const float nm = m[g] == -INFINITY ? 0.f : -m[g];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                sc[u][g] = __builtin_amdgcn_exp2f(fmaf(sc[u][g], c2, nm));   // now the weight p
-                l[g] += sc[u][g];
-            }
+            const float nm = m[g] == -INFINITY ? 0.f : m[g];
+            sc[g] = __builtin_amdgcn_exp2f(sc[g] - nm);   // now the weight p
+            l[g] += sc[g];
         }
         // P.V with each value element widened once and used by all G rows.
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
+        for (int e = 0; e < VEC; ++e) {
+            const uint32_t w = vv[BF16 ? e / 2 : e];
+            const float v = BF16 ? ((e & 1) ? bf16hi(w) : bf16lo(w)) : __uint_as_float(w);
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                const uint32_t w = st.v[u][BF16 ? e / 2 : e];
-                const float v = BF16 ? ((e & 1) ? bf16hi(w) : bf16lo(w)) : __uint_as_float(w);
-#pragma unroll
-                for (int g = 0; g < G; ++g) acc[g][e] = fmaf(sc[u][g], v, acc[g][e]);
-            }
+            for (int g = 0; g < G; ++g) acc[g][e] = fmaf(sc[g], v, acc[g][e]);
         }
     };
 
-    // Steady state without data-dependent branches between a load and its use:
-    // the waitcnt the compiler places before each compute then only covers the
-    // stage being computed (vmcnt = loads of the other stage), not every load in
-    // flight.  Loads are issued for whole 64-token blocks; iterations past t1
-    // read the clamped last row and are masked, and the row codes / table
-    // entries of blocks past t1 are clamped to the last token, so every address
-    // stays inside the request.
-    const int n_it = (t1 - t0 + TPI - 1) / TPI;
-    uint32_t code = row_code(t0, table_entry(t0));   // row codes of the block being issued
-    int32_t entry_nxt = table_entry(t0 + 64);        // table entries of the block after it
-    KVStage<U> sa, sb;
-    issue(sa, 0, code);
-    bool live = true;
-    for (int blk = 0; live; ++blk) {
-#pragma unroll
-        for (int i = 0; i < IPB; i += 2) {
-            const int j = blk * IPB + i;
-            if (j >= n_it) {
-                live = false;
-                break;
-            }
-            issue(sb, j + 1, code);
-            compute(sa);
-            if (i + 2 == IPB) {
-                code = row_code(t0 + (blk + 1) * 64, entry_nxt);
-                entry_nxt = table_entry(t0 + (blk + 2) * 64);
-            }
-            issue(sa, j + 2, code);
-            compute(sb);
+    const int n_st = (t1 - t0 + TPW - 1) / TPW;
+    if (block_has_cold(1)) table_dma(1);
+    const int pro = min(S - 1, n_st);
+    for (int j = 0; j < pro; ++j) issue(j);
+    int j = 0;
+    for (; j + S - 1 < n_st; ++j) {
+        wait_vm_lds<2 * (S - 2)>();   // stage j has landed: only stages j+1 .. j+S-2 may be in flight
+        const int jn = j + S - 1;
+        if (jn % SPB == 0) {         // first stage of block n: its table entries landed with stage j
+            const int n = jn / SPB;
+            code = code_from_lds(n);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // table read done before it is overwritten
+            if (block_has_cold(n + 1)) table_dma(n + 1);
         }
+        issue(jn);
+        compute(j);
     }
+    wait_vm_lds<0>();
+    for (; j < n_st; ++j) compute(j);
 
     // Combine the TPW token groups of the wave (lanes sub, sub+LPT, ...).
+    // Every DMA has landed (waited above), so the ring may be reused.
     const int srow = slot;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -389,13 +462,18 @@ __device__ __forceinline__ void attend_range(const Args &a, const Req &r, int b,
 }
 
 // Occupancy: 4 waves per SIMD (<= 128 VGPRs) for group sizes up to 5.
+// Occupancy: 4 waves per SIMD (<= 128 VGPRs) up to G = 6, 3 above; the LDS
+// ring (4 x 8.25 KB per block of 4 waves) admits 4 blocks per CU.
 template <bool BF16, int D, int G>
-__global__ __launch_bounds__(256, (G <= 5 ? 4 : 2)) void flat_kernel(Args a, int part, FlatLaunch fl) {
+__global__ __launch_bounds__(256, (G <= 6 ? 4 : 3)) void flat_kernel(Args a, int part, FlatLaunch fl) {
+    extern __shared__ __attribute__((aligned(1024))) char flat_smem[];
     const int k = blockIdx.x;
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int h = blockIdx.y * kFlatWavesMax + wave;
     if (h >= a.Hkv) return;
+    char *ring = flat_smem + wave * FlatGeom<BF16, D>::WAVEB;
+    const uint32_t ring_off = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_offset(ring));
     const int64_t T = fl.total;
     const int nb = fl.blocks;
     const int64_t s0 = (T * k) / nb, s1 = (T * (k + 1)) / nb;
@@ -421,7 +499,7 @@ __global__ __launch_bounds__(256, (G <= 5 ? 4 : 2)) void flat_kernel(Args a, int
         const int t0 = lo + (int)(lo_s - o0);
         const int t1 = min(hi, lo + (int)(hi_s - o0));   // device data shorter than the plan: clamp
         if (t1 <= t0) continue;
-        attend_range<BF16, D, G>(a, r, b, h, t0, t1, slot0 + slot, lane);
+        attend_range<BF16, D, G>(a, r, b, h, t0, t1, slot0 + slot, lane, ring, ring_off);
     }
 }
 
@@ -450,34 +528,6 @@ __global__ __launch_bounds__(256, (G <= 5 ? 4 : 2)) void flat_kernel(Args a, int
 // banks.
 // ---------------------------------------------------------------------------
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) char lds_char_t;
-
-__device__ __forceinline__ uint32_t lds_offset(const void *p) {
-    return (uint32_t)(uintptr_t)(const lds_char_t *)p;
-}
-
-// One wave-wide global->LDS copy: this lane's 16 bytes (at gbase + voff) land
-// at lds_base + 16 * lane.  gbase and lds_base must be wave-uniform.  M0 (the
-// LDS base of the copy) is saved and restored around the instruction; the
-// s_nop covers the M0-write hazard.
-__device__ __forceinline__ void dma16(const void *gbase, uint32_t voff, uint32_t lds_base) {
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %3\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, %2\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(voff), "s"(gbase), "s"(lds_base)
-        : "memory");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
 __device__ __forceinline__ int swap_bits23(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
 
 // V tile chunk placement.  Logical 16-byte chunk c of LDS row r sits at
@@ -961,16 +1011,17 @@ template <bool BF16, int D>
 spkv_status launch_flat_d(const Args &a, int part, const FlatLaunch &f, int head_groups, hipStream_t st) {
     const int waves = a.Hkv < kFlatWavesMax ? a.Hkv : kFlatWavesMax;
     dim3 grid(f.blocks, head_groups), block(64 * waves);
+    const size_t lds = (size_t)waves * FlatGeom<BF16, D>::WAVEB;
     TimedLaunch tl(SPKV_KERNEL_FLAT, st);
     switch (a.G) {
-    case 1: flat_kernel<BF16, D, 1><<<grid, block, 0, st>>>(a, part, f); break;
-    case 2: flat_kernel<BF16, D, 2><<<grid, block, 0, st>>>(a, part, f); break;
-    case 3: flat_kernel<BF16, D, 3><<<grid, block, 0, st>>>(a, part, f); break;
-    case 4: flat_kernel<BF16, D, 4><<<grid, block, 0, st>>>(a, part, f); break;
-    case 5: flat_kernel<BF16, D, 5><<<grid, block, 0, st>>>(a, part, f); break;
-    case 6: flat_kernel<BF16, D, 6><<<grid, block, 0, st>>>(a, part, f); break;
-    case 7: flat_kernel<BF16, D, 7><<<grid, block, 0, st>>>(a, part, f); break;
-    case 8: flat_kernel<BF16, D, 8><<<grid, block, 0, st>>>(a, part, f); break;
+    case 1: flat_kernel<BF16, D, 1><<<grid, block, lds, st>>>(a, part, f); break;
+    case 2: flat_kernel<BF16, D, 2><<<grid, block, lds, st>>>(a, part, f); break;
+    case 3: flat_kernel<BF16, D, 3><<<grid, block, lds, st>>>(a, part, f); break;
+    case 4: flat_kernel<BF16, D, 4><<<grid, block, lds, st>>>(a, part, f); break;
+    case 5: flat_kernel<BF16, D, 5><<<grid, block, lds, st>>>(a, part, f); break;
+    case 6: flat_kernel<BF16, D, 6><<<grid, block, lds, st>>>(a, part, f); break;
+    case 7: flat_kernel<BF16, D, 7><<<grid, block, lds, st>>>(a, part, f); break;
+    case 8: flat_kernel<BF16, D, 8><<<grid, block, lds, st>>>(a, part, f); break;
     default: return fail(SPKV_E_INVAL, "unsupported GQA group size");
     }
     return check_launch("flat_kernel");

@@ -60,6 +60,8 @@ spkv_status validate_batch(const spkv_batch *b, const spkv_kv *kv) {
             if (b->host_group_indptr[g + 1] < b->host_group_indptr[g])
                 return fail(SPKV_E_INVAL, "group_indptr must be non-decreasing");
             if (b->host_hot_len[g] < 0 || b->host_hot_base[g] < 0) return fail(SPKV_E_INVAL, "negative hot_base/hot_len");
+            if ((int64_t)b->host_hot_len[g] * b->head_dim * 4 >= (int64_t(1) << 32))
+                return fail(SPKV_E_INVAL, "group " + std::to_string(g) + " prefix longer than a 4 GiB slab per head");
             if (kv && b->host_hot_base[g] + b->host_hot_len[g] > kv->hot_capacity)
                 return fail(SPKV_E_INVAL, "group " + std::to_string(g) + " slab exceeds the HOT capacity");
         }
