@@ -45,7 +45,49 @@ def parse():
     ap.add_argument("--contiguous", action="store_true", help="COLD pages handed out in order (no shuffle)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle timing sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="measured HBM traffic per launch (written by shared_prefix_paged_amd/profile_step.py)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only copy a MIB-MiB device buffer 5 times (counter calibration) and exit")
     return ap.parse_args()
+
+
+def copy_probe(mib: int) -> int:
+    """A plain device-to-device copy of known size: MIB MiB read and MIB MiB written per launch."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
+    return 0
+
+
+def source_digest() -> str:
+    """Digest of the sources that decide what the kernels read and write."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "shared_prefix_paged_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(path: str, config: str, mode: str, kernel: str):
+    """HBM bytes per launch of `kernel` from calibrated FETCH_SIZE + WRITE_SIZE
+    counters, if they were taken on the current sources; else None."""
+    try:
+        with open(path) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("sources") != source_digest():
+        return None
+    rec = t.get("runs", {}).get(f"{config}/{mode}", {}).get(kernel)
+    return None if rec is None else rec.get("traffic_bytes")
 
 
 def kv_bytes_per_token(hkv, d, esz):
@@ -54,6 +96,8 @@ def kv_bytes_per_token(hkv, d, esz):
 
 def main():
     args = parse()
+    if args.copy_probe:
+        return copy_probe(args.copy_probe)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
               "this build has no multi-GPU path.", file=sys.stderr)
@@ -145,11 +189,16 @@ def main():
     value = tokens / wall
 
     # ---- per-kernel durations from HIP events on the launch stream ----------
-    lens_before = batch.lens_h.copy()
+    # (the plan's per-request partial-state counts are recorded at every step
+    # for the byte accounting below)
+    per_step = []
     with R.KernelTimer() as kt:
-        tok2 = 0
         for _ in range(args.steps):
-            tok2 += one_step()
+            one_step()
+            choice = state["choice"]
+            casc = list(map(int, choice)) if len(choice) else None
+            fp, pp = batch.plan_parts(casc)
+            per_step.append((batch.lens_h.copy(), fp, pp, bool(len(choice) and choice[0])))
         torch.cuda.synchronize()
     kt_ms = {k: kt.read(k) for k in (A.SPKV_KERNEL_PREFIX, A.SPKV_KERNEL_FLAT, A.SPKV_KERNEL_MERGE,
                                      A.SPKV_KERNEL_CACHE)}
@@ -158,37 +207,32 @@ def main():
     plan = batch.plan(list(map(int, choice)) if len(choice) else None)
 
     # Algorithmic bytes / FLOPs of one launch, averaged over the profiled steps
-    # (the lengths grow by one token per step).
-    def chunk_for(n, tau, cap, gran):
-        c = max(tau, -(-n // cap))
-        return -(-c // gran) * gran
-
-    def splits_for(n, c):
-        return 0 if n <= 0 else -(-n // c)
-
+    # (the lengths grow by one token per step).  Paged pass: K and V rows of
+    # every token it attends, block-table entries of its COLD tokens, the
+    # query rows once per partial state, and the partial states it writes.
+    # Prefix pass: the HOT slab once, member queries, partial states.  Merge:
+    # every partial state, then O and LSE.
     rows = B * Hq
-    steps_lens = [lens_before + j + 1 for j in range(args.steps)]
-    lp_dense = np.zeros(B, np.int64) if cascade else lp_of
-    flat_bytes, flat_partial_bytes = [], 0.0
-    for L in steps_lens:
-        Lf = L + lp_dense
-        nf = sum(splits_for(int(x), chunk_for(int(x), plan.flat_chunk, plan.flat_split_cap, plan.flat_granule))
-                 for x in Lf)
-        flat_bytes.append(int(Lf.sum()) * kvb + 4 * int(np.sum(-(-L // P))) + rows * d * esz
-                          + Hq * nf * (d + 1) * 4)
-        flat_partial_bytes += Hq * nf * (d + 1) * 4 / len(steps_lens)
-    flat_bytes = float(np.mean(flat_bytes))
-    prefix_partial_bytes = 0.0
-    groups = [(int(lp), int(np.sum(wl.group_of == g))) for g, lp in enumerate(wl.group_prefix_len)]
-    prefix_bytes = prefix_flops = 0.0
-    if cascade:
-        for lp, n in groups:
-            npf = splits_for(lp, chunk_for(lp, plan.prefix_chunk, plan.prefix_split_cap, plan.prefix_granule))
-            prefix_bytes += lp * kvb + n * Hq * d * esz + n * Hq * npf * (d + 1) * 4
-            prefix_partial_bytes += n * Hq * npf * (d + 1) * 4
-            prefix_flops += 4.0 * n * Hq * lp * d
-    # merge: reads every partial state written by the two passes, writes O and LSE
-    merge_bytes = (flat_partial_bytes + prefix_partial_bytes) + rows * (d + 1) * 4
+    flat_b, prefix_b, prefix_f, merge_b = [], [], [], []
+    for L, fp, pp, casc in per_step:
+        Lf = L + (np.zeros(B, np.int64) if casc else lp_of)
+        part_bytes = Hq * int(fp.sum()) * (d + 1) * 4
+        flat_b.append(int(Lf.sum()) * kvb + 4 * int(np.sum(-(-L // P))) + Hq * int(fp.sum()) * d * esz + part_bytes)
+        pb = pf = ppart = 0.0
+        if casc:
+            for g, lp in enumerate(wl.group_prefix_len):
+                members = np.flatnonzero(wl.group_of == g)
+                if lp <= 0 or len(members) == 0:
+                    continue
+                npf = int(pp[members[0]])
+                pb += int(lp) * kvb + len(members) * Hq * d * esz + len(members) * Hq * npf * (d + 1) * 4
+                ppart += len(members) * Hq * npf * (d + 1) * 4
+                pf += 4.0 * len(members) * Hq * int(lp) * d
+        prefix_b.append(pb)
+        prefix_f.append(pf)
+        merge_b.append(part_bytes + ppart + rows * (d + 1) * 4)
+    flat_bytes, prefix_bytes = float(np.mean(flat_b)), float(np.mean(prefix_b))
+    prefix_flops, merge_bytes = float(np.mean(prefix_f)), float(np.mean(merge_b))
 
     kernels = {}
     for name, kid, nbytes, flops in (("prefix_mfma", A.SPKV_KERNEL_PREFIX, prefix_bytes, prefix_flops),
@@ -213,6 +257,7 @@ def main():
         roofline = {"bound": "hbm", "achieved": dk["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(dk["gbps"] / HBM_PEAK_GBPS, 4), "traffic": None}
     roofline["kernel"] = dom
+    roofline["traffic"] = measured_traffic(args.traffic, args.config, args.mode, dom)
     attn_us = sum(k["avg_us"] for k in kernels.values())
 
     # ---- oracle on the host cores, bounded sample ---------------------------

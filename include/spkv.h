@@ -311,23 +311,30 @@ spkv_status spkv_decode_step(const spkv_batch *batch, const spkv_kv *kv, const s
  * Plan inspection and kernel timing (measurement support).
  * ==================================================================== */
 typedef struct spkv_plan_info {
-    int32_t flat_chunk;            /* base tokens per flat work item (per request it may be larger) */
-    int32_t flat_splits;           /* max flat partials per row (grid x) */
-    int32_t prefix_chunk;          /* base keys per prefix work item */
+    int32_t flat_chunk;            /* tokens per range of the paged pass (stream-K; largest sub-batch) */
+    int32_t flat_splits;           /* max paged-pass partials of one request (<= flat_split_cap) */
+    int32_t prefix_chunk;          /* base keys per prefix work item (bf16 MFMA pass) */
     int32_t prefix_splits;         /* max prefix partials per row */
     int32_t prefix_waves;          /* waves per prefix work item (32 query rows each) */
     int32_t prefix_mtiles;         /* max row tiles per (group, KV head) */
-    int64_t flat_items;            /* non-empty flat work items */
+    int64_t flat_items;            /* paged-pass work items (ranges x KV-head groups) */
     int64_t prefix_items;          /* non-empty prefix work items */
     int64_t workspace_bytes;       /* bytes this plan uses */
-    int32_t flat_split_cap;        /* per request: chunk = roundup(max(flat_chunk, ceil(L / cap)), granule) */
-    int32_t flat_granule;
-    int32_t prefix_split_cap;      /* per group: same rule with prefix_chunk */
+    int32_t flat_split_cap;        /* bound on the paged-pass partials of one request */
+    int32_t flat_granule;          /* reserved (0) */
+    int32_t prefix_split_cap;      /* per group: chunk = roundup(max(prefix_chunk, ceil(Lp / cap)), granule) */
     int32_t prefix_granule;
 } spkv_plan_info;
 
-/* Plan the launch for a given per-group choice (host [ng]; NULL = all cascade). */
 spkv_status spkv_plan_query(const spkv_batch *batch, const int32_t *cascade, spkv_plan_info *out);
+
+/* Partial states the plan writes per request (host arrays of length B, filled
+ * by the call): flat_parts[b] by the paged pass, prefix_parts[b] per query row
+ * by the prefix part (0 without a cascade prefix).  The merge of request b
+ * combines flat_parts[b] + prefix_parts[b] states per query row ([GKV] Eq. (1)
+ * applied across all of them).  Either pointer may be NULL. */
+spkv_status spkv_plan_parts(const spkv_batch *batch, const int32_t *cascade, int32_t *flat_parts,
+                            int32_t *prefix_parts);
 
 #define SPKV_KERNEL_PREFIX  0   /* prefix contraction (bf16 MFMA) */
 #define SPKV_KERNEL_FLAT    1   /* paged pass: suffix part, or whole context when flat */

@@ -27,7 +27,6 @@ constexpr int kMaxKvHeads = 16;
 constexpr int kFlatSplitCap = 64;      // partials per row from the flat pass
 constexpr int kPrefixSplitCap = 64;    // partials per row from the prefix pass
 constexpr int kPrefixKeyTile = 32;     // keys per MFMA tile in the prefix kernel
-constexpr int kFlatGranule = 16;       // flat chunks are multiples of this many tokens
 constexpr int kFlatWaves = 4;          // KV heads (one wave each) per flat block
 constexpr int kFlatMinTokens = 64;     // shortest flat range per block
 constexpr int kFlatWaveSlots = 16;     // resident flat waves per CU (128 VGPRs)
@@ -54,6 +53,26 @@ struct FlatLaunch {
     int64_t total;                     // tokens of the sub-batch
     int32_t offs[kFlatArgReqs + 1];    // exclusive prefix sums of the request lengths
 };
+
+// Range (block) index containing token x when T tokens are cut into nb
+// ranges [floor(k*T/nb), floor((k+1)*T/nb)).
+SPKV_HD inline int range_of(int64_t x, int64_t T, int nb) {
+    int k = (int)((x * nb) / T);
+    if (k + 1 < nb && (T * (k + 1)) / nb <= x) ++k;
+    return k;
+}
+
+// Partial states written for request i of a flat launch, and its first range.
+SPKV_HD inline int flat_parts(const FlatLaunch &f, int i, int *first) {
+    const int64_t o0 = f.offs[i], o1 = f.offs[i + 1];
+    if (f.blocks <= 0 || o1 <= o0) {
+        *first = 0;
+        return 0;
+    }
+    const int k0 = range_of(o0, f.total, f.blocks);
+    *first = k0;
+    return range_of(o1 - 1, f.total, f.blocks) - k0 + 1;
+}
 
 // The launch plan of one decode call (host-computed, deterministic).
 struct Plan {

@@ -24,6 +24,8 @@ using spkv::fail;
 using spkv::FlatLaunch;
 using spkv::GroupMask;
 using spkv::Plan;
+using spkv::flat_parts;
+using spkv::range_of;
 
 namespace {
 
@@ -246,26 +248,6 @@ struct FlatGeom {
     static_assert(kFlatStages - 1 < SPB, "prologue stays inside the first 64-token block");
     static_assert((kFlatStages & (kFlatStages - 1)) == 0, "ring index is a mask");
 };
-
-// Range (block) index containing token x when T tokens are cut into nb
-// ranges [floor(k*T/nb), floor((k+1)*T/nb)).
-__device__ __forceinline__ int range_of(int64_t x, int64_t T, int nb) {
-    int k = (int)((x * nb) / T);
-    if (k + 1 < nb && (T * (k + 1)) / nb <= x) ++k;
-    return k;
-}
-
-// Partial states written for request i of a flat launch, and the first range.
-__device__ __forceinline__ int flat_parts(const FlatLaunch &f, int i, int *first) {
-    const int64_t o0 = f.offs[i], o1 = f.offs[i + 1];
-    if (f.blocks <= 0 || o1 <= o0) {
-        *first = 0;
-        return 0;
-    }
-    const int k0 = range_of(o0, f.total, f.blocks);
-    *first = k0;
-    return range_of(o1 - 1, f.total, f.blocks) - k0 + 1;
-}
 
 // Online softmax of the G query rows of KV head h over tokens [t0, t1) of
 // request b; the normalised partial state goes to partial slot `slot`.
@@ -1103,7 +1085,7 @@ Args make_args(const spkv_batch *b, const spkv_kv *kv, const Plan &p, void *ws) 
     a.flat_splits = p.flat_splits;
     a.flat_tau = p.flat_chunk;
     a.prefix_tau = p.prefix_chunk > 0 ? p.prefix_chunk : 1;
-    a.prefix_granule = p.prefix_as_flat ? spkv::kFlatGranule : spkv::kPrefixKeyTile;
+    a.prefix_granule = spkv::kPrefixKeyTile;
     a.prefix_mode = !p.run_prefix ? 0 : (p.prefix_as_flat ? 2 : 1);
     a.cascade = p.cascade;
     return a;

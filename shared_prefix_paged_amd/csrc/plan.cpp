@@ -268,9 +268,42 @@ spkv_status spkv_plan_query(const spkv_batch *batch, const int32_t *cascade, spk
     out->prefix_items = p.prefix_items;
     out->workspace_bytes = p.ws_bytes;
     out->flat_split_cap = kFlatSplitCap;
-    out->flat_granule = kFlatGranule;
+    out->flat_granule = 0;
     out->prefix_split_cap = kPrefixSplitCap;
-    out->prefix_granule = p.prefix_as_flat ? kFlatGranule : kPrefixKeyTile;
+    out->prefix_granule = kPrefixKeyTile;
+    return SPKV_OK;
+}
+
+spkv_status spkv_plan_parts(const spkv_batch *batch, const int32_t *cascade, int32_t *flat_parts_out,
+                            int32_t *prefix_parts_out) {
+    spkv_status st = validate_batch(batch, nullptr);
+    if (st != SPKV_OK) return st;
+    Plan p;
+    st = make_plan(batch, cascade, kPlanCUs, &p);
+    if (st != SPKV_OK) return st;
+    const int B = batch->batch;
+    int first = 0;
+    if (flat_parts_out) {
+        for (int b = 0; b < B; ++b) flat_parts_out[b] = 0;
+        for (const auto &f : p.flat)
+            for (int i = 0; i < f.nreq; ++i) flat_parts_out[f.b0 + i] = flat_parts(f, i, &first);
+    }
+    if (prefix_parts_out) {
+        for (int b = 0; b < B; ++b) prefix_parts_out[b] = 0;
+        if (p.prefix_as_flat) {
+            for (const auto &f : p.pflat)
+                for (int i = 0; i < f.nreq; ++i) prefix_parts_out[f.b0 + i] = flat_parts(f, i, &first);
+        } else if (p.run_prefix) {
+            for (int b = 0; b < B; ++b) {
+                const int g = batch->host_group_of[b];
+                if (g < 0 || !((p.cascade.bits[g >> 5] >> (g & 31)) & 1u)) continue;
+                const int64_t lp = batch->host_hot_len[g];
+                if (lp <= 0) continue;
+                prefix_parts_out[b] = std::min<int32_t>(
+                    p.prefix_splits, splits_for(lp, chunk_for(lp, p.prefix_chunk, kPrefixSplitCap, kPrefixKeyTile)));
+            }
+        }
+    }
     return SPKV_OK;
 }
 

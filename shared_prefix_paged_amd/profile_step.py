@@ -1,0 +1,160 @@
+"""Profiles the decode step of bench.py with rocprofv3 (on a machine with the GPU).
+
+    python shared_prefix_paged_amd/profile_step.py [--config C1] [--mode step] [--out DIR]
+
+Runs, each as its own rocprofv3 process (program directly after ``--``, from
+/tmp with TMPDIR=/tmp, under a hard time limit):
+
+  1. ``--kernel-trace --stats`` over ``bench.py`` (the timed command itself);
+  2. ``--pmc FETCH_SIZE`` and 3. ``--pmc WRITE_SIZE`` over a short bench run;
+  4./5. the same two counters over ``bench.py --copy-probe 256``, a plain
+     device copy that reads and writes 256 MiB, to turn counter readings into
+     bytes (factor = known bytes / counter reading).
+
+Writes ``profiles/<config>_<mode>_kernel_stats.md`` (per-kernel durations),
+``profiles/<config>_<mode>_traffic.md`` (counter readings, factors, bytes per
+launch) and updates ``profiles/traffic.json``, which bench.py reads for its
+roofline ``traffic`` field while the kernel sources are unchanged.  Raw
+rocprofv3 output stays in --out.  This script itself never touches the GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import json
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+KERNELS = {"flat_kernel": "flat_paged", "prefix_mfma_kernel": "prefix_mfma", "merge_kernel": "merge"}
+COPY_MIB = 256
+
+
+def kernel_key(name: str):
+    base = name.replace("(anonymous namespace)::", "")
+    base = base.split("<")[0].split("(")[0].replace("void ", "").strip()
+    return KERNELS.get(base)
+
+
+def rocprof(args, out_dir, tag, prog, limit=240):
+    cmd = ["rocprofv3"] + args + ["-f", "csv", "-d", os.path.join(out_dir, tag), "-o", tag, "--",
+                                  sys.executable] + prog
+    env = dict(os.environ, TMPDIR="/tmp")
+    print(f"[profile] {tag}: {' '.join(cmd)}", flush=True)
+    with open(os.path.join(out_dir, tag + ".log"), "w") as log:
+        r = subprocess.run(cmd, cwd="/tmp", env=env, stdout=log, stderr=subprocess.STDOUT, timeout=limit)
+    files = glob.glob(os.path.join(out_dir, tag, "**", f"{tag}_*.csv"), recursive=True)
+    # rocprofv3 may end with a signal after the program has finished and its
+    # results are complete; the csv files decide.
+    if not files:
+        raise RuntimeError(f"{tag}: rocprofv3 exited {r.returncode} without results")
+    return cmd, files
+
+
+def counter_means(files, counter):
+    sums, counts = {}, {}
+    for f in files:
+        if not f.endswith("counter_collection.csv"):
+            continue
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter:
+                continue
+            k = kernel_key(r["Kernel_Name"]) or r["Kernel_Name"]
+            sums[k] = sums.get(k, 0.0) + float(r["Counter_Value"])
+            counts[k] = counts.get(k, 0) + 1
+    return {k: (sums[k] / counts[k], counts[k]) for k in sums}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--config", default="C1")
+    ap.add_argument("--mode", default="step")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "profile"), help="raw rocprofv3 output")
+    ap.add_argument("--prof-dir", default=os.path.join(ROOT, "profiles"), help="where the summaries go")
+    a = ap.parse_args()
+    os.makedirs(a.out, exist_ok=True)
+    prof_dir = os.path.abspath(a.prof_dir)
+    os.makedirs(prof_dir, exist_ok=True)
+    bench = os.path.join(ROOT, "bench.py")
+    run = [bench, "--config", a.config, "--mode", a.mode, "--no-cpu-baseline"]
+    name = f"{a.config.lower()}_{a.mode}"
+
+    # 1. kernel trace + stats of the bench command
+    cmd, files = rocprof(["--kernel-trace", "--stats"], a.out, "stats",
+                         run + ["--steps", str(a.steps), "--warmup", str(a.warmup)])
+    stats = [f for f in files if f.endswith("kernel_stats.csv")]
+    lines = [f"# Kernel durations: {a.config}, mode {a.mode}", "",
+             "rocprofv3 kernel trace of one bench.py run (every kernel of the warmup, timed and",
+             "per-kernel-timing steps). Command, run from /tmp with TMPDIR=/tmp:", "", "```",
+             " ".join(os.path.relpath(c, ROOT) if c.startswith(ROOT) else c for c in cmd), "```", "",
+             "| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---|---|---|---|---|"]
+    for r in csv.DictReader(open(stats[0])):
+        n = r["Name"].replace("(anonymous namespace)::", "").replace("|", "/")
+        n = n.split("(")[0] if "<" not in n else n.split(">(")[0] + ">"
+        lines.append(f"| `{n[:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+    open(os.path.join(prof_dir, f"{name}_kernel_stats.md"), "w").write("\n".join(lines) + "\n")
+
+    # 2-5. HBM traffic counters, calibrated on a copy of known size
+    short = run + ["--steps", "3", "--warmup", "1"]
+    readings, cmds = {}, {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        c1, f1 = rocprof(["--pmc", counter], a.out, f"{counter.lower()}_bench", short, limit=120)
+        c2, f2 = rocprof(["--pmc", counter], a.out, f"{counter.lower()}_copy", [bench, "--copy-probe", str(COPY_MIB)],
+                         limit=120)
+        readings[counter] = (counter_means(f1, counter), counter_means(f2, counter))
+        cmds[counter] = (c1, c2)
+    factors = {}
+    for counter, (_, copy) in readings.items():
+        kib, _ = max(copy.values(), key=lambda v: v[0])        # the copy kernel: the largest reading
+        factors[counter] = (COPY_MIB << 20) / (kib * 1024.0)
+    runs = {}
+    for k in KERNELS.values():
+        f = readings["FETCH_SIZE"][0].get(k)
+        w = readings["WRITE_SIZE"][0].get(k)
+        if f is None or w is None:
+            continue
+        runs[k] = {"fetch_kib": round(f[0], 1), "write_kib": round(w[0], 1), "dispatches": f[1],
+                   "traffic_bytes": int(f[0] * 1024 * factors["FETCH_SIZE"] + w[0] * 1024 * factors["WRITE_SIZE"])}
+    sys.path.insert(0, ROOT)
+    from importlib import util
+    spec = util.spec_from_file_location("bench_mod", bench)
+    bm = util.module_from_spec(spec)
+    spec.loader.exec_module(bm)                                # for source_digest only (no GPU use)
+    tpath = os.path.join(prof_dir, "traffic.json")
+    try:
+        t = json.load(open(tpath if os.path.exists(tpath) else os.path.join(ROOT, "profiles", "traffic.json")))
+    except (OSError, ValueError):
+        t = {}
+    if t.get("sources") != bm.source_digest():
+        t = {"sources": bm.source_digest(), "runs": {}}
+    t["runs"][f"{a.config}/{a.mode}"] = runs
+    t["factors"] = factors
+    json.dump(t, open(tpath, "w"), indent=1, sort_keys=True)
+    md = [f"# HBM traffic per launch: {a.config}, mode {a.mode}", "",
+          f"FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each in its own rocprofv3 run, scaled by",
+          f"the same counter over a plain {COPY_MIB} MiB device copy (reads and writes {COPY_MIB} MiB).", "",
+          "| counter | copy reading (KiB) | factor (bytes per KiB read) |", "|---|---|---|"]
+    for counter, (_, copy) in readings.items():
+        kib, _ = max(copy.values(), key=lambda v: v[0])
+        md.append(f"| {counter} | {kib:.1f} | {factors[counter] * 1024:.1f} |")
+    md += ["", "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | dispatches | traffic (MB per launch) |",
+           "|---|---|---|---|---|"]
+    for k, r in runs.items():
+        md.append(f"| {k} | {r['fetch_kib']} | {r['write_kib']} | {r['dispatches']} | {r['traffic_bytes'] / 1e6:.1f} |")
+    md += ["", "Commands (from /tmp, TMPDIR=/tmp):", "", "```"]
+    for counter, (c1, c2) in cmds.items():
+        for c in (c1, c2):
+            md.append(" ".join(os.path.relpath(x, ROOT) if x.startswith(ROOT) else x for x in c))
+    md += ["```", "", f"Kernel sources digest: {t['sources']}"]
+    open(os.path.join(prof_dir, f"{name}_traffic.md"), "w").write("\n".join(md) + "\n")
+    print(json.dumps(runs), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -298,6 +298,18 @@ class DecodeBatch:
         check(lib.spkv_plan_query(C.byref(self.struct), arr, C.byref(info)))
         return info
 
+    def plan_parts(self, cascade: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+        """Per-request partial-state counts (paged pass, prefix part) of the plan."""
+        B = len(self.lens_h)
+        flat = np.zeros(max(B, 1), dtype=np.int32)
+        pre = np.zeros(max(B, 1), dtype=np.int32)
+        arr = None
+        if cascade is not None:
+            self._casc = np.ascontiguousarray(cascade, dtype=np.int32)
+            arr = _ptr(self._casc, C.c_int32)
+        check(lib.spkv_plan_parts(C.byref(self.struct), arr, _ptr(flat, C.c_int32), _ptr(pre, C.c_int32)))
+        return flat[:B], pre[:B]
+
 
 def default_params(mode: int = A.SPKV_MODE_PER_GROUP) -> A.spkv_dispatch_params:
     p = A.spkv_dispatch_params()

@@ -1,0 +1,66 @@
+"""Host planning of the paged pass (CPU only): the per-request partial-state
+counts reported by spkv_plan_parts equal those of the stream-K definition -
+a sub-batch's tokens, concatenated in request order, cut into `blocks` equal
+ranges [floor(k*T/n), floor((k+1)*T/n)), one partial per (range, request)
+overlap - recomputed here by brute force over token indices."""
+import numpy as np
+import pytest
+import torch
+
+from shared_prefix_paged_amd import runtime as R
+
+
+def batch_of(lens, groups, group_len, hkv=8, hq=32, d=128, page=1):
+    B = len(lens)
+    q = torch.zeros((B, hq, d), dtype=torch.bfloat16)
+    mb = max(1, max((l + page - 1) // page for l in lens)) if B else 1
+    tables = np.full((B, mb), -1, np.int32)
+    bases = list(np.cumsum([0] + list(group_len))[:-1])
+    return R.DecodeBatch(q, groups, bases, group_len, tables, lens, page, hkv)
+
+
+def brute_force_parts(L, nb):
+    """Partial count per request when sum(L) tokens are cut into nb equal ranges."""
+    T = int(np.sum(L))
+    owner = np.repeat(np.arange(len(L)), L)              # request of every token
+    parts = np.zeros(len(L), np.int64)
+    for k in range(nb):
+        lo, hi = (T * k) // nb, (T * (k + 1)) // nb
+        for r in np.unique(owner[lo:hi]):
+            parts[r] += 1
+    return parts
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_flat_parts_match_equal_range_definition(seed):
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(3, 40))
+    lens = [int(x) for x in rng.integers(0, 3000, size=B)]
+    lens[0] = max(lens[0], 1)
+    groups = [int(g) for g in rng.integers(-1, 3, size=B)]
+    group_len = [int(x) for x in rng.integers(0, 5000, size=3)]
+    bt = batch_of(lens, groups, group_len)
+    for cascade in ([1, 1, 1], [0, 0, 0], [1, 0, 1]):
+        info = bt.plan(cascade)
+        flat, pre = bt.plan_parts(cascade)
+        # tokens of the paged pass: COLD, plus the HOT prefix of members of non-cascade groups
+        L = np.array([lens[b] + (group_len[groups[b]] if groups[b] >= 0 and not cascade[groups[b]] else 0)
+                      for b in range(B)], np.int64)
+        head_groups = -(-8 // 4)
+        nb = int(info.flat_items) // head_groups
+        assert nb >= 1
+        np.testing.assert_array_equal(flat, brute_force_parts(L, nb))
+        assert flat.max() <= info.flat_splits <= info.flat_split_cap
+        for b in range(B):
+            g = groups[b]
+            if g >= 0 and cascade[g] and group_len[g] > 0:
+                assert 1 <= pre[b] <= info.prefix_splits
+            else:
+                assert pre[b] == 0
+
+
+def test_members_of_one_group_share_prefix_parts():
+    bt = batch_of([100, 5, 900, 1], [0, 0, 1, 0], [4096, 300])
+    flat, pre = bt.plan_parts(None)
+    assert pre[0] == pre[1] == pre[3] >= 1 and pre[2] >= 1
+    assert (flat >= 1).all()
