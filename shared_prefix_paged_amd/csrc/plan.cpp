@@ -168,7 +168,7 @@ spkv_status make_plan(const spkv_batch *b, const int32_t *cascade, int32_t num_c
     p->run_prefix = max_lp_c > 0;
     if (p->run_prefix && bf16) {
         int w = (int)std::min<int64_t>(4, (max_m + 31) / 32);
-        p->prefix_waves = std::max(1, w);
+        p->prefix_waves = w <= 1 ? 1 : (w == 2 ? 2 : 4);   // tile variants: 1, 2 or 4 waves of 32 rows
         const int64_t mt = 32 * p->prefix_waves;
         p->prefix_mtiles = (int32_t)((max_m + mt - 1) / mt);
         for (int g = 0; g < ng; ++g) {

@@ -64,3 +64,12 @@ def test_members_of_one_group_share_prefix_parts():
     flat, pre = bt.plan_parts(None)
     assert pre[0] == pre[1] == pre[3] >= 1 and pre[2] >= 1
     assert (flat >= 1).all()
+
+
+@pytest.mark.parametrize("members", [1, 2, 3, 5, 17, 40])
+def test_prefix_tile_is_a_built_variant(members):
+    # 4 query heads per KV head: members * 4 rows per group; tiles of 1, 2 or 4 waves exist
+    bt = batch_of([50] * members, [0] * members, [2048], hkv=8, hq=32)
+    info = bt.plan(None)
+    assert info.prefix_waves in (1, 2, 4)
+    assert info.prefix_waves * 32 * info.prefix_mtiles >= members * 4
