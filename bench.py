@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM traffic per launch (written by shared_prefix_paged_amd/profile_step.py)")
+    ap.add_argument("--sweep-lp", default=None, metavar="L1,L2,...",
+                    help="time cascade and dense attention at each prefix length (C3 crossover sweep) and exit")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-MiB device buffer 5 times (counter calibration) and exit")
     return ap.parse_args()
@@ -62,6 +64,60 @@ def copy_probe(mib: int) -> int:
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
+    return 0
+
+
+def sweep_lp(args) -> int:
+    """Attention time of both backends (forced) and the dispatcher's choice at
+    each prefix length; one JSON line.  Same workload recipe at every length
+    (the configuration's batch, heads and suffix lengths)."""
+    import numpy as np
+    import torch
+    import workloads as W
+    from shared_prefix_paged_amd import runtime as R
+    from shared_prefix_paged_amd import _abi as A
+    from hip_setup import setup_single_step
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    cfg0 = W.CONFIGS[args.config]
+    rows = []
+    for lp in [int(x) for x in args.sweep_lp.split(",")]:
+        wl = W.make_workload(cfg0, prefix_len=lp, extra_steps=4)
+        cfg = wl.cfg
+        st = setup_single_step(wl, device=dev)
+        B = wl.batch
+        out = torch.empty((B, cfg.num_q_heads, cfg.head_dim), dtype=torch.float32, device=dev)
+        lse = torch.empty((B, cfg.num_q_heads), dtype=torch.float32, device=dev)
+        ws = torch.empty(st.batch.workspace_size(), dtype=torch.uint8, device=dev)
+        rec = {"lp": lp, "kv_tokens": int(sum(wl.prefix_len_of(b) + int(wl.suffix_len[b]) for b in range(B)))}
+        for name, mode in (("cascade", A.SPKV_MODE_FORCE_CASCADE), ("dense", A.SPKV_MODE_FORCE_DENSE),
+                           ("dispatch", A.SPKV_MODE_PER_GROUP)):
+            params = R.default_params(mode)
+            for _ in range(3):
+                _, _, choice = R.decode_step(st.batch, st.pools, params, ws, out, lse)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            n = max(1, args.steps)
+            e0.record()
+            for _ in range(n):
+                R.decode_step(st.batch, st.pools, params, ws, out, lse)
+            e1.record()
+            torch.cuda.synchronize()
+            rec[f"{name}_us"] = round(1e3 * e0.elapsed_time(e1) / n, 2)
+            if name == "dispatch":
+                rec["dispatch_choice"] = "cascade" if len(choice) and choice[0] else "dense"
+        rec["best"] = "cascade" if rec["cascade_us"] < rec["dense_us"] else "dense"
+        print(f"[sweep] {json.dumps(rec)}", file=sys.stderr, flush=True)
+        rows.append(rec)
+        del st, ws, out, lse
+        torch.cuda.empty_cache()
+    cross = [r["lp"] for r in rows if r["best"] == "cascade"]
+    print(json.dumps({"metric": "attention time per step, cascade vs dense, by prefix length",
+                      "unit": "us", "config": {"workload": f"{args.config} recipe, Lp swept", "batch": B,
+                                               "steps_per_point": max(1, args.steps)},
+                      "rows": rows, "cascade_wins_from_lp": min(cross) if cross else None,
+                      "dispatch_agrees": all(r["dispatch_choice"] == r["best"] for r in rows)}), flush=True)
     return 0
 
 
@@ -98,6 +154,8 @@ def main():
     args = parse()
     if args.copy_probe:
         return copy_probe(args.copy_probe)
+    if args.sweep_lp:
+        return sweep_lp(args)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
               "this build has no multi-GPU path.", file=sys.stderr)
