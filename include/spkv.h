@@ -188,6 +188,24 @@ spkv_status spkv_copy_blocks(const int32_t *pairs, int32_t n, void *k_cold, void
                              int32_t num_pages, int32_t page_size,
                              int32_t num_kv_heads, int32_t head_dim, int32_t dtype, void *stream);
 
+/* One decode step's appends in one launch ([PKV] How it works, steps 1-3):
+ * token i's K and V rows ([n, Hkv, d] each, device) are written at COLD slot
+ * host_slots[i], and, when tables is not NULL, request r = host_rows[i] (or i
+ * when host_rows is NULL) gets
+ *     tables[r * max_blocks + lens[r] / P] = host_slots[i] / P;  lens[r] += 1
+ * on the device (a fresh page, a copy-on-write replacement or an append into
+ * the current page alike).  host_slots and host_rows are host arrays (the
+ * allocator's output); their values are copied into the launch at call time,
+ * so no upload is needed.  Rows must be distinct within one call; slots
+ * outside [0, cold_slots), rows outside [0, num_rows) and entries beyond
+ * max_blocks are skipped.  Run spkv_copy_blocks for the step's
+ * copy-on-write pairs first: the copy must not overwrite the new token. */
+spkv_status spkv_append_tokens(const void *k_new, const void *v_new, const int32_t *host_slots,
+                               const int32_t *host_rows, int32_t n, void *k_cold, void *v_cold, int64_t cold_slots,
+                               int32_t *tables, int32_t max_blocks, int32_t *lens, int32_t num_rows,
+                               int32_t page_size, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                               void *stream);
+
 /* Device-side mirror of one append per request ([PKV] How it works, steps 2
  * and 3: the new token's page enters the block table the attention kernel
  * reads).  For i in 0..n-1 with r = rows[i]:

@@ -80,6 +80,8 @@ SIGNATURES = {
     "spkv_reshape_and_cache": (c_i32, [c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i64, c_i32, c_i32, c_i32, c_vp]),
     "spkv_copy_blocks": (c_i32, [c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp]),
     "spkv_block_table_append": (c_i32, [c_vp, c_i32, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_vp]),
+    "spkv_append_tokens": (c_i32, [c_vp, c_vp, P_i32, P_i32, c_i32, c_vp, c_vp, c_i64, c_vp, c_i32, c_vp, c_i32,
+                                   c_i32, c_i32, c_i32, c_i32, c_vp]),
     "spkv_workspace_size": (c_sz, [P_batch]),
     "spkv_cascade_decode": (c_i32, [P_batch, P_kv, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "spkv_dense_decode": (c_i32, [P_batch, P_kv, c_vp, c_vp, c_vp, c_sz, c_vp]),

@@ -934,6 +934,40 @@ __global__ __launch_bounds__(256) void block_table_append_kernel(int32_t *tables
     lens[r] = len + 1;
 }
 
+// One decode step's appends in one launch: token i's K and V rows go to COLD
+// slot slots[i], and request rows[i]'s device block table and length follow
+// the append.  Slots and rows arrive from the host allocator through the
+// kernel arguments (no upload); block x handles token x.
+constexpr int kAppendArgTokens = 256;
+struct AppendArgs {
+    int32_t n;
+    int32_t slots[kAppendArgTokens];
+    int32_t rows[kAppendArgTokens];
+};
+
+__global__ __launch_bounds__(256) void append_tokens_kernel(const u32x4_t *knew, const u32x4_t *vnew, AppendArgs aa,
+                                                            u32x4_t *kcold, u32x4_t *vcold, int64_t cold_slots,
+                                                            int pieces_per_slot, int32_t *tables, int max_blocks,
+                                                            int32_t *lens, int num_rows, int page_size) {
+    const int tok = blockIdx.x;
+    if (tok >= aa.n) return;
+    const int64_t slot = aa.slots[tok];
+    if (slot < 0 || slot >= cold_slots) return;
+    for (int p = threadIdx.x; p < pieces_per_slot; p += blockDim.x) {
+        kcold[slot * pieces_per_slot + p] = knew[(int64_t)tok * pieces_per_slot + p];
+        vcold[slot * pieces_per_slot + p] = vnew[(int64_t)tok * pieces_per_slot + p];
+    }
+    if (threadIdx.x == 0 && tables) {
+        const int r = aa.rows[tok];
+        if (r < 0 || r >= num_rows) return;
+        const int len = lens[r];
+        const int blk = len / page_size;
+        if (len < 0 || blk >= max_blocks) return;
+        tables[(int64_t)r * max_blocks + blk] = (int32_t)(slot / page_size);
+        lens[r] = len + 1;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Launch plumbing and optional per-launch timing.
 // ---------------------------------------------------------------------------
@@ -1170,6 +1204,38 @@ spkv_status spkv_reshape_and_cache(const void *k_new, const void *v_new, const i
         (const u32x4_t *)k_new, (const u32x4_t *)v_new, slot_mapping, n, (u32x4_t *)k_cold, (u32x4_t *)v_cold,
         cold_slots, pps);
     return check_launch("reshape_and_cache_kernel");
+}
+
+spkv_status spkv_append_tokens(const void *k_new, const void *v_new, const int32_t *host_slots,
+                               const int32_t *host_rows, int32_t n, void *k_cold, void *v_cold, int64_t cold_slots,
+                               int32_t *tables, int32_t max_blocks, int32_t *lens, int32_t num_rows,
+                               int32_t page_size, int32_t hkv, int32_t d, int32_t dtype, void *stream) {
+    spkv_status st = check_kv_shape(hkv, d, dtype);
+    if (st != SPKV_OK) return st;
+    if (n < 0 || cold_slots < 0 || page_size < 1 || max_blocks < 0 || num_rows < 0)
+        return fail(SPKV_E_INVAL, "append_tokens: bad size");
+    if (n == 0) return SPKV_OK;
+    if (!k_new || !v_new || !host_slots || !k_cold || !v_cold)
+        return fail(SPKV_E_INVAL, "append_tokens: null pointer");
+    if (tables && !lens) return fail(SPKV_E_INVAL, "append_tokens: tables without lens");
+    const int esz = dtype == SPKV_DTYPE_BF16 ? 2 : 4;
+    const int pps = hkv * d * esz / 16;
+    for (int32_t i0 = 0; i0 < n; i0 += kAppendArgTokens) {
+        AppendArgs aa;
+        aa.n = std::min(kAppendArgTokens, n - i0);
+        for (int i = 0; i < aa.n; ++i) {
+            aa.slots[i] = host_slots[i0 + i];
+            aa.rows[i] = host_rows ? host_rows[i0 + i] : i0 + i;
+        }
+        TimedLaunch tl(SPKV_KERNEL_CACHE, (hipStream_t)stream);
+        const int64_t off = (int64_t)i0 * pps;
+        append_tokens_kernel<<<(unsigned)aa.n, 128, 0, (hipStream_t)stream>>>(
+            (const u32x4_t *)k_new + off, (const u32x4_t *)v_new + off, aa, (u32x4_t *)k_cold, (u32x4_t *)v_cold,
+            cold_slots, pps, tables, max_blocks, lens, num_rows, page_size);
+        st = check_launch("append_tokens_kernel");
+        if (st != SPKV_OK) return st;
+    }
+    return SPKV_OK;
 }
 
 spkv_status spkv_copy_blocks(const int32_t *pairs, int32_t n, void *k_cold, void *v_cold, int32_t num_pages,

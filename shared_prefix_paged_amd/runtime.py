@@ -224,6 +224,23 @@ def block_table_append(tables, max_blocks: int, lens, rows, slots, page_size: in
                                       _dp(slots), int(rows.numel()), int(page_size), stream_handle(stream)))
 
 
+def append_tokens(k_new, v_new, slots: np.ndarray, k_cold, v_cold, cold_slots: int, page_size: int,
+                  num_kv_heads: int, head_dim: int, tables=None, max_blocks: int = 0, lens=None,
+                  rows: Optional[np.ndarray] = None, stream=None):
+    """One step's appends in one launch (spkv_append_tokens): K/V rows to their
+    COLD slots and, with device tables/lens, the block-table update.  slots
+    and rows are host int32 arrays (the allocator's output)."""
+    slots = np.ascontiguousarray(slots, dtype=np.int32)
+    rows_a = None if rows is None else np.ascontiguousarray(rows, dtype=np.int32)
+    n = int(slots.size)
+    check(lib.spkv_append_tokens(_dp(k_new), _dp(v_new), _ptr(slots, C.c_int32),
+                                 None if rows_a is None else _ptr(rows_a, C.c_int32), n, _dp(k_cold), _dp(v_cold),
+                                 int(cold_slots), _dp(tables) if tables is not None else None, int(max_blocks),
+                                 _dp(lens) if lens is not None else None,
+                                 int(lens.numel()) if lens is not None else 0, int(page_size), int(num_kv_heads),
+                                 int(head_dim), dtype_code(k_cold), stream_handle(stream)))
+
+
 class KVPools:
     """Caller-owned device pools; ``struct`` is the spkv_kv describing them."""
 
