@@ -146,6 +146,13 @@ __device__ __forceinline__ float fdot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+// max(v[l], v[l ^ 32]) in every lane l (v_permlane32_swap exchanges the
+// upper half of one register with the lower half of another).
+__device__ __forceinline__ float max_of_halves(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // ---------------------------------------------------------------------------
 // Global->LDS DMA (global_load_lds_*): lane l's bytes land at M0 + size * l.
 // The compiler does not track these loads, so every wait on them is an
@@ -586,46 +593,55 @@ __global__ __launch_bounds__(64 * W) void prefix_mfma_kernel(Args a) {
     // builtin is 32-bit and must not be applied to these 64-bit pointers.)
     const uint32_t smem0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_offset(smem));
 
-    // Per-lane source rows and LDS placement of the DMAs.  K row r holds key
-    // swap_bits23(r); chunk c of a row sits at vchunk/kchunk-swizzled positions.
-    int koff[IPW], voff[IPW];
-    uint32_t wdst[IPW];
+    // Per-lane source offsets and LDS placement of the DMAs, fixed for the
+    // whole range (K row r of a tile holds key swap_bits23(r); the 16-byte
+    // chunks of a row sit at their swizzled positions).  Per tile only the
+    // wave-uniform source base moves.
+    uint32_t ksrc[IPW], vsrc[IPW], wdst[IPW];
+    int krow[IPW], vrow[IPW];
     {
         const int p = lane % CPR;
 #pragma unroll
         for (int i = 0; i < IPW; ++i) {
             const int r0 = (wave * IPW + i) * RPI;
             const int r = r0 + lane / CPR;
-            koff[i] = swap_bits23(r);
-            voff[i] = r;
-            // physical chunk p of row r holds logical chunk kc / vc
-            const int kc = p ^ (r % CPR);
-            const int vc = vchunk_logical<CPR>(r, p);
-            koff[i] = (koff[i] << 16) | (kc << 4);
-            voff[i] = (voff[i] << 16) | (vc << 4);
+            krow[i] = swap_bits23(r);
+            vrow[i] = r;
+            ksrc[i] = (uint32_t)(krow[i] * ROWB + ((p ^ (r % CPR)) << 4));
+            vsrc[i] = (uint32_t)(r * ROWB + (vchunk_logical<CPR>(r, p) << 4));
             wdst[i] = (uint32_t)__builtin_amdgcn_readfirstlane((int)(r0 * ROWB));
         }
     }
-    auto issue = [&](int t) {
+    // Tile t of the range into LDS stage st.  In the last tile of a range that
+    // ends inside it, rows past the end re-read the last valid key (in bounds;
+    // those keys are masked before the softmax).
+    auto issue = [&](int t, int st) {
         const int kt = k0 + t * NT;
-        const uint32_t kst = smem0 + (uint32_t)((t % STAGES) * 2 * TILEB);
-        const uint32_t vst = kst + TILEB;
-        const bool tail = kt + NT > k1;
+        const char *kg = kh + (int64_t)kt * ROWB;
+        const char *vg = vh + (int64_t)kt * ROWB;
+        const uint32_t kst = smem0 + (uint32_t)(st * 2 * TILEB), vst = kst + TILEB;
+        if (kt + NT <= k1) {
 #pragma unroll
-        for (int i = 0; i < IPW; ++i) {
-            int kr = kt + (koff[i] >> 16), vr = kt + (voff[i] >> 16);
-            if (tail) {   // rows past the key range read the last valid key (in bounds; masked later)
-                kr = min(kr, k1 - 1);
-                vr = min(vr, k1 - 1);
+            for (int i = 0; i < IPW; ++i) {
+                dma16(kg, ksrc[i], kst + wdst[i]);
+                dma16(vg, vsrc[i], vst + wdst[i]);
             }
-            dma16(kh, (uint32_t)(kr * ROWB + (koff[i] & 0xffff)), kst + wdst[i]);
-            dma16(vh, (uint32_t)(vr * ROWB + (voff[i] & 0xffff)), vst + wdst[i]);
+        } else {
+            const int last = k1 - 1 - kt;
+#pragma unroll
+            for (int i = 0; i < IPW; ++i) {
+                const int kr = min(krow[i], last), vr = min(vrow[i], last);
+                dma16(kg, ksrc[i] + (uint32_t)((kr - krow[i]) * ROWB), kst + wdst[i]);
+                dma16(vg, vsrc[i] + (uint32_t)((vr - vrow[i]) * ROWB), vst + wdst[i]);
+            }
         }
     };
 
-#pragma unroll
-    for (int t = 0; t < STAGES - 1; ++t)
-        if (t < ntiles) issue(t);
+    // Prologue.  The compiler waits for its own loads with vmcnt(0), which
+    // also covers every DMA in flight, so the member index and Q (loads it
+    // tracks) are read while only tile 0 is in flight, and tiles 1 .. STAGES-2
+    // follow once Q has landed.
+    issue(0, 0);
 
     // This lane's query row (column of S^T / O^T).
     const int row = mt * 32 * W + wave * 32 + col;
@@ -644,11 +660,14 @@ __global__ __launch_bounds__(64 * W) void prefix_mfma_kernel(Args a) {
             u32x4_t v = row_ok ? *(const u32x4_t *)(qp + k * 16) : u32x4_t{0, 0, 0, 0};
             qf[k] = __builtin_bit_cast(bf16x8_t, v);
         }
-        // Consume Q here so the compiler waits for its loads once, before the
-        // loop, and not inside it (where the tile DMAs are still in flight).
+        // Consume Q here so the compiler waits for its loads now, before the
+        // next DMAs are issued, and not inside the loop.
 #pragma unroll
         for (int k = 0; k < KS; ++k) asm volatile("" ::"v"(__builtin_bit_cast(u32x4_t, qf[k])));
     }
+#pragma unroll
+    for (int t = 1; t < STAGES - 1; ++t)
+        if (t < ntiles) issue(t, t);
 
     f32x16_t oacc[NDB];
 #pragma unroll
@@ -663,96 +682,113 @@ __global__ __launch_bounds__(64 * W) void prefix_mfma_kernel(Args a) {
     float m_run = -INFINITY, l_run = 0.f;
     const float c2 = a.scale_log2;
 
-    const int krow_off = col * ROWB;
-    const int g16 = lane >> 4, j16 = lane & 15;
-
-    for (int t = 0; t < ntiles; ++t) {
-        if (t + STAGES - 2 < ntiles) wait_vmcnt<AHEAD>();
-        else wait_vmcnt<0>();
-        __builtin_amdgcn_s_barrier();          // tile t visible; every wave is done with tile t-1
-        asm volatile("" ::: "memory");
-        if (t + STAGES - 1 < ntiles) issue(t + STAGES - 1);
-
-        const char *ks = smem + (t % STAGES) * 2 * TILEB;
-        const char *vs = ks + TILEB;
-        const int kt = k0 + t * NT;
-
-        // S^T = K . Q^T
-        f32x16_t sacc;
+    // Loop-invariant LDS read offsets.  K: lane (col, half) reads 16 bytes of
+    // key row col per k-step.  V (transposing reads): rows r1 and r1 + 4 of
+    // the first 16-key step and r1 + 16, r1 + 20 of the second share one chunk
+    // placement (it depends on the row modulo 4), so one offset per 32-column
+    // block serves all four; the rest are immediates.
+    uint32_t kofs[KS], vofs[NDB];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) sacc[j] = 0.f;
+    for (int k = 0; k < KS; ++k) kofs[k] = (uint32_t)(col * ROWB + (((2 * k + half) ^ (col % CPR)) << 4));
+    {
+        const int g16 = lane >> 4, j16 = lane & 15;
+        const int r1 = 8 * (g16 >> 1) + (j16 >> 2);
 #pragma unroll
-        for (int k = 0; k < KS; ++k) {
-            const int c = 2 * k + half;
-            const bf16x8_t af = *(const bf16x8_t *)(ks + krow_off + ((c ^ (col % CPR)) << 4));
-            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[k], sacc, 0, 0, 0);
+        for (int db = 0; db < NDB; ++db) {
+            const int dpiece = 32 * db + 16 * (g16 & 1) + 4 * (j16 & 3);
+            const int c = dpiece >> 3, inner = (dpiece & 7) * 2;
+            vofs[db] = (uint32_t)(r1 * ROWB + (vchunk_phys<CPR>(r1, c) << 4) + inner);
         }
-        if (kt + NT > k1) {   // last tile of the range: mask keys past its end
+    }
+    const lds_char_t *lsm = (const lds_char_t *)smem;
+    constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;   // (1.0, 1.0) in bf16
+
+    // Tile t sits in stage t % STAGES; the stage loop is unrolled so that all
+    // LDS addresses are a per-lane offset plus an immediate.
+    for (int t0 = 0; t0 < ntiles; t0 += STAGES) {
 #pragma unroll
-            for (int j = 0; j < 16; ++j)
-                if (kt + 16 * (j >> 3) + 8 * half + (j & 7) >= k1) sacc[j] = -INFINITY;
-        }
-        // Online softmax along keys (one query row per lane, two lane halves).
-        float mx = fmaxf(fmaxf(sacc[0], sacc[1]), sacc[2]);
+        for (int st = 0; st < STAGES; ++st) {
+            const int t = t0 + st;
+            if (t >= ntiles) break;
+            if (t + STAGES - 2 < ntiles) wait_vmcnt<AHEAD>();
+            else wait_vmcnt<0>();
+            __builtin_amdgcn_s_barrier();      // tile t visible; every wave is done with tile t-1
+            asm volatile("" ::: "memory");
+            if (t + STAGES - 1 < ntiles) issue(t + STAGES - 1, (st + STAGES - 1) % STAGES);
+
+            const lds_char_t *ks = lsm + st * 2 * TILEB;
+            const lds_char_t *vs = ks + TILEB;
+            const int kt = k0 + t * NT;
+
+            // S^T = K . Q^T
+            f32x16_t sacc;
 #pragma unroll
-        for (int j = 3; j < 16; j += 2) mx = fmaxf(fmaxf(mx, sacc[j]), sacc[j + 1 < 16 ? j + 1 : j]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c2;
-        const bool grow = mx > m_run + kRescaleSlack;
-        if (__any(grow)) {
-            const float mnew = grow ? mx : m_run;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
-            m_run = mnew;
-            l_run *= alpha;
+            for (int j = 0; j < 16; ++j) sacc[j] = 0.f;
 #pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
-        }
-        const float nm = -m_run;
-        float psum = 0.f;
-        uint32_t pk[8], pl[8];
-#pragma unroll
-        for (int j = 0; j < 16; j += 2) {
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[j], c2, nm));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[j + 1], c2, nm));
-            bf16x2_t pp = {(__bf16)p0, (__bf16)p1};   // round to nearest even
-            const uint32_t w = __builtin_bit_cast(uint32_t, pp);
-            pk[j >> 1] = w;
-            const float h0 = bf16lo(w), h1 = bf16hi(w);
-            if constexpr (SPLIT_P) {
-                bf16x2_t ll = {(__bf16)(p0 - h0), (__bf16)(p1 - h1)};
-                pl[j >> 1] = __builtin_bit_cast(uint32_t, ll);
-                psum += p0 + p1;
-            } else {
-                // Normalise by the weights the MFMA actually uses, so the
-                // output stays a convex combination of V rows.
-                psum += h0 + h1;
+            for (int k = 0; k < KS; ++k) {
+                const bf16x8_t af = *(const bf16x8_t __attribute__((address_space(3))) *)(ks + kofs[k]);
+                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[k], sacc, 0, 0, 0);
             }
-        }
-        l_run += psum;
+            if (kt + NT > k1) {   // last tile of the range: mask keys past its end
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+                    if (kt + 16 * (j >> 3) + 8 * half + (j & 7) >= k1) sacc[j] = -INFINITY;
+            }
+            // Online softmax along keys (one query row per lane, two lane halves).
+            float mx = fmaxf(fmaxf(sacc[0], sacc[1]), sacc[2]);
+#pragma unroll
+            for (int j = 3; j < 16; j += 2) mx = fmaxf(fmaxf(mx, sacc[j]), sacc[j + 1 < 16 ? j + 1 : j]);
+            mx = max_of_halves(mx) * c2;
+            const bool grow = mx > m_run + kRescaleSlack;
+            if (__any(grow)) {
+                const float mnew = grow ? mx : m_run;
+                const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
+                m_run = mnew;
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
+            }
+            const float nm = -m_run;
+            uint32_t pk[8], pl[8];
+#pragma unroll
+            for (int j = 0; j < 16; j += 2) {
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[j], c2, nm));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[j + 1], c2, nm));
+                bf16x2_t pp = {(__bf16)p0, (__bf16)p1};   // round to nearest even
+                const uint32_t w = __builtin_bit_cast(uint32_t, pp);
+                pk[j >> 1] = w;
+                if constexpr (SPLIT_P) {
+                    bf16x2_t ll = {(__bf16)(p0 - bf16lo(w)), (__bf16)(p1 - bf16hi(w))};
+                    pl[j >> 1] = __builtin_bit_cast(uint32_t, ll);
+                    l_run += p0 + p1;
+                } else {
+                    // Normalise by the weights the MFMA actually uses, so the
+                    // output stays a convex combination of V rows.
+                    l_run = fdot2(w, kOnesBf16x2, l_run);
+                }
+            }
 
-        // O^T += V^T . P^T, two 16-key steps; V^T operands by transposing reads.
+            // O^T += V^T . P^T, two 16-key steps; V^T operands by transposing reads.
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            const u32x4_t pb = {pk[4 * kb + 0], pk[4 * kb + 1], pk[4 * kb + 2], pk[4 * kb + 3]};
-            const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pb);
-            const u32x4_t plb = {pl[4 * kb + 0], pl[4 * kb + 1], pl[4 * kb + 2], pl[4 * kb + 3]};
-            const bf16x8_t pfl = __builtin_bit_cast(bf16x8_t, plb);
-            const int r1 = 16 * kb + 8 * (g16 >> 1) + (j16 >> 2);   // key row of the first read
-            const int r2 = r1 + 4;
+            for (int kb = 0; kb < 2; ++kb) {
+                const u32x4_t pb = {pk[4 * kb + 0], pk[4 * kb + 1], pk[4 * kb + 2], pk[4 * kb + 3]};
+                const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pb);
+                const u32x4_t plb = {pl[4 * kb + 0], pl[4 * kb + 1], pl[4 * kb + 2], pl[4 * kb + 3]};
+                const bf16x8_t pfl = __builtin_bit_cast(bf16x8_t, plb);
+                const lds_char_t *vk = vs + kb * 16 * ROWB;
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                const int dpiece = 32 * db + 16 * (g16 & 1) + 4 * (j16 & 3);
-                const int c = dpiece >> 3, inner = (dpiece & 7) * 2;
-                const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (v4i16_t __attribute__((address_space(3))) *)(lds_char_t *)(vs + r1 * ROWB + (vchunk_phys<CPR>(r1, c) << 4) + inner));
-                const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (v4i16_t __attribute__((address_space(3))) *)(lds_char_t *)(vs + r2 * ROWB + (vchunk_phys<CPR>(r2, c) << 4) + inner));
-                const u32x4_t w = {__builtin_bit_cast(u32x2_t, lo).x, __builtin_bit_cast(u32x2_t, lo).y,
-                                   __builtin_bit_cast(u32x2_t, hi).x, __builtin_bit_cast(u32x2_t, hi).y};
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w), pf, oacc[db], 0, 0, 0);
-                if constexpr (SPLIT_P)
-                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w), pfl, oacc[db], 0, 0, 0);
+                for (int db = 0; db < NDB; ++db) {
+                    typedef v4i16_t __attribute__((address_space(3))) *lds_v4i16_ptr;
+                    const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(vk + vofs[db]));
+                    const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(vk + 4 * ROWB + vofs[db]));
+                    const u32x4_t w = {__builtin_bit_cast(u32x2_t, lo).x, __builtin_bit_cast(u32x2_t, lo).y,
+                                       __builtin_bit_cast(u32x2_t, hi).x, __builtin_bit_cast(u32x2_t, hi).y};
+                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w), pf, oacc[db], 0, 0, 0);
+                    if constexpr (SPLIT_P)
+                        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w), pfl, oacc[db], 0, 0, 0);
+                }
             }
         }
     }
@@ -1140,17 +1176,21 @@ spkv_status run_decode(const spkv_batch *b, const spkv_kv *kv, const int32_t *ca
     Args a = make_args(b, kv, p, ws);
     hipStream_t hs = (hipStream_t)stream;
     const bool bf16 = b->dtype == SPKV_DTYPE_BF16;
-    if (p.run_prefix && bf16) {
-        st = launch_prefix(a, p, b->head_dim, hs);
-        if (st != SPKV_OK) return st;
-    }
-    // Sub-batch i is entry i of both paged passes.
+    // The paged (HBM-bound) pass runs first, the prefix contraction (MFMA-
+    // bound) second: the prefix pass's partial states are then still in the
+    // last-level cache when the merge reads them, and their write-back does
+    // not compete with the paged pass's reads.  Sub-batch i is entry i of
+    // both paged passes.
     for (size_t i = 0; i < p.flat.size(); ++i) {
         if (p.run_prefix && !bf16) {
             st = launch_flat(a, false, b->head_dim, kPartPrefix, p.pflat[i], p.flat_head_groups, hs);
             if (st != SPKV_OK) return st;
         }
         st = launch_flat(a, bf16, b->head_dim, kPartRest, p.flat[i], p.flat_head_groups, hs);
+        if (st != SPKV_OK) return st;
+    }
+    if (p.run_prefix && bf16) {
+        st = launch_prefix(a, p, b->head_dim, hs);
         if (st != SPKV_OK) return st;
     }
     static const FlatLaunch kNone{};

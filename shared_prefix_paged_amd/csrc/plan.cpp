@@ -177,10 +177,27 @@ spkv_status make_plan(const spkv_batch *b, const int32_t *cascade, int32_t num_c
             if (n == 0 || lp == 0 || !mask_get(p->cascade, g)) continue;
             prefix_work += Hkv * ((n * G + mt - 1) / mt) * lp;
         }
+        // Two blocks per CU are resident (the LDS ring of a block is 64 KB):
+        // size the key chunk so that all blocks fit in one round.  Rounding
+        // each group's last chunk up can add a block per row tile, so grow
+        // the chunk until the exact block count fits (or every group is one
+        // chunk).
         const int64_t target = std::max<int64_t>(1, (int64_t)num_cus * 2);
         int64_t pt = (prefix_work + target - 1) / target;
         pt = std::max<int64_t>(pt, 256);
         pt = (pt + kPrefixKeyTile - 1) / kPrefixKeyTile * kPrefixKeyTile;
+        auto blocks_for = [&](int64_t chunk) {
+            int64_t nb = 0;
+            for (int g = 0; g < ng; ++g) {
+                const int64_t n = b->host_group_indptr[g + 1] - b->host_group_indptr[g];
+                const int64_t lp = b->host_hot_len[g];
+                if (n == 0 || lp == 0 || !mask_get(p->cascade, g)) continue;
+                nb += Hkv * ((n * G + mt - 1) / mt) *
+                      splits_for(lp, chunk_for(lp, (int32_t)chunk, kPrefixSplitCap, kPrefixKeyTile));
+            }
+            return nb;
+        };
+        while (pt < max_lp_c && pt < (1 << 20) && blocks_for(pt) > target) pt += kPrefixKeyTile;
         p->prefix_chunk = (int32_t)std::min<int64_t>(pt, 1 << 20);
         p->prefix_splits = std::min<int32_t>(kPrefixSplitCap, splits_for(max_lp_c, p->prefix_chunk));
     } else if (p->run_prefix) {

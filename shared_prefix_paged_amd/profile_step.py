@@ -9,13 +9,17 @@ Runs, each as its own rocprofv3 process (program directly after ``--``, from
   2. ``--pmc FETCH_SIZE`` and 3. ``--pmc WRITE_SIZE`` over a short bench run;
   4./5. the same two counters over ``bench.py --copy-probe 256``, a plain
      device copy that reads and writes 256 MiB, to turn counter readings into
-     bytes (factor = known bytes / counter reading).
+     bytes (factor = known bytes / counter reading);
+  6./7. two passes of shader-sequencer counters over a short bench run: MFMA
+     busy cycles and bf16 MFMA operations (the prefix contraction), VALU, LDS
+     and bank-conflict cycles (every kernel).
 
 Writes ``profiles/<config>_<mode>_kernel_stats.md`` (per-kernel durations),
 ``profiles/<config>_<mode>_traffic.md`` (counter readings, factors, bytes per
-launch) and updates ``profiles/traffic.json``, which bench.py reads for its
-roofline ``traffic`` field while the kernel sources are unchanged.  Raw
-rocprofv3 output stays in --out.  This script itself never touches the GPU.
+launch), ``profiles/<config>_<mode>_counters.md`` (MFMA and LDS counters)
+and updates ``profiles/traffic.json``, which bench.py reads for its roofline
+``traffic`` field while the kernel sources are unchanged.  Raw rocprofv3 output
+stays in --out.  This script itself never touches the GPU.
 """
 from __future__ import annotations
 
@@ -30,6 +34,14 @@ import sys
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KERNELS = {"flat_kernel": "flat_paged", "prefix_mfma_kernel": "prefix_mfma", "merge_kernel": "merge"}
 COPY_MIB = 256
+NUM_CUS, SIMDS_PER_CU, NUM_XCC = 256, 4, 8
+# Counter passes: at most 8 SQ and 2 GRBM counters each (one hardware pass).
+SQ_PASSES = (
+    ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_MFMA", "SQ_BUSY_CU_CYCLES",
+     "SQ_WAVE_CYCLES", "SQ_WAVES", "GRBM_GUI_ACTIVE"),
+    ("SQ_INSTS_VALU", "SQ_ACTIVE_INST_VALU", "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_INSTS_LDS", "SQ_LDS_IDX_ACTIVE",
+     "SQ_LDS_BANK_CONFLICT", "SQ_WAIT_INST_LDS", "SQ_WAIT_INST_ANY"),
+)
 
 
 def kernel_key(name: str):
@@ -92,7 +104,11 @@ def main():
              "per-kernel-timing steps). Command, run from /tmp with TMPDIR=/tmp:", "", "```",
              " ".join(os.path.relpath(c, ROOT) if c.startswith(ROOT) else c for c in cmd), "```", "",
              "| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---|---|---|---|---|"]
+    avg_ns = {}
     for r in csv.DictReader(open(stats[0])):
+        k = kernel_key(r["Name"])
+        if k:
+            avg_ns[k] = float(r["AverageNs"])
         n = r["Name"].replace("(anonymous namespace)::", "").replace("|", "/")
         n = n.split("(")[0] if "<" not in n else n.split(">(")[0] + ">"
         lines.append(f"| `{n[:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
@@ -152,6 +168,43 @@ def main():
             md.append(" ".join(os.path.relpath(x, ROOT) if x.startswith(ROOT) else x for x in c))
     md += ["```", "", f"Kernel sources digest: {t['sources']}"]
     open(os.path.join(prof_dir, f"{name}_traffic.md"), "w").write("\n".join(md) + "\n")
+
+    # 6-7. shader-sequencer counters (MFMA, VALU, LDS) per kernel
+    sq, sq_cmds = {}, []
+    for i, counters in enumerate(SQ_PASSES):
+        c, f = rocprof(["--pmc"] + list(counters), a.out, f"sq{i + 1}_bench", short, limit=120)
+        sq_cmds.append(c)
+        for counter in counters:
+            for k, (v, _) in counter_means(f, counter).items():
+                sq.setdefault(k, {})[counter] = v
+    cm = [f"# Shader counters per launch: {a.config}, mode {a.mode}", "",
+          "Means per dispatch over a short bench run, summed over the chip's shader engines and XCDs.",
+          f"Derived: kernel cycles = GRBM_GUI_ACTIVE / {NUM_XCC} (one reading per XCD); MFMA busy =",
+          f"SQ_VALU_MFMA_BUSY_CYCLES / (kernel cycles x {NUM_CUS} CUs x {SIMDS_PER_CU} SIMDs); bf16 MFMA rate =",
+          "SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 flops / average duration (kernel trace) against 2.5 PFLOP/s;",
+          "LDS bank-conflict share = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE.", "",
+          "| kernel | avg us | MFMA busy | bf16 MFMA TFLOP/s | % of peak | VALU insts | LDS insts | "
+          "bank-conflict share |", "|---|---|---|---|---|---|---|---|"]
+    for k in KERNELS.values():
+        v = sq.get(k)
+        if not v:
+            continue
+        cyc = v.get("GRBM_GUI_ACTIVE", 0.0) / NUM_XCC
+        busy = v.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (cyc * NUM_CUS * SIMDS_PER_CU) if cyc > 0 else 0.0
+        t = avg_ns.get(k, 0.0) * 1e-9
+        tf = v.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512 / t / 1e12 if t > 0 else 0.0
+        lds = v.get("SQ_LDS_IDX_ACTIVE", 0.0)
+        bc = v.get("SQ_LDS_BANK_CONFLICT", 0.0) / lds if lds > 0 else 0.0
+        cm.append(f"| {k} | {t * 1e6:.2f} | {100 * busy:.1f} % | {tf:.1f} | {100 * tf / 2500:.1f} % | "
+                  f"{v.get('SQ_INSTS_VALU', 0):.0f} | {v.get('SQ_INSTS_LDS', 0):.0f} | {100 * bc:.1f} % |")
+    cm += ["", "Raw means per dispatch:", "", "| kernel | counter | value |", "|---|---|---|"]
+    for k in KERNELS.values():
+        for counter, val in sorted(sq.get(k, {}).items()):
+            cm.append(f"| {k} | {counter} | {val:.1f} |")
+    cm += ["", "Commands (from /tmp, TMPDIR=/tmp):", "", "```"]
+    cm += [" ".join(os.path.relpath(x, ROOT) if x.startswith(ROOT) else x for x in c) for c in sq_cmds]
+    cm += ["```", "", f"Kernel sources digest: {bm.source_digest()}"]
+    open(os.path.join(prof_dir, f"{name}_counters.md"), "w").write("\n".join(cm) + "\n")
     print(json.dumps(runs), flush=True)
     return 0
 

@@ -73,3 +73,25 @@ def test_prefix_tile_is_a_built_variant(members):
     info = bt.plan(None)
     assert info.prefix_waves in (1, 2, 4)
     assert info.prefix_waves * 32 * info.prefix_mtiles >= members * 4
+
+
+@pytest.mark.parametrize("shape", [
+    # (requests, groups, prefix lengths, Hq, Hkv)
+    (64, 1, [16384], 32, 8),                 # Llama-3.1-8B layer, one shared prefix
+    (128, 1, [16384], 20, 4),                # Qwen-2.5-14B half-head share
+    (256, 1, [16384], 10, 2),                # Qwen-2.5-32B quarter-head share
+    (256, 1, [4096], 10, 2),
+    (256, 1, [32768], 10, 2),
+    (128, 8, [2048, 16384, 9000, 4100, 12000, 7000, 15000, 3000], 32, 8),   # eight prefix groups
+])
+def test_prefix_blocks_fit_one_resident_round(shape):
+    # Two prefix blocks are resident per CU (256 CUs): a grid of more than 512
+    # live blocks runs a second, mostly idle round.
+    n, ng, lps, hq, hkv = shape
+    groups = [min(i // (n // ng), ng - 1) for i in range(n)]
+    bt = batch_of([300] * n, groups, lps, hkv=hkv, hq=hq)
+    info = bt.plan(None)
+    assert 0 < info.prefix_items <= 2 * 256
+    # and the chunk does not grow past what one round needs
+    units = sum(hkv * -(-(groups.count(g) * (hq // hkv)) // (32 * info.prefix_waves)) for g in range(ng))
+    assert info.prefix_items >= min(2 * 256, units) // 2
