@@ -29,7 +29,10 @@ constexpr int kPrefixSplitCap = 64;    // partials per row from the prefix pass
 constexpr int kPrefixKeyTile = 32;     // keys per MFMA tile in the prefix kernel
 constexpr int kFlatWaves = 4;          // KV heads (one wave each) per flat block
 constexpr int kFlatMinTokens = 64;     // shortest flat range per block
-constexpr int kFlatWaveSlots = 16;     // resident flat waves per CU (128 VGPRs)
+constexpr int kFlatWaveSlots = 16;     // resident flat waves per CU (128 VGPRs), float32 pass
+constexpr int kFlatMfmaTokens = 16;    // tokens per ring stage of the bf16 (MFMA) paged pass
+constexpr int kFlatMfmaStages = 4;     // ring stages per wave of the bf16 paged pass
+constexpr int kLdsPerCU = 160 * 1024;  // LDS bytes per CU (gfx950)
 constexpr int kSplitPBelow = 256;      // prefixes shorter than this carry P as bf16 hi + lo
 
 // Per-group cascade bitmask passed to kernels by value.
@@ -95,6 +98,19 @@ struct Plan {
     bool prefix_split_p;      // some cascade group is short: carry P as bf16 hi + lo
     bool prefix_as_flat;      // float32 pools: prefix part via a per-request pass
 };
+
+// LDS bytes of one wave of the bf16 paged pass: its ring (K and V rows of
+// kFlatMfmaTokens tokens per stage) and a 64-entry block-table buffer.
+SPKV_HD constexpr int flat_mfma_wave_bytes(int d) { return kFlatMfmaStages * 2 * kFlatMfmaTokens * d * 2 + 256; }
+
+// Resident paged-pass blocks per CU for blocks of `hpb` waves: the float32
+// pass is bound by registers (kFlatWaveSlots waves), the bf16 pass by its
+// LDS rings.
+inline int flat_blocks_per_cu(bool bf16, int d, int hpb) {
+    if (!bf16) return kFlatWaveSlots / hpb > 0 ? kFlatWaveSlots / hpb : 1;
+    const int n = kLdsPerCU / (hpb * flat_mfma_wave_bytes(d));
+    return n > 0 ? n : 1;
+}
 
 // Chunk length of one request or group: at least `tau`, large enough that at
 // most `cap` chunks cover `len`, rounded up to `granule`.

@@ -34,6 +34,7 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -450,18 +451,299 @@ __device__ __forceinline__ void attend_range(const Args &a, const Req &r, int b,
     }
 }
 
-// Occupancy: 4 waves per SIMD (<= 128 VGPRs) for group sizes up to 5.
-// Occupancy: 4 waves per SIMD (<= 128 VGPRs) up to G = 6, 3 above; the LDS
-// ring (4 x 8.25 KB per block of 4 waves) admits 4 blocks per CU.
+// ---------------------------------------------------------------------------
+// Flat paged pass, bf16: scores and the weighted sum on MFMA.  One wave per
+// KV head as above; the head's G query rows are the N columns of 16x16 MFMA
+// tiles (columns n >= G carry zero queries and are never stored).  Per ring
+// stage of 16 tokens:
+//   S^T[token, row] = K_stage . Q^T          D/32 x v_mfma_f32_16x16x32_bf16
+//   online softmax along tokens, in the log2 domain
+//   O^T[dim, row]  += V_stage^T . P^T         D/16 x 2 x v_mfma_f32_16x16x16_bf16
+// 16x16 MFMA operand layouts (n = lane % 16, q = lane / 16):
+//   16x16x32: A[m][k] in lane m + 16*(k/8), element k%8; B[k][n] likewise
+//   16x16x16: A[m][k] in lane m + 16*(k/4), element k%4; B[k][n] likewise
+//   D[m][n] in lane n + 16*(m/4), register m%4
+// so the score tile gives lane (n, q) row n's scores of tokens 4q .. 4q+3,
+// which is exactly its B operand of the P.V step.  P goes to the MFMA as two
+// bf16 terms (hi + lo), so the weights carry ~16 significant bits.  V^T comes
+// from LDS by transposing reads (ds_read_b64_tr_b16: within 16 lanes, lane i
+// receives element e of the 8-byte chunk addressed by lane 4e + i/4,
+// component i%4).
+//
+// K and V rows are gathered into a per-wave LDS ring by DMA as in the float32
+// pass; a DMA lands 1 KB (RPI rows), lane l at +16*l.  The 16-byte chunks of
+// a stage row are XOR-swizzled (K: by the row, V: by pairs) so that the K
+// reads (16 rows, one chunk each) and the transposing V reads (16 rows,
+// 32 bytes each) spread over all LDS banks.
+// ---------------------------------------------------------------------------
+template <int D>
+struct FlatMfmaGeom {
+    static constexpr int S = spkv::kFlatMfmaStages;
+    static constexpr int TOK = spkv::kFlatMfmaTokens;   // tokens per stage
+    static constexpr int ROWB = D * 2;                   // bytes per K/V row
+    static constexpr int OPB = TOK * ROWB;               // bytes per stage operand
+    static constexpr int STAGEB = 2 * OPB;               // K then V
+    static constexpr int CPR = ROWB / 16;                // 16-byte chunks per row
+    static constexpr int RPI = 1024 / ROWB;              // rows per wave-wide DMA
+    static constexpr int NDMA = TOK / RPI;               // DMAs per operand per stage
+    static constexpr int RPP = 256 / ROWB;               // rows per 256-byte bank period
+    static constexpr int SPB = 64 / TOK;                 // stages per 64-token block
+    static constexpr int TABB = 256;
+    static constexpr int WAVEB = S * STAGEB + TABB;
+    static constexpr int KS = D / 32;                    // score MFMAs per stage
+    static constexpr int NDB = D / 16;                   // 16-dim output blocks
+    static_assert(TOK == 16, "one 16x16 score tile per stage");
+    static_assert(S - 1 < SPB, "prologue stays inside the first 64-token block");
+    static_assert((S & (S - 1)) == 0, "ring index is a mask");
+};
+static_assert(FlatMfmaGeom<128>::WAVEB == spkv::flat_mfma_wave_bytes(128), "plan and kernel agree on the ring");
+static_assert(FlatMfmaGeom<64>::WAVEB == spkv::flat_mfma_wave_bytes(64), "plan and kernel agree on the ring");
+
+// Physical chunk of logical chunk c in stage row r (an involution in c).
+template <int D>
+__device__ __forceinline__ int kswz(int r, int c) {
+    using F = FlatMfmaGeom<D>;
+    return c ^ ((r / F::RPP) & (F::CPR - 1));
+}
+template <int D>
+__device__ __forceinline__ int vswz(int r, int c) {
+    using F = FlatMfmaGeom<D>;
+    return c ^ (2 * ((r / F::RPP) & (F::CPR / 2 - 1)));
+}
+
+// Reductions over the four 16-lane groups (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float max_of_groups(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_of_groups(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+template <int D, int G>
+__device__ __forceinline__ void attend_range_mfma(const Args &a, const Req &r, int b, int h, int t0, int t1,
+                                                  int slot, int lane, char *ring, uint32_t ring_off) {
+    using F = FlatMfmaGeom<D>;
+    constexpr int S = F::S, TOK = F::TOK, SPB = F::SPB, NDMA = F::NDMA, KS = F::KS, NDB = F::NDB;
+    constexpr float kRescaleSlack = 8.f;     // see the prefix kernel: exact for any reference
+    static_assert(G >= 1 && G <= 16, "query rows of a head fit the 16 MFMA columns");
+
+    const int n = lane & 15;                 // query row of the head (padding when >= G)
+    const int q = lane >> 4;                 // 16-lane group
+    const int row0 = b * a.Hq + h * G;
+
+    const char *khot = (const char *)a.k_hot;
+    const char *vhot = (const char *)a.v_hot;
+    const char *kcold = (const char *)a.k_cold;
+    const char *vcold = (const char *)a.v_cold;
+    const int32_t *table = a.tables + (int64_t)b * a.max_blocks;
+    const int64_t num_pages = a.cold_slots / a.page_size;
+    const uint32_t hot_row0 = (uint32_t)(r.base * a.Hkv + (int64_t)h * r.lp);
+    const int32_t *tab_lds = (const int32_t *)(ring + S * F::STAGEB);
+    const uint32_t tab_off = ring_off + S * F::STAGEB;
+
+    // Row codes (HOT slab row, bit 31 set, or COLD slot row), one token of the
+    // current 64-token block per lane, exactly as in the float32 pass.
+    auto lane_token = [&](int nb) { return min(t0 + 64 * nb + lane, t1 - 1); };
+    auto first_entry = [&](int nb) { return (max(t0 + 64 * nb, r.lp) - r.lp) / a.page_size; };
+    auto block_has_cold = [&](int nb) { return t0 + 64 * nb < t1 && t0 + 64 * nb + 63 >= r.lp; };
+    auto code_of = [&](int t, int32_t entry) -> uint32_t {
+        if (t < r.lp) return 0x80000000u | (hot_row0 + (uint32_t)t);
+        int64_t page = entry;
+        page = page < 0 ? 0 : (page >= num_pages ? num_pages - 1 : page);
+        return (uint32_t)((page * a.page_size + (t - r.lp) % a.page_size) * a.Hkv + h);
+    };
+    auto table_dma = [&](int nb) {
+        const int e = max(0, min(first_entry(nb) + lane, a.max_blocks - 1));
+        dma4(table, (uint32_t)e * 4u, tab_off);
+    };
+    auto code_from_lds = [&](int nb) -> uint32_t {
+        const int t = lane_token(nb);
+        int32_t entry = 0;
+        if (t >= r.lp) entry = tab_lds[max(0, min((t - r.lp) / a.page_size - first_entry(nb), 63))];
+        return code_of(t, entry);
+    };
+
+    // Q^T as the B operand of the score MFMAs: lane (n, q) holds elements
+    // 32s + 8q .. 32s + 8q + 7 of query row n for step s (zeros for n >= G).
+    // Loaded, with the row codes of block 0, before any DMA is in flight.
+    bf16x8_t qb[KS];
+    {
+        const uint16_t *qp = (const uint16_t *)a.q + (int64_t)(row0 + min(n, G - 1)) * D + 8 * q;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const u32x4_t v = n < G ? *(const u32x4_t *)(qp + 32 * s) : u32x4_t{0, 0, 0, 0};
+            qb[s] = __builtin_bit_cast(bf16x8_t, v);
+        }
+    }
+    uint32_t code;
+    {
+        const int t = lane_token(0);
+        int32_t entry = 0;
+        if (t >= r.lp) entry = table[max(0, min((t - r.lp) / a.page_size, a.max_blocks - 1))];
+        code = code_of(t, entry);
+    }
+#pragma unroll
+    for (int s = 0; s < KS; ++s) asm volatile("" ::"v"(__builtin_bit_cast(u32x4_t, qb[s])));
+    asm volatile("" ::"v"(code));
+
+    // Loop-invariant offsets.  DMA i of an operand lands stage rows
+    // RPI*i .. RPI*i + RPI-1; this lane writes row RPI*i + lane / CPR at
+    // physical chunk lane % CPR and so fetches the logical chunk kept there.
+    uint32_t ksrc[NDMA], vsrc[NDMA];
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i) {
+        const int rr = F::RPI * i + lane / F::CPR, p = lane % F::CPR;
+        ksrc[i] = (uint32_t)(kswz<D>(rr, p) << 4);
+        vsrc[i] = (uint32_t)(vswz<D>(rr, p) << 4);
+    }
+    // LDS reads (absolute LDS addresses of ring slot 0).  K for score step s:
+    // row n (token), logical chunk 4s + q.  V for output block db: lane
+    // (j = n, q) reads row 4q + j/4, bytes 32*db + 8*(j%4) of the row, i.e.
+    // logical chunk 2*db + (j%4)/2 at byte 8*(j%2).
+    uint32_t krd[KS], vrd[NDB];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) krd[s] = ring_off + (uint32_t)(n * F::ROWB + (kswz<D>(n, 4 * s + q) << 4));
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+        const int rr = 4 * q + n / 4;
+        vrd[db] = ring_off + (uint32_t)(F::OPB + rr * F::ROWB + (vswz<D>(rr, 2 * db + (n & 3) / 2) << 4) + 8 * (n & 1));
+    }
+
+    // Stage j: tokens t0 + 16j .. t0 + 16j + 15 into ring slot j % S.
+    auto issue = [&](int j) {
+        const uint32_t dst = ring_off + (uint32_t)((j & (S - 1)) * F::STAGEB);
+#pragma unroll
+        for (int i = 0; i < NDMA; ++i) {
+            const int ti = (j % SPB) * TOK + F::RPI * i + lane / F::CPR;   // token inside its 64-block
+            const uint32_t c = (uint32_t)__shfl((int)code, ti, 64);
+            const bool hot = c >> 31;
+            const int64_t off = (int64_t)(c & 0x7fffffffu) * F::ROWB;
+            dma16_at((hot ? khot : kcold) + off + ksrc[i], dst + 1024u * i);
+            dma16_at((hot ? vhot : vcold) + off + vsrc[i], dst + F::OPB + 1024u * i);
+        }
+    };
+
+    f32x4_t oacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+    const float c2 = a.scale_log2;
+    const int nvalid = t1 - t0;
+    typedef v4i16_t __attribute__((address_space(3))) *lds_v4i16_ptr;
+    typedef bf16x8_t __attribute__((address_space(3))) *lds_bf16x8_ptr;
+
+    // Stage j from ring slot st (st == j % S, a constant after unrolling).
+    auto compute = [&](int j, int st) {
+        // All LDS reads of the stage first (their latencies overlap), then the math.
+        bf16x8_t kf[KS];
+        s16x4_t va[NDB];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) kf[s] = *(lds_bf16x8_ptr)(uintptr_t)(krd[s] + st * F::STAGEB);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+            va[db] = __builtin_bit_cast(s16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                     (lds_v4i16_ptr)(uintptr_t)(vrd[db] + st * F::STAGEB)));
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], qb[s], sacc, 0, 0, 0);
+        float sv[4];
+        const int tok = j * TOK + 4 * q;         // first of this lane's four tokens, relative to t0
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sv[i] = tok + i < nvalid ? sacc[i] * c2 : -INFINITY;
+        const float mx = max_of_groups(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
+        const bool grow = mx > m_run + kRescaleSlack;
+        if (__any(grow)) {
+            const float mnew = grow ? mx : m_run;
+            const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
+            m_run = mnew;
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+        }
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sv[i] - m_run);
+        l_run += (p[0] + p[1]) + (p[2] + p[3]);
+        const bf16x2_t h01 = {(__bf16)p[0], (__bf16)p[1]}, h23 = {(__bf16)p[2], (__bf16)p[3]};
+        const uint32_t w01 = __builtin_bit_cast(uint32_t, h01), w23 = __builtin_bit_cast(uint32_t, h23);
+        const bf16x2_t l01 = {(__bf16)(p[0] - bf16lo(w01)), (__bf16)(p[1] - bf16hi(w01))};
+        const bf16x2_t l23 = {(__bf16)(p[2] - bf16lo(w23)), (__bf16)(p[3] - bf16hi(w23))};
+        const s16x4_t phi = __builtin_bit_cast(s16x4_t, u32x2_t{w01, w23});
+        const s16x4_t plo = __builtin_bit_cast(
+            s16x4_t, u32x2_t{__builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23)});
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[db], phi, oacc[db], 0, 0, 0);
+            oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[db], plo, oacc[db], 0, 0, 0);
+        }
+    };
+
+    const int n_st = (nvalid + TOK - 1) / TOK;
+    if (block_has_cold(1)) table_dma(1);
+    const int pro = min(S - 1, n_st);
+    for (int j = 0; j < pro; ++j) issue(j);
+    for (int j0 = 0; j0 < n_st; j0 += S) {
+#pragma unroll
+        for (int st = 0; st < S; ++st) {
+            const int j = j0 + st;
+            if (j >= n_st) break;
+            const int jn = j + S - 1;
+            if (jn < n_st) {
+                wait_vm_lds<2 * NDMA * (S - 2)>();   // stage j landed: only stages j+1 .. j+S-2 in flight
+                if (jn % SPB == 0) {                 // first stage of block jn/SPB: its table entries landed
+                    const int nb = jn / SPB;
+                    code = code_from_lds(nb);
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // table read before it is overwritten
+                    if (block_has_cold(nb + 1)) table_dma(nb + 1);
+                }
+                issue(jn);
+            } else {
+                wait_vm_lds<0>();
+            }
+            compute(j, st);
+        }
+    }
+
+    // Every DMA has landed (the last stages waited for all), so the ring may
+    // be reused.  The four lane groups hold disjoint dims of the same rows and
+    // the same reference m_run; only the normaliser needs their sum.
+    const float lt = sum_of_groups(l_run);
+    if (n < G) {
+        const int64_t prow = (int64_t)(row0 + n) * a.splits_total + slot;
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        float *dst = a.o_part + prow * D + 4 * q;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+            *(float4 *)(dst + 16 * db) =
+                make_float4(oacc[db][0] * inv, oacc[db][1] * inv, oacc[db][2] * inv, oacc[db][3] * inv);
+        if (q == 0) a.lse_part[prow] = lt > 0.f ? m_run + __log2f(lt) : -INFINITY;
+    }
+}
+
+// Occupancy, float32: 4 waves per SIMD (<= 128 VGPRs) up to G = 6, 3 above;
+// the LDS ring (4 x 8.25 KB per block of 4 waves) admits 4 blocks per CU.
+// bf16: the LDS ring (4 x 8 KB per wave for d = 128) admits one or two
+// blocks per CU, so registers are not the limit.
 template <bool BF16, int D, int G>
-__global__ __launch_bounds__(256, (G <= 6 ? 4 : 3)) void flat_kernel(Args a, int part, FlatLaunch fl) {
+__global__ __launch_bounds__(256, (BF16 ? 2 : (G <= 6 ? 4 : 3))) void flat_kernel(Args a, int part, FlatLaunch fl) {
     extern __shared__ __attribute__((aligned(1024))) char flat_smem[];
     const int k = blockIdx.x;
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int h = blockIdx.y * kFlatWavesMax + wave;
     if (h >= a.Hkv) return;
-    char *ring = flat_smem + wave * FlatGeom<BF16, D>::WAVEB;
+    constexpr int WAVEB = BF16 ? FlatMfmaGeom<D>::WAVEB : FlatGeom<BF16, D>::WAVEB;
+    char *ring = flat_smem + wave * WAVEB;
     const uint32_t ring_off = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_offset(ring));
     const int64_t T = fl.total;
     const int nb = fl.blocks;
@@ -488,7 +770,8 @@ __global__ __launch_bounds__(256, (G <= 6 ? 4 : 3)) void flat_kernel(Args a, int
         const int t0 = lo + (int)(lo_s - o0);
         const int t1 = min(hi, lo + (int)(hi_s - o0));   // device data shorter than the plan: clamp
         if (t1 <= t0) continue;
-        attend_range<BF16, D, G>(a, r, b, h, t0, t1, slot0 + slot, lane, ring, ring_off);
+        if constexpr (BF16) attend_range_mfma<D, G>(a, r, b, h, t0, t1, slot0 + slot, lane, ring, ring_off);
+        else attend_range<BF16, D, G>(a, r, b, h, t0, t1, slot0 + slot, lane, ring, ring_off);
     }
 }
 
@@ -516,7 +799,6 @@ __global__ __launch_bounds__(256, (G <= 6 ? 4 : 3)) void flat_kernel(Args a, int
 // the 4x16-bit chunk addressed by lane 4e + i/4, component i%4) hit distinct
 // banks.
 // ---------------------------------------------------------------------------
-typedef short v4i16_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ int swap_bits23(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
 
 // V tile chunk placement.  Logical 16-byte chunk c of LDS row r sits at
@@ -1059,24 +1341,34 @@ spkv_status check_launch(const char *what) {
     return SPKV_OK;
 }
 
+// Dynamic LDS above 64 KB is granted per kernel once its limit is raised.
+template <bool BF16, int D, int G>
+spkv_status launch_flat_g(const Args &a, int part, const FlatLaunch &f, dim3 grid, dim3 block, size_t lds,
+                          hipStream_t st) {
+    static const hipError_t attr = hipFuncSetAttribute((const void *)flat_kernel<BF16, D, G>,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, spkv::kLdsPerCU);
+    if (attr != hipSuccess) return fail(SPKV_E_HIP, std::string("flat_kernel LDS limit: ") + hipGetErrorString(attr));
+    flat_kernel<BF16, D, G><<<grid, block, lds, st>>>(a, part, f);
+    return check_launch("flat_kernel");
+}
+
 template <bool BF16, int D>
 spkv_status launch_flat_d(const Args &a, int part, const FlatLaunch &f, int head_groups, hipStream_t st) {
     const int waves = a.Hkv < kFlatWavesMax ? a.Hkv : kFlatWavesMax;
     dim3 grid(f.blocks, head_groups), block(64 * waves);
-    const size_t lds = (size_t)waves * FlatGeom<BF16, D>::WAVEB;
+    const size_t lds = (size_t)waves * (BF16 ? FlatMfmaGeom<D>::WAVEB : FlatGeom<BF16, D>::WAVEB);
     TimedLaunch tl(SPKV_KERNEL_FLAT, st);
     switch (a.G) {
-    case 1: flat_kernel<BF16, D, 1><<<grid, block, lds, st>>>(a, part, f); break;
-    case 2: flat_kernel<BF16, D, 2><<<grid, block, lds, st>>>(a, part, f); break;
-    case 3: flat_kernel<BF16, D, 3><<<grid, block, lds, st>>>(a, part, f); break;
-    case 4: flat_kernel<BF16, D, 4><<<grid, block, lds, st>>>(a, part, f); break;
-    case 5: flat_kernel<BF16, D, 5><<<grid, block, lds, st>>>(a, part, f); break;
-    case 6: flat_kernel<BF16, D, 6><<<grid, block, lds, st>>>(a, part, f); break;
-    case 7: flat_kernel<BF16, D, 7><<<grid, block, lds, st>>>(a, part, f); break;
-    case 8: flat_kernel<BF16, D, 8><<<grid, block, lds, st>>>(a, part, f); break;
+    case 1: return launch_flat_g<BF16, D, 1>(a, part, f, grid, block, lds, st);
+    case 2: return launch_flat_g<BF16, D, 2>(a, part, f, grid, block, lds, st);
+    case 3: return launch_flat_g<BF16, D, 3>(a, part, f, grid, block, lds, st);
+    case 4: return launch_flat_g<BF16, D, 4>(a, part, f, grid, block, lds, st);
+    case 5: return launch_flat_g<BF16, D, 5>(a, part, f, grid, block, lds, st);
+    case 6: return launch_flat_g<BF16, D, 6>(a, part, f, grid, block, lds, st);
+    case 7: return launch_flat_g<BF16, D, 7>(a, part, f, grid, block, lds, st);
+    case 8: return launch_flat_g<BF16, D, 8>(a, part, f, grid, block, lds, st);
     default: return fail(SPKV_E_INVAL, "unsupported GQA group size");
     }
-    return check_launch("flat_kernel");
 }
 
 spkv_status launch_flat(const Args &a, bool bf16, int d, int part, const FlatLaunch &f, int head_groups,

@@ -94,10 +94,11 @@ static inline bool mask_get(const GroupMask &m, int g) { return (m.bits[g >> 5] 
 // ranges per head group as one full round of resident blocks, no shorter than
 // kFlatMinTokens, and few enough that no request spans more than
 // kFlatSplitCap ranges.
-static std::vector<FlatLaunch> plan_flat(const std::vector<int64_t> &L, int head_groups, int hpb, int32_t num_cus) {
+static std::vector<FlatLaunch> plan_flat(const std::vector<int64_t> &L, int head_groups, int blocks_per_cu,
+                                         int32_t num_cus) {
     std::vector<FlatLaunch> out;
     const int B = (int)L.size();
-    const int64_t resident = std::max<int64_t>(1, (int64_t)num_cus * kFlatWaveSlots / hpb / head_groups);
+    const int64_t resident = std::max<int64_t>(1, (int64_t)num_cus * blocks_per_cu / head_groups);
     for (int b0 = 0; b0 < B; b0 += kFlatArgReqs) {
         FlatLaunch f{};
         f.b0 = b0;
@@ -155,7 +156,7 @@ spkv_status make_plan(const spkv_batch *b, const int32_t *cascade, int32_t num_c
             const bool dense_member = g >= 0 && !mask_get(p->cascade, g);
             L[(size_t)i] = b->host_cold_lens[i] + (dense_member ? b->host_hot_len[g] : 0);
         }
-        p->flat = plan_flat(L, p->flat_head_groups, hpb, num_cus);
+        p->flat = plan_flat(L, p->flat_head_groups, flat_blocks_per_cu(bf16, D, hpb), num_cus);
     }
     p->flat_splits = 0;
     p->flat_chunk = 0;
@@ -207,7 +208,7 @@ spkv_status make_plan(const spkv_batch *b, const int32_t *cascade, int32_t num_c
             const int g = b->host_group_of[i];
             L[(size_t)i] = (g >= 0 && mask_get(p->cascade, g)) ? b->host_hot_len[g] : 0;
         }
-        p->pflat = plan_flat(L, p->flat_head_groups, hpb, num_cus);
+        p->pflat = plan_flat(L, p->flat_head_groups, flat_blocks_per_cu(false, D, hpb), num_cus);
         p->prefix_splits = 0;
         p->prefix_chunk = 0;
         for (const auto &f : p->pflat) {
