@@ -82,23 +82,31 @@ struct Req {
     bool casc;      // group takes the prefix contraction
 };
 
+// Load through the constant address space: the kernels never write these
+// arrays, and a wave-uniform address then becomes a scalar load (counted by
+// lgkmcnt, so it never waits for vector-memory DMAs in flight).
+template <class T>
+__device__ __forceinline__ T ld_const(const T *p) {
+    return *(const __attribute__((address_space(4))) T *)p;
+}
+
 __device__ __forceinline__ Req req_geo(const Args &a, int b) {
     Req r;
-    int g = a.group_of[b];
+    int g = ld_const(a.group_of + b);
     r.g = (g >= 0 && g < a.ng) ? g : -1;
     r.base = 0;
     r.lp = 0;
     r.casc = false;
     if (r.g >= 0) {
-        int64_t base = a.hot_base[r.g];
-        int lp = a.hot_len[r.g];
+        int64_t base = ld_const(a.hot_base + r.g);
+        int lp = ld_const(a.hot_len + r.g);
         if (base >= 0 && lp > 0 && base + lp <= a.hot_capacity) {
             r.base = base;
             r.lp = lp;
         }
         r.casc = mask_get(a.cascade, r.g);
     }
-    int ls = a.cold_lens[b];
+    int ls = ld_const(a.cold_lens + b);
     const int64_t cap = (int64_t)a.max_blocks * a.page_size;
     r.ls = ls < 0 ? 0 : (ls > cap ? (int)cap : ls);
     if (a.cold_slots < a.page_size) r.ls = 0;   // no COLD page to read
@@ -749,11 +757,14 @@ __global__ __launch_bounds__(256, (BF16 ? 2 : (G <= 6 ? 4 : 3))) void flat_kerne
     const int nb = fl.blocks;
     const int64_t s0 = (T * k) / nb, s1 = (T * (k + 1)) / nb;
     if (s0 >= s1) return;
-    int i = 0, hi_i = fl.nreq;          // first request whose tokens reach past s0
-    while (i < hi_i) {
-        const int mid = (i + hi_i) >> 1;
-        if (fl.offs[mid + 1] > s0) hi_i = mid;
-        else i = mid + 1;
+    // First request whose tokens reach past s0: the number of requests that
+    // end at or before s0 (offs is non-decreasing), counted in one pass
+    // instead of a chain of dependent loads.
+    int i = 0;
+#pragma unroll
+    for (int j = 0; j < (spkv::kFlatArgReqs + 63) / 64; ++j) {
+        const int idx = lane + 64 * j;
+        i += __popcll(__ballot(idx < fl.nreq && fl.offs[idx + 1] <= s0));
     }
     const int slot0 = part == kPartRest ? a.prefix_splits : 0;
     for (; i < fl.nreq; ++i) {
