@@ -16,6 +16,7 @@
 #include <cmath>
 #include <cstring>
 #include <mutex>
+#include <type_traits>
 #include <vector>
 
 #include "internal.h"
@@ -35,6 +36,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef float f32x4v_t __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -1113,8 +1115,9 @@ __global__ __launch_bounds__(256) void merge_kernel(Args a, float *out, float *l
                                                     FlatLaunch fp) {
     constexpr int LPP = D / 4;      // lanes per partial row (float4 each)
     constexpr int PPW = 64 / LPP;   // partial rows per wave-wide load
-    constexpr int UNR = 4;          // loads in flight per lane
-    const int wave = threadIdx.x >> 6;
+    constexpr int BATCH = 40 / PPW; // wave-wide loads in flight (40 partials)
+    constexpr int SMALL = 16 / PPW; // the same for rows of at most 16 partials
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: geometry by scalar loads
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)fr.b0 * a.Hq + (int64_t)blockIdx.x * 4 + wave;
     if (row >= (int64_t)(fr.b0 + fr.nreq) * a.Hq) return;
@@ -1134,42 +1137,73 @@ __global__ __launch_bounds__(256) void merge_kernel(Args a, float *out, float *l
     const int n = np + nf;           // <= 128
     const int64_t prow0 = row * a.splits_total;
     auto slot_of = [&](int k) { return k < np ? k : a.prefix_splits + (k - np); };
-
-    // Weights: lane k holds partials k and k + 64.
-    const float l0 = lane < n ? a.lse_part[prow0 + slot_of(lane)] : -INFINITY;
-    const float l1 = lane + 64 < n ? a.lse_part[prow0 + slot_of(lane + 64)] : -INFINITY;
-    float mx = fmaxf(l0, l1);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-    const float muse = mx == -INFINITY ? 0.f : mx;
-    const float w0 = exp2f(l0 - muse), w1 = exp2f(l1 - muse);
-    float wsum = w0 + w1;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) wsum += __shfl_xor(wsum, off, 64);
+    if (n == 0) {                    // empty context: zero output, log-sum-exp -inf
+        if (lane < D / 4) *(float4 *)(out + row * D + lane * 4) = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (lse_out && lane == 0) lse_out[row] = -INFINITY;
+        return;
+    }
 
     const int sub = lane % LPP;      // float4 column of the row
     const int which = lane / LPP;    // partial within a wave-wide load
+    // Row base (wave-uniform) plus a 32-bit byte offset per lane.
+    const char *prow_base = (const char *)(a.o_part + prow0 * D);
+    auto part_ptr = [&](int k) {
+        return (const f32x4v_t *)(prow_base + (uint32_t)(slot_of(k) * (D * 4) + sub * 16));
+    };
+
+    // Issue the weights' loads and the first batch of partial rows together:
+    // a row costs about one memory round trip, not one per few partials.
+    // Loads past the last partial re-read partial 0 (in bounds; weight 0), so
+    // a batch is straight-line code with a single wait; rows with few partials
+    // take a smaller batch.  (Non-temporal: partial states are read once, and
+    // must not displace K/V lines the next step reads again.)
+    const float l0 = lane < n ? a.lse_part[prow0 + slot_of(lane)] : -INFINITY;
+    const float l1 = lane + 64 < n ? a.lse_part[prow0 + slot_of(lane + 64)] : -INFINITY;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int k0 = 0; k0 < n; k0 += PPW * UNR) {
-        float4 v[UNR];
-        float w[UNR];
+    float mx = -INFINITY, wsum = 0.f;
+    auto run = [&](auto nb_tag) {
+        constexpr int NB = decltype(nb_tag)::value;
+        f32x4v_t v[NB];
 #pragma unroll
-        for (int u = 0; u < UNR; ++u) {
-            const int k = k0 + u * PPW + which;
+        for (int u = 0; u < NB; ++u) {
+            const int k = u * PPW + which;
+            v[u] = __builtin_nontemporal_load(part_ptr(k < n ? k : 0));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // Weights: lane k holds partials k and k + 64.
+        mx = fmaxf(l0, l1);
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+        const float muse = mx == -INFINITY ? 0.f : mx;
+        const float w0 = exp2f(l0 - muse), w1 = exp2f(l1 - muse);
+        wsum = w0 + w1;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) wsum += __shfl_xor(wsum, off, 64);
+        auto weight = [&](int k) {
             const int kk = k < n ? k : 0;
             const float wa = __shfl(w0, kk & 63, 64), wb = __shfl(w1, kk & 63, 64);
-            w[u] = k < n ? (kk < 64 ? wa : wb) : 0.f;
-            v[u] = k < n ? *(const float4 *)(a.o_part + (prow0 + slot_of(kk)) * D + sub * 4)
-                         : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
+            return k < n ? (kk < 64 ? wa : wb) : 0.f;
+        };
+        for (int k0 = 0;;) {
 #pragma unroll
-        for (int u = 0; u < UNR; ++u) {
-            acc.x = fmaf(w[u], v[u].x, acc.x);
-            acc.y = fmaf(w[u], v[u].y, acc.y);
-            acc.z = fmaf(w[u], v[u].z, acc.z);
-            acc.w = fmaf(w[u], v[u].w, acc.w);
+            for (int u = 0; u < NB; ++u) {
+                const float w = weight(k0 + u * PPW + which);
+                acc.x = fmaf(w, v[u].x, acc.x);
+                acc.y = fmaf(w, v[u].y, acc.y);
+                acc.z = fmaf(w, v[u].z, acc.z);
+                acc.w = fmaf(w, v[u].w, acc.w);
+            }
+            k0 += PPW * NB;
+            if (k0 >= n) break;
+#pragma unroll
+            for (int u = 0; u < NB; ++u) {
+                const int k = k0 + u * PPW + which;
+                v[u] = __builtin_nontemporal_load(part_ptr(k < n ? k : 0));
+            }
         }
-    }
+    };
+    if (n <= PPW * SMALL) run(std::integral_constant<int, SMALL>{});
+    else run(std::integral_constant<int, BATCH>{});
 #pragma unroll
     for (int off = LPP; off < 64; off <<= 1) {
         acc.x += __shfl_xor(acc.x, off, 64);
