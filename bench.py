@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--page-size", type=int, default=None, help="override the COLD page size")
     ap.add_argument("--contiguous", action="store_true", help="COLD pages handed out in order (no shuffle)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle timing sample")
+    ap.add_argument("--cold-runs", type=int, default=50,
+                    help="timed runs of the cold-cache protocol (0: skip); 10 untimed runs precede them")
+    ap.add_argument("--flush-mib", type=int, default=1024, help="bytes written before each cold-cache run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM traffic per launch (written by shared_prefix_paged_amd/profile_step.py)")
@@ -174,7 +177,8 @@ def main():
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
     cfg = W.CONFIGS[args.config]
-    total_steps = args.warmup + 2 * args.steps + 1
+    cold_warm = 10 if args.cold_runs > 0 else 0
+    total_steps = args.warmup + 2 * args.steps + 1 + cold_warm + max(0, args.cold_runs)
     wl = W.make_workload(cfg, prefix_len=args.lp, page_size=args.page_size, extra_steps=max(32, total_steps + 1))
     if args.contiguous:
         wl.free_order = None
@@ -206,7 +210,7 @@ def main():
     lp_of = np.array([wl.prefix_len_of(b) for b in range(B)], dtype=np.int64)
     state = {"i": 0, "choice": None}
 
-    def one_step():
+    def one_step(flush=None):
         i = state["i"]
         slots, cows = cold.append_batch(seqs)                       # host allocator
         if cows:
@@ -217,6 +221,8 @@ def main():
                         tables=batch.tables, max_blocks=mb, lens=batch.lens)
         batch.lens_h += 1                                            # host mirror of the lengths
         batch.struct.q = q_steps[i].data_ptr()
+        if flush is not None:
+            flush()                                                  # outside the event window
         _, _, choice = R.decode_step(batch, pools, params, ws, out, lse)
         state["choice"] = choice
         state["i"] = i + 1
@@ -255,6 +261,52 @@ def main():
         torch.cuda.synchronize()
     kt_ms = {k: kt.read(k) for k in (A.SPKV_KERNEL_PREFIX, A.SPKV_KERNEL_FLAT, A.SPKV_KERNEL_MERGE,
                                      A.SPKV_KERNEL_CACHE)}
+
+    # ---- cold-cache protocol: the last-level cache (256 MB) and the L2s are
+    # flushed by a large write (then a read of another buffer, so the flush's
+    # dirty lines are written back beforehand) before each timed run; the
+    # flush completes before the attention call, and a run's time is the sum
+    # of its attention kernels' event durations (host planning and the append
+    # are outside it).
+    cold_res = None
+    if args.cold_runs > 0:
+        scratch = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device=dev)
+        clean = torch.zeros(args.flush_mib << 20, dtype=torch.uint8, device=dev)
+        fill = [0]
+
+        def flush():
+            # the write evicts every cached line; reading a second buffer then
+            # writes those dirty lines back and leaves clean ones, so no
+            # write-back of the flush lands inside the timed window
+            fill[0] ^= 1
+            scratch.fill_(fill[0])
+            clean.view(torch.int64).sum()
+
+        for _ in range(cold_warm):
+            one_step(flush)
+        torch.cuda.synchronize()
+        times, toks = [], []
+        attn_ids = (A.SPKV_KERNEL_PREFIX, A.SPKV_KERNEL_FLAT, A.SPKV_KERNEL_MERGE)
+
+        def flush_and_wait():
+            flush()
+            torch.cuda.synchronize()
+
+        for _ in range(args.cold_runs):
+            with R.KernelTimer() as ktc:
+                toks.append(one_step(flush_and_wait))
+                torch.cuda.synchronize()
+                times.append(1e3 * sum(ktc.read(k)[0] for k in attn_ids))
+        del scratch, clean
+        t = np.array(times)
+        med = float(np.median(t))
+        cold_res = {"runs": args.cold_runs, "flush_bytes": args.flush_mib << 20,
+                "median_us": round(med, 2), "p10_us": round(float(np.percentile(t, 10)), 2),
+                "p90_us": round(float(np.percentile(t, 90)), 2),
+                "kv_tokens_per_s": round(float(np.median(toks)) / (med * 1e-6), 1),
+                "window": "sum of the attention kernels' event durations, after a write of flush_bytes "
+                          "and a read of as many other bytes have completed",
+                "warm_attention_us": None}
     choice = state["choice"]
     cascade = bool(len(choice) and choice[0])
     plan = batch.plan(list(map(int, choice)) if len(choice) else None)
@@ -312,11 +364,26 @@ def main():
     roofline["kernel"] = dom
     roofline["traffic"] = measured_traffic(args.traffic, args.config, args.mode, dom)
     attn_us = sum(k["avg_us"] for k in kernels.values())
+    if cold_res is not None:
+        cold_res["warm_attention_us"] = round(attn_us, 2)
+    # Step roofline: T* = sum over kernels of max(bytes / HBM peak, flops / MFMA peak).
+    t_star = 0.0
+    for name, nbytes, flops in (("prefix_mfma", prefix_bytes, prefix_flops), ("flat_paged", flat_bytes, 0.0),
+                                ("merge", merge_bytes, 0.0)):
+        if name in kernels:
+            t_star += max(nbytes / (HBM_PEAK_GBPS * 1e3), flops / (BF16_PEAK_TFLOPS * 1e6))
+    step_roofline = {"t_star_us": round(t_star, 2), "t_measured_us": round(attn_us, 2),
+                     "frac": round(t_star / attn_us, 4) if attn_us > 0 else None,
+                     "note": "T* = sum over kernels of max(alg bytes / 8 TB/s, alg flops / 2.5 PFLOP/s); "
+                             "T measured = sum of per-kernel event durations (warm)"}
+    if cold_res is not None:
+        cold_res["step_roofline_frac"] = round(t_star / cold_res["median_us"], 4)
 
     # ---- oracle on the host cores, bounded sample ---------------------------
-    cpu = None
+    cpu = cpu_1t = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, args.cpu_seconds)
+        cpu_1t = cpu_baseline(wl, args.cpu_seconds / 2, threads=1)
 
     line = {
         "metric": METRIC,
@@ -345,29 +412,37 @@ def main():
         "kernels": kernels,
         "plan": {f: int(getattr(plan, f)) for f, _ in plan._fields_},
         "roofline": roofline,
+        "step_roofline": step_roofline,
+        "cold_cache": cold_res,
         "cpu_baseline": cpu,
+        "cpu_baseline_1t": cpu_1t,
     }
     print(json.dumps(line), flush=True)
     return 0
 
 
-def cpu_baseline(wl, budget_s: float):
-    """The oracle, untuned, on the host cores: fp64 attention per request until the budget is spent."""
-    import numpy as np
+def cpu_baseline(wl, budget_s: float, threads=None):
+    """The oracle, untuned, on the host cores: fp64 attention per request until
+    the budget is spent.  threads=1 limits the BLAS pools to one thread."""
+    import contextlib
     from oracle.attention import decode_reference
+    limit = contextlib.nullcontext()
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        from threadpoolctl import threadpool_info, threadpool_limits
+        if threads is not None:
+            limit = threadpool_limits(limits=threads)
+        pool = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
-        threads = os.cpu_count() or 1
-    cores = min(threads, len(os.sched_getaffinity(0)))
+        pool = os.cpu_count() or 1
+    cores = 1 if threads == 1 else min(pool, len(os.sched_getaffinity(0)))
     done, tokens, t0 = 0, 0, time.perf_counter()
     order = list(range(wl.batch))
-    while done < len(order) and time.perf_counter() - t0 < budget_s:
-        b = order[done]
-        decode_reference(wl, rows=[b])
-        tokens += wl.prefix_len_of(b) + int(wl.suffix_len[b])
-        done += 1
+    with limit:
+        while done < len(order) and time.perf_counter() - t0 < budget_s:
+            b = order[done]
+            decode_reference(wl, rows=[b])
+            tokens += wl.prefix_len_of(b) + int(wl.suffix_len[b])
+            done += 1
     el = time.perf_counter() - t0
     return {"value": round(tokens / el, 1), "unit": "KV-tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{done} of {wl.batch} requests of the same workload (all query heads, "
