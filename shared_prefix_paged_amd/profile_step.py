@@ -92,7 +92,7 @@ def main():
     prof_dir = os.path.abspath(a.prof_dir)
     os.makedirs(prof_dir, exist_ok=True)
     bench = os.path.join(ROOT, "bench.py")
-    run = [bench, "--config", a.config, "--mode", a.mode, "--no-cpu-baseline"]
+    run = [bench, "--config", a.config, "--mode", a.mode, "--no-cpu-baseline", "--cold-runs", "0"]
     name = f"{a.config.lower()}_{a.mode}"
 
     # 1. kernel trace + stats of the bench command
