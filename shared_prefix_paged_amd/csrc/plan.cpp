@@ -328,14 +328,16 @@ spkv_status spkv_plan_parts(const spkv_batch *batch, const int32_t *cascade, int
 void spkv_dispatch_params_default(spkv_dispatch_params *p) {
     if (!p) return;
     // Fitted on MI355X from the prefix-length sweeps of the 8B-shaped (B = 64,
-    // M = 256) and 32B-shaped (B = 256, M = 1280) workloads: the flat pass
-    // re-reads a shared prefix at ~6.5 TB/s (cache-assisted), the prefix
-    // contraction runs at ~420 TFLOP/s, and the cascade path costs ~10 us more
-    // per step (prefix launch, extra partial states); crossover near Lp = 260.
+    // M = 256) and 32B-shaped (B = 256, M = 1280) workloads with the MFMA
+    // paged pass: the flat pass re-reads a shared prefix at ~10 TB/s (the
+    // re-reads are mostly cache hits), the prefix contraction runs at
+    // ~420 TFLOP/s, and taking the cascade path at all costs ~18 us per step
+    // (the prefix launch and its partial states); crossover between Lp = 512
+    // and 1024 at both shapes.
     p->mode = SPKV_MODE_PER_GROUP;
     p->min_group_requests = 2;
-    p->fixed_cost_us = 10.0;
-    p->flat_gbps = 6500.0;
+    p->fixed_cost_us = 18.0;
+    p->flat_gbps = 10000.0;
     p->prefix_gbps = 4000.0;
     p->prefix_tflops = 420.0;
 }
@@ -367,21 +369,30 @@ spkv_status spkv_dispatch(const spkv_batch *b, const spkv_dispatch_params *prm, 
     }
     if (prm->flat_gbps <= 0 || prm->prefix_gbps <= 0 || prm->prefix_tflops <= 0)
         return fail(SPKV_E_INVAL, "dispatch: rates must be positive");
+    // A group's benefit from cascade is the time the flat pass spends re-reading
+    // its prefix for every member, minus its prefix contraction.  The fixed
+    // cost is paid once per step by whichever groups take cascade, so the set
+    // of groups with a positive benefit goes cascade exactly when their total
+    // benefit exceeds it (this minimises the modelled step time).
+    double total = 0.0;
     for (int g = 0; g < ng; ++g) {
+        cascade_out[g] = 0;
         const int64_t n = b->host_group_indptr[g + 1] - b->host_group_indptr[g];
         const double lp = (double)b->host_hot_len[g];
-        if (n < prm->min_group_requests || lp <= 0 || b->dtype != SPKV_DTYPE_BF16) {
-            cascade_out[g] = 0;
-            continue;
-        }
+        if (n < prm->min_group_requests || lp <= 0 || b->dtype != SPKV_DTYPE_BF16) continue;
         // Effective M of the group's prefix contraction (Eq. (2) per group).
         const double m_eff = (double)n * G;
         const double t_flat = n * lp * kvb / (prm->flat_gbps * 1e3);                    // us
         const double t_bytes = lp * kvb / (prm->prefix_gbps * 1e3);
         const double t_flops = 4.0 * m_eff * lp * b->head_dim * b->num_kv_heads / (prm->prefix_tflops * 1e6);
-        const double t_casc = std::max(t_bytes, t_flops) + prm->fixed_cost_us;
-        cascade_out[g] = t_casc < t_flat ? 1 : 0;
+        const double benefit = t_flat - std::max(t_bytes, t_flops);
+        if (benefit > 0.0) {
+            cascade_out[g] = 1;
+            total += benefit;
+        }
     }
+    if (total <= prm->fixed_cost_us)
+        for (int g = 0; g < ng; ++g) cascade_out[g] = 0;
     return SPKV_OK;
 }
 

@@ -1,0 +1,74 @@
+"""Host dispatcher (CPU only): per-group cascade-vs-flat choice.
+
+The rule minimises a modelled step time: a group's benefit from cascade is the
+time the flat pass spends re-reading its prefix for every member minus its
+prefix contraction, and the cascade path's fixed cost is paid once per step.
+These tests pin the structure of that rule with explicit parameters (the
+MI355X-fitted default constants are data, checked only by timing)."""
+import numpy as np
+import pytest
+import torch
+
+from shared_prefix_paged_amd import _abi as A
+from shared_prefix_paged_amd import runtime as R
+
+
+def batch_of(group_of, group_len, hkv=8, hq=32, d=128, dtype="bf16"):
+    B = len(group_of)
+    q = torch.zeros((B, hq, d), dtype=torch.bfloat16 if dtype == "bf16" else torch.float32)
+    tables = np.full((B, 2), 0, np.int32)
+    lens = [1] * B
+    bases = list(np.cumsum([0] + list(group_len))[:-1])
+    return R.DecodeBatch(q, list(group_of), bases, list(group_len), tables, lens, 1, hkv)
+
+
+def params(fixed, flat_gbps=10000.0, prefix_gbps=4000.0, prefix_tflops=420.0, min_req=2):
+    p = R.default_params(A.SPKV_MODE_PER_GROUP)
+    p.fixed_cost_us, p.flat_gbps, p.prefix_gbps, p.prefix_tflops = fixed, flat_gbps, prefix_gbps, prefix_tflops
+    p.min_group_requests = min_req
+    return p
+
+
+def benefit_us(n, lp, hkv=8, hq=32, d=128, flat_gbps=10000.0, prefix_gbps=4000.0, prefix_tflops=420.0):
+    kvb = 2 * hkv * d * 2
+    t_flat = n * lp * kvb / (flat_gbps * 1e3)
+    t_c = max(lp * kvb / (prefix_gbps * 1e3), 4.0 * n * (hq // hkv) * lp * d * hkv / (prefix_tflops * 1e6))
+    return t_flat - t_c
+
+
+def test_one_group_needs_benefit_above_fixed_cost():
+    b = benefit_us(16, 2048)
+    bt = batch_of([0] * 16, [2048])
+    assert list(R.dispatch(bt, params(fixed=b - 1.0))) == [1]
+    assert list(R.dispatch(bt, params(fixed=b + 1.0))) == [0]
+
+
+def test_fixed_cost_is_shared_by_the_groups_that_take_cascade():
+    # each group alone is below the fixed cost, together above it
+    b = benefit_us(16, 2048)
+    bt = batch_of([0] * 16 + [1] * 16, [2048, 2048])
+    assert list(R.dispatch(bt, params(fixed=1.5 * b))) == [1, 1]
+    assert list(R.dispatch(bt, params(fixed=2.5 * b))) == [0, 0]
+
+
+def test_group_without_benefit_stays_flat_while_others_take_cascade():
+    # a single-request group re-reads its prefix once: no benefit (and below the minimum size)
+    bt = batch_of([0] * 16 + [1] + [2] * 2, [8192, 8192, 16])
+    got = list(R.dispatch(bt, params(fixed=5.0)))
+    assert got[0] == 1 and got[1] == 0
+    assert benefit_us(2, 16) < 0 and got[2] == 0
+
+
+def test_float32_and_forced_modes():
+    bt = batch_of([0] * 8, [4096], dtype="f32")
+    assert list(R.dispatch(bt, params(fixed=0.0))) == [0]          # the MFMA contraction is bf16 only
+    bt = batch_of([0] * 8, [4096])
+    assert list(R.dispatch(bt, R.default_params(A.SPKV_MODE_FORCE_DENSE))) == [0]
+    assert list(R.dispatch(bt, R.default_params(A.SPKV_MODE_FORCE_CASCADE))) == [1]
+
+
+@pytest.mark.parametrize("lp,expect", [(256, 0), (512, 0), (1024, 1), (16384, 1)])
+def test_default_constants_on_the_swept_shapes(lp, expect):
+    # the 8B-shaped layer (B = 64) at the swept prefix lengths: cascade from Lp = 1024
+    bt = batch_of([0] * 64, [lp])
+    assert list(R.dispatch(bt, R.default_params(A.SPKV_MODE_PER_GROUP))) == [expect]

@@ -55,6 +55,16 @@ def small_cases():
         "bf16_hkv16": lambda: W.make_custom(
             batch=3, num_q_heads=16, num_kv_heads=16, head_dim=64, dtype="bf16", group_prefix_len=[33],
             group_of=[0, 0, 0], suffix_len=[5, 6, 400], seed=18),
+        # the remaining query-rows-per-head counts of the bf16 paged pass (3, 6, 7)
+        "bf16_d128_g3": lambda: W.make_custom(
+            batch=6, num_q_heads=6, num_kv_heads=2, head_dim=128, dtype="bf16", group_prefix_len=[260],
+            group_of=[0, -1, 0, 0, -1, 0], suffix_len=[15, 81, 16, 1, 17, 129], seed=19),
+        "bf16_d128_g6": lambda: W.make_custom(
+            batch=5, num_q_heads=12, num_kv_heads=2, head_dim=128, dtype="bf16", group_prefix_len=[48],
+            group_of=[0, 0, -1, 0, 0], suffix_len=[63, 64, 65, 2, 200], seed=20),
+        "bf16_d64_g7": lambda: W.make_custom(
+            batch=4, num_q_heads=7, num_kv_heads=1, head_dim=64, dtype="bf16", group_prefix_len=[700],
+            group_of=[0, 0, 0, -1], suffix_len=[31, 1, 500, 47], seed=21),
     }
 
 
