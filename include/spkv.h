@@ -342,6 +342,8 @@ typedef struct spkv_plan_info {
     int32_t flat_granule;          /* reserved (0) */
     int32_t prefix_split_cap;      /* per group: chunk = roundup(max(prefix_chunk, ceil(Lp / cap)), granule) */
     int32_t prefix_granule;
+    int32_t prefix_key_halves;     /* 2: each prefix work item's key chunk is split over two wave sets whose
+                                      states merge in LDS (one partial per row per item either way) */
 } spkv_plan_info;
 
 spkv_status spkv_plan_query(const spkv_batch *batch, const int32_t *cascade, spkv_plan_info *out);

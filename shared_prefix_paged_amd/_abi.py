@@ -47,7 +47,8 @@ class spkv_plan_info(C.Structure):
     _fields_ = [("flat_chunk", c_i32), ("flat_splits", c_i32), ("prefix_chunk", c_i32), ("prefix_splits", c_i32),
                 ("prefix_waves", c_i32), ("prefix_mtiles", c_i32), ("flat_items", c_i64),
                 ("prefix_items", c_i64), ("workspace_bytes", c_i64), ("flat_split_cap", c_i32),
-                ("flat_granule", c_i32), ("prefix_split_cap", c_i32), ("prefix_granule", c_i32)]
+                ("flat_granule", c_i32), ("prefix_split_cap", c_i32), ("prefix_granule", c_i32),
+                ("prefix_key_halves", c_i32)]
 
 
 P_batch, P_kv, P_params = C.POINTER(spkv_batch), C.POINTER(spkv_kv), C.POINTER(spkv_dispatch_params)

@@ -85,7 +85,8 @@ struct Plan {
     int32_t flat_splits;      // partial slots per row reserved for the flat pass
     int32_t prefix_chunk;     // base tau for the prefix pass (multiple of kPrefixKeyTile)
     int32_t prefix_splits;    // grid x of the prefix kernel
-    int32_t prefix_waves;     // waves per prefix block (32 rows each)
+    int32_t prefix_waves;     // row waves per prefix block (32 rows each)
+    int32_t prefix_key_halves;  // 2: each block's key chunk is split over two wave sets
     int32_t prefix_mtiles;    // grid y of the prefix kernel
     int32_t splits_total;     // prefix_splits + flat_splits (partial stride per row)
     int64_t flat_items;

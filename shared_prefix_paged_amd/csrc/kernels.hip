@@ -839,8 +839,12 @@ __device__ __forceinline__ int vchunk_logical(int r, int p) {
 // SPLIT_P: P is rounded to bf16 for the P.V MFMA.  Its relative rounding error
 // (2^-8) averages out over long prefixes; for short ones (few keys per row)
 // P is carried as two bf16 terms, hi + lo, and P.V takes two MFMA passes.
-template <int D, int W, bool SPLIT_P>
-__global__ __launch_bounds__(64 * W) void prefix_mfma_kernel(Args a) {
+// KH = 2: the block's key chunk is cut in two halves, each taken by W waves
+// over the same W x 32 query rows with a ring of its own; the halves merge
+// their states through LDS ([GKV] Eq. (1)) before one partial is written, so
+// a row gets half as many partial states at the same number of waves per CU.
+template <int D, int W, bool SPLIT_P, int KH = 1>
+__global__ __launch_bounds__(64 * W * KH) void prefix_mfma_kernel(Args a) {
     constexpr int NT = spkv::kPrefixKeyTile;   // 32 keys per tile
     constexpr int STAGES = 4;
     constexpr int KS = D / 16;                 // MFMA k-steps for Q.K
@@ -852,7 +856,8 @@ __global__ __launch_bounds__(64 * W) void prefix_mfma_kernel(Args a) {
     constexpr int IPW = NT / RPI / W;          // DMAs per wave per tile per operand
     static_assert(IPW >= 1 && (NT / RPI) % W == 0, "tile must split evenly over the waves");
     constexpr int AHEAD = (STAGES - 2) * 2 * IPW;   // DMAs issued after a tile's own
-    __shared__ __attribute__((aligned(1024))) char smem[STAGES * 2 * TILEB];
+    static_assert(KH == 1 || KH == 2, "one or two key halves");
+    __shared__ __attribute__((aligned(1024))) char smem[KH * STAGES * 2 * TILEB];
 
     const int gz = blockIdx.z;
     const int g = gz / a.Hkv;
@@ -871,13 +876,21 @@ __global__ __launch_bounds__(64 * W) void prefix_mfma_kernel(Args a) {
     const int nsplit = spkv::splits_for(lp, chunk);
     const int s = blockIdx.x;
     if (s >= nsplit) return;
-    const int k0 = s * chunk;
-    const int k1 = min(lp, k0 + chunk);
-    const int ntiles = (k1 - k0 + NT - 1) / NT;
-
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave_id = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    const int wave = wave_id % W;            // row wave (32 query rows)
+    const int khalf = wave_id / W;           // key half
     const int lane = tid & 63;
+    // Tiles of the block's chunk: the first ceil(n/2) to half 0, the rest to
+    // half 1.  Every wave runs nt_loop steps (a half with fewer tiles only
+    // takes part in the barriers), so the barrier count is the same for all.
+    const int kc0 = s * chunk;
+    const int kc1 = min(lp, kc0 + chunk);
+    const int nt_all = (kc1 - kc0 + NT - 1) / NT;
+    const int nt_loop = KH == 1 ? nt_all : (nt_all + 1) / 2;
+    const int k0 = kc0 + (khalf ? nt_loop * NT : 0);
+    const int k1 = khalf ? kc1 : min(kc1, kc0 + nt_loop * NT);
+    const int ntiles = khalf ? nt_all - nt_loop : nt_loop;
     const int half = lane >> 5;
     const int col = lane & 31;
 
@@ -886,7 +899,8 @@ __global__ __launch_bounds__(64 * W) void prefix_mfma_kernel(Args a) {
     // kh / vh are wave-uniform (kernel arguments and block indices only), so
     // they live in SGPRs as the DMA's "s" operand requires.  (The readfirstlane
     // builtin is 32-bit and must not be applied to these 64-bit pointers.)
-    const uint32_t smem0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_offset(smem));
+    const uint32_t smem0 =
+        (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_offset(smem + khalf * STAGES * 2 * TILEB));
 
     // Per-lane source offsets and LDS placement of the DMAs, fixed for the
     // whole range (K row r of a tile holds key swap_bits23(r); the 16-byte
@@ -936,7 +950,7 @@ __global__ __launch_bounds__(64 * W) void prefix_mfma_kernel(Args a) {
     // also covers every DMA in flight, so the member index and Q (loads it
     // tracks) are read while only tile 0 is in flight, and tiles 1 .. STAGES-2
     // follow once Q has landed.
-    issue(0, 0);
+    if (ntiles > 0) issue(0, 0);
 
     // This lane's query row (column of S^T / O^T).
     const int row = mt * 32 * W + wave * 32 + col;
@@ -995,20 +1009,24 @@ __global__ __launch_bounds__(64 * W) void prefix_mfma_kernel(Args a) {
             vofs[db] = (uint32_t)(r1 * ROWB + (vchunk_phys<CPR>(r1, c) << 4) + inner);
         }
     }
-    const lds_char_t *lsm = (const lds_char_t *)smem;
+    const lds_char_t *lsm = (const lds_char_t *)(smem + khalf * STAGES * 2 * TILEB);
     constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;   // (1.0, 1.0) in bf16
 
     // Tile t sits in stage t % STAGES; the stage loop is unrolled so that all
     // LDS addresses are a per-lane offset plus an immediate.
-    for (int t0 = 0; t0 < ntiles; t0 += STAGES) {
+    for (int t0 = 0; t0 < nt_loop; t0 += STAGES) {
 #pragma unroll
         for (int st = 0; st < STAGES; ++st) {
             const int t = t0 + st;
-            if (t >= ntiles) break;
-            if (t + STAGES - 2 < ntiles) wait_vmcnt<AHEAD>();
-            else wait_vmcnt<0>();
+            if (t >= nt_loop) break;
+            const bool act = t < ntiles;   // this half still has tile t
+            if (act) {
+                if (t + STAGES - 2 < ntiles) wait_vmcnt<AHEAD>();
+                else wait_vmcnt<0>();
+            }
             __builtin_amdgcn_s_barrier();      // tile t visible; every wave is done with tile t-1
             asm volatile("" ::: "memory");
+            if (!act) continue;
             if (t + STAGES - 1 < ntiles) issue(t + STAGES - 1, (st + STAGES - 1) % STAGES);
 
             const lds_char_t *ks = lsm + st * 2 * TILEB;
@@ -1088,6 +1106,35 @@ __global__ __launch_bounds__(64 * W) void prefix_mfma_kernel(Args a) {
         }
     }
 
+    if constexpr (KH == 2) {
+        // Half 1 hands its state (per lane: O^T registers, reference max and
+        // normaliser) to the matching lane of half 0 through the ring's LDS.
+        __builtin_amdgcn_s_barrier();          // every wave is done with both rings
+        asm volatile("" ::: "memory");
+        constexpr int NV = NDB * 16 + 2;
+        float *xch = (float *)smem + (size_t)wave * NV * 64 + lane;
+        if (khalf == 1) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) xch[(db * 16 + j) * 64] = oacc[db][j];
+            xch[(NV - 2) * 64] = m_run;
+            xch[(NV - 1) * 64] = l_run;
+        }
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (khalf == 1) return;
+        const float m1 = xch[(NV - 2) * 64], l1 = xch[(NV - 1) * 64];
+        const float mt = fmaxf(m_run, m1);
+        const float mu = mt == -INFINITY ? 0.f : mt;
+        const float a0 = __builtin_amdgcn_exp2f(m_run - mu), a1 = __builtin_amdgcn_exp2f(m1 - mu);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) oacc[db][j] = oacc[db][j] * a0 + xch[(db * 16 + j) * 64] * a1;
+        l_run = l_run * a0 + l1 * a1;
+        m_run = mt;
+    }
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
     if (!row_ok) return;
     const int64_t prow = ((int64_t)qb * a.Hq + qj) * a.splits_total + s;
@@ -1427,10 +1474,14 @@ spkv_status launch_flat(const Args &a, bool bf16, int d, int part, const FlatLau
 
 spkv_status launch_prefix(const Args &a, const Plan &p, int d, hipStream_t st) {
     if (p.prefix_splits <= 0 || p.prefix_mtiles <= 0) return SPKV_OK;
-    dim3 grid(p.prefix_splits, p.prefix_mtiles, a.ng * a.Hkv), block(64 * p.prefix_waves);
+    dim3 grid(p.prefix_splits, p.prefix_mtiles, a.ng * a.Hkv), block(64 * p.prefix_waves * p.prefix_key_halves);
     TimedLaunch tl(SPKV_KERNEL_PREFIX, st);
-    const int key = p.prefix_waves * 1000 + d + (p.prefix_split_p ? 10000 : 0);
+    const int key = p.prefix_waves * 1000 + d + (p.prefix_split_p ? 10000 : 0) + (p.prefix_key_halves == 2 ? 100000 : 0);
     switch (key) {
+    case 104128: prefix_mfma_kernel<128, 4, false, 2><<<grid, block, 0, st>>>(a); break;
+    case 104064: prefix_mfma_kernel<64, 4, false, 2><<<grid, block, 0, st>>>(a); break;
+    case 114128: prefix_mfma_kernel<128, 4, true, 2><<<grid, block, 0, st>>>(a); break;
+    case 114064: prefix_mfma_kernel<64, 4, true, 2><<<grid, block, 0, st>>>(a); break;
     case 1128: prefix_mfma_kernel<128, 1, false><<<grid, block, 0, st>>>(a); break;
     case 2128: prefix_mfma_kernel<128, 2, false><<<grid, block, 0, st>>>(a); break;
     case 4128: prefix_mfma_kernel<128, 4, false><<<grid, block, 0, st>>>(a); break;

@@ -128,6 +128,7 @@ static std::vector<FlatLaunch> plan_flat(const std::vector<int64_t> &L, int head
 
 spkv_status make_plan(const spkv_batch *b, const int32_t *cascade, int32_t num_cus, Plan *p) {
     *p = Plan{};
+    p->prefix_key_halves = 1;
     const int B = b->batch, ng = b->num_groups, Hkv = b->num_kv_heads, D = b->head_dim;
     const int G = b->num_q_heads / Hkv;
     p->num_groups = ng;
@@ -170,6 +171,10 @@ spkv_status make_plan(const spkv_batch *b, const int32_t *cascade, int32_t num_c
     if (p->run_prefix && bf16) {
         int w = (int)std::min<int64_t>(4, (max_m + 31) / 32);
         p->prefix_waves = w <= 1 ? 1 : (w == 2 ? 2 : 4);   // tile variants: 1, 2 or 4 waves of 32 rows
+        // Tiles of 4 row waves take the two-key-half variant: one 8-wave block
+        // (two 64 KB rings) per CU instead of two 4-wave blocks, and half as
+        // many partial states per row.
+        p->prefix_key_halves = p->prefix_waves == 4 ? 2 : 1;
         const int64_t mt = 32 * p->prefix_waves;
         p->prefix_mtiles = (int32_t)((max_m + mt - 1) / mt);
         for (int g = 0; g < ng; ++g) {
@@ -178,12 +183,12 @@ spkv_status make_plan(const spkv_batch *b, const int32_t *cascade, int32_t num_c
             if (n == 0 || lp == 0 || !mask_get(p->cascade, g)) continue;
             prefix_work += Hkv * ((n * G + mt - 1) / mt) * lp;
         }
-        // Two blocks per CU are resident (the LDS ring of a block is 64 KB):
-        // size the key chunk so that all blocks fit in one round.  Rounding
-        // each group's last chunk up can add a block per row tile, so grow
-        // the chunk until the exact block count fits (or every group is one
-        // chunk).
-        const int64_t target = std::max<int64_t>(1, (int64_t)num_cus * 2);
+        // 128 KB of LDS rings per CU: two blocks of one key half or one block
+        // of two.  Size the key chunk so that all blocks fit in one round.
+        // Rounding each group's last chunk up can add a block per row tile,
+        // so grow the chunk until the exact block count fits (or every group
+        // is one chunk).
+        const int64_t target = std::max<int64_t>(1, (int64_t)num_cus * 2 / p->prefix_key_halves);
         int64_t pt = (prefix_work + target - 1) / target;
         pt = std::max<int64_t>(pt, 256);
         pt = (pt + kPrefixKeyTile - 1) / kPrefixKeyTile * kPrefixKeyTile;
@@ -289,6 +294,7 @@ spkv_status spkv_plan_query(const spkv_batch *batch, const int32_t *cascade, spk
     out->flat_granule = 0;
     out->prefix_split_cap = kPrefixSplitCap;
     out->prefix_granule = kPrefixKeyTile;
+    out->prefix_key_halves = p.prefix_key_halves;
     return SPKV_OK;
 }
 

@@ -65,6 +65,15 @@ def small_cases():
         "bf16_d64_g7": lambda: W.make_custom(
             batch=4, num_q_heads=7, num_kv_heads=1, head_dim=64, dtype="bf16", group_prefix_len=[700],
             group_of=[0, 0, 0, -1], suffix_len=[31, 1, 500, 47], seed=21),
+        # groups of more than 64 query rows take the two-key-half prefix tiles:
+        # a last chunk of one 32-key tile (second half idle), an odd tile count,
+        # and a prefix shorter than one tile
+        "bf16_d128_halves_ragged": lambda: W.make_custom(
+            batch=24, num_q_heads=16, num_kv_heads=4, head_dim=128, dtype="bf16", group_prefix_len=[276, 326, 21],
+            group_of=[0] * 18 + [1, 1, 2, 2, -1, 1], suffix_len=list(range(1, 25)), seed=22),
+        "bf16_d64_halves_ragged": lambda: W.make_custom(
+            batch=11, num_q_heads=8, num_kv_heads=1, head_dim=64, dtype="bf16", group_prefix_len=[545, 7],
+            group_of=[0] * 9 + [1, 1], suffix_len=[3, 70, 1, 5, 9, 130, 2, 33, 64, 17, 8], seed=23),
     }
 
 

@@ -71,8 +71,19 @@ def test_prefix_tile_is_a_built_variant(members):
     # 4 query heads per KV head: members * 4 rows per group; tiles of 1, 2 or 4 waves exist
     bt = batch_of([50] * members, [0] * members, [2048], hkv=8, hq=32)
     info = bt.plan(None)
-    assert info.prefix_waves in (1, 2, 4)
+    assert info.prefix_waves in (1, 2, 4) and info.prefix_key_halves == (2 if info.prefix_waves == 4 else 1)
     assert info.prefix_waves * 32 * info.prefix_mtiles >= members * 4
+
+
+def test_ragged_parity_cases_take_two_key_halves():
+    # the GPU parity cases built for the two-key-half prefix tiles do reach them
+    for lens, groups, glen, hq, hkv, d in [
+            (list(range(1, 25)), [0] * 18 + [1, 1, 2, 2, -1, 1], [276, 326, 21], 16, 4, 128),
+            ([3, 70, 1, 5, 9, 130, 2, 33, 64, 17, 8], [0] * 9 + [1, 1], [545, 7], 8, 1, 64)]:
+        info = batch_of(lens, groups, glen, hkv=hkv, hq=hq, d=d).plan(None)
+        assert info.prefix_waves == 4 and info.prefix_key_halves == 2
+        # the base chunk leaves a ragged last chunk in the longest prefix
+        assert max(glen) % info.prefix_chunk != 0
 
 
 @pytest.mark.parametrize("shape", [
@@ -85,13 +96,15 @@ def test_prefix_tile_is_a_built_variant(members):
     (128, 8, [2048, 16384, 9000, 4100, 12000, 7000, 15000, 3000], 32, 8),   # eight prefix groups
 ])
 def test_prefix_blocks_fit_one_resident_round(shape):
-    # Two prefix blocks are resident per CU (256 CUs): a grid of more than 512
-    # live blocks runs a second, mostly idle round.
+    # 128 KB of LDS rings per CU (256 CUs) hold two blocks of one key half or
+    # one block of two: a grid past that many live blocks runs a second,
+    # mostly idle round.
     n, ng, lps, hq, hkv = shape
     groups = [min(i // (n // ng), ng - 1) for i in range(n)]
     bt = batch_of([300] * n, groups, lps, hkv=hkv, hq=hq)
     info = bt.plan(None)
-    assert 0 < info.prefix_items <= 2 * 256
+    resident = 2 * 256 // info.prefix_key_halves
+    assert 0 < info.prefix_items <= resident
     # and the chunk does not grow past what one round needs
     units = sum(hkv * -(-(groups.count(g) * (hq // hkv)) // (32 * info.prefix_waves)) for g in range(ng))
-    assert info.prefix_items >= min(2 * 256, units) // 2
+    assert info.prefix_items >= min(resident, units) // 2
