@@ -12,6 +12,7 @@
 // so exp2 maps to the hardware's v_exp_f32; partial LSE values stored in the
 // workspace are base 2, and only outputs are converted to natural log.
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <cmath>
 #include <cstring>
@@ -1406,24 +1407,40 @@ hipEvent_t take_event(Timing &t) {
     return e;
 }
 
+// With timing on, a launch goes through hipExtLaunchKernelGGL with a start and
+// a stop event: the events take the dispatch's own begin and end timestamps,
+// so no marker packet sits between two kernels of the stream and the duration
+// is the kernel's alone.  Otherwise it is a plain launch.
 struct TimedLaunch {
     int kernel;
     hipStream_t st;
     hipEvent_t a = nullptr, b = nullptr;
+    bool used = false;
     TimedLaunch(int k, hipStream_t s) : kernel(k), st(s) {
         Timing &t = timing();
         std::lock_guard<std::mutex> g(t.mu);
         if (!t.on) return;
         a = take_event(t);
         b = take_event(t);
-        if (a) (void)hipEventRecord(a, st);
+    }
+    template <typename... P, typename... V>
+    void launch(void (*kern)(P...), dim3 grid, dim3 block, size_t lds, V... args) {
+        if (a && b) {
+            hipExtLaunchKernelGGL(kern, grid, block, (std::uint32_t)lds, st, a, b, 0u, args...);
+            used = true;
+        } else {
+            kern<<<grid, block, lds, st>>>(args...);
+        }
     }
     ~TimedLaunch() {
-        if (!a || !b) return;
-        (void)hipEventRecord(b, st);
         Timing &t = timing();
         std::lock_guard<std::mutex> g(t.mu);
-        t.pending.push_back({kernel, a, b});
+        if (a && b && used) {
+            t.pending.push_back({kernel, a, b});
+            return;
+        }
+        if (a) t.pool.push_back(a);
+        if (b) t.pool.push_back(b);
     }
 };
 
@@ -1436,11 +1453,11 @@ spkv_status check_launch(const char *what) {
 // Dynamic LDS above 64 KB is granted per kernel once its limit is raised.
 template <bool BF16, int D, int G>
 spkv_status launch_flat_g(const Args &a, int part, const FlatLaunch &f, dim3 grid, dim3 block, size_t lds,
-                          hipStream_t st) {
+                          TimedLaunch &tl) {
     static const hipError_t attr = hipFuncSetAttribute((const void *)flat_kernel<BF16, D, G>,
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, spkv::kLdsPerCU);
     if (attr != hipSuccess) return fail(SPKV_E_HIP, std::string("flat_kernel LDS limit: ") + hipGetErrorString(attr));
-    flat_kernel<BF16, D, G><<<grid, block, lds, st>>>(a, part, f);
+    tl.launch(flat_kernel<BF16, D, G>, grid, block, lds, a, part, f);
     return check_launch("flat_kernel");
 }
 
@@ -1451,14 +1468,14 @@ spkv_status launch_flat_d(const Args &a, int part, const FlatLaunch &f, int head
     const size_t lds = (size_t)waves * (BF16 ? FlatMfmaGeom<D>::WAVEB : FlatGeom<BF16, D>::WAVEB);
     TimedLaunch tl(SPKV_KERNEL_FLAT, st);
     switch (a.G) {
-    case 1: return launch_flat_g<BF16, D, 1>(a, part, f, grid, block, lds, st);
-    case 2: return launch_flat_g<BF16, D, 2>(a, part, f, grid, block, lds, st);
-    case 3: return launch_flat_g<BF16, D, 3>(a, part, f, grid, block, lds, st);
-    case 4: return launch_flat_g<BF16, D, 4>(a, part, f, grid, block, lds, st);
-    case 5: return launch_flat_g<BF16, D, 5>(a, part, f, grid, block, lds, st);
-    case 6: return launch_flat_g<BF16, D, 6>(a, part, f, grid, block, lds, st);
-    case 7: return launch_flat_g<BF16, D, 7>(a, part, f, grid, block, lds, st);
-    case 8: return launch_flat_g<BF16, D, 8>(a, part, f, grid, block, lds, st);
+    case 1: return launch_flat_g<BF16, D, 1>(a, part, f, grid, block, lds, tl);
+    case 2: return launch_flat_g<BF16, D, 2>(a, part, f, grid, block, lds, tl);
+    case 3: return launch_flat_g<BF16, D, 3>(a, part, f, grid, block, lds, tl);
+    case 4: return launch_flat_g<BF16, D, 4>(a, part, f, grid, block, lds, tl);
+    case 5: return launch_flat_g<BF16, D, 5>(a, part, f, grid, block, lds, tl);
+    case 6: return launch_flat_g<BF16, D, 6>(a, part, f, grid, block, lds, tl);
+    case 7: return launch_flat_g<BF16, D, 7>(a, part, f, grid, block, lds, tl);
+    case 8: return launch_flat_g<BF16, D, 8>(a, part, f, grid, block, lds, tl);
     default: return fail(SPKV_E_INVAL, "unsupported GQA group size");
     }
 }
@@ -1478,22 +1495,22 @@ spkv_status launch_prefix(const Args &a, const Plan &p, int d, hipStream_t st) {
     TimedLaunch tl(SPKV_KERNEL_PREFIX, st);
     const int key = p.prefix_waves * 1000 + d + (p.prefix_split_p ? 10000 : 0) + (p.prefix_key_halves == 2 ? 100000 : 0);
     switch (key) {
-    case 104128: prefix_mfma_kernel<128, 4, false, 2><<<grid, block, 0, st>>>(a); break;
-    case 104064: prefix_mfma_kernel<64, 4, false, 2><<<grid, block, 0, st>>>(a); break;
-    case 114128: prefix_mfma_kernel<128, 4, true, 2><<<grid, block, 0, st>>>(a); break;
-    case 114064: prefix_mfma_kernel<64, 4, true, 2><<<grid, block, 0, st>>>(a); break;
-    case 1128: prefix_mfma_kernel<128, 1, false><<<grid, block, 0, st>>>(a); break;
-    case 2128: prefix_mfma_kernel<128, 2, false><<<grid, block, 0, st>>>(a); break;
-    case 4128: prefix_mfma_kernel<128, 4, false><<<grid, block, 0, st>>>(a); break;
-    case 1064: prefix_mfma_kernel<64, 1, false><<<grid, block, 0, st>>>(a); break;
-    case 2064: prefix_mfma_kernel<64, 2, false><<<grid, block, 0, st>>>(a); break;
-    case 4064: prefix_mfma_kernel<64, 4, false><<<grid, block, 0, st>>>(a); break;
-    case 11128: prefix_mfma_kernel<128, 1, true><<<grid, block, 0, st>>>(a); break;
-    case 12128: prefix_mfma_kernel<128, 2, true><<<grid, block, 0, st>>>(a); break;
-    case 14128: prefix_mfma_kernel<128, 4, true><<<grid, block, 0, st>>>(a); break;
-    case 11064: prefix_mfma_kernel<64, 1, true><<<grid, block, 0, st>>>(a); break;
-    case 12064: prefix_mfma_kernel<64, 2, true><<<grid, block, 0, st>>>(a); break;
-    case 14064: prefix_mfma_kernel<64, 4, true><<<grid, block, 0, st>>>(a); break;
+    case 104128: tl.launch(prefix_mfma_kernel<128, 4, false, 2>, grid, block, 0, a); break;
+    case 104064: tl.launch(prefix_mfma_kernel<64, 4, false, 2>, grid, block, 0, a); break;
+    case 114128: tl.launch(prefix_mfma_kernel<128, 4, true, 2>, grid, block, 0, a); break;
+    case 114064: tl.launch(prefix_mfma_kernel<64, 4, true, 2>, grid, block, 0, a); break;
+    case 1128: tl.launch(prefix_mfma_kernel<128, 1, false>, grid, block, 0, a); break;
+    case 2128: tl.launch(prefix_mfma_kernel<128, 2, false>, grid, block, 0, a); break;
+    case 4128: tl.launch(prefix_mfma_kernel<128, 4, false>, grid, block, 0, a); break;
+    case 1064: tl.launch(prefix_mfma_kernel<64, 1, false>, grid, block, 0, a); break;
+    case 2064: tl.launch(prefix_mfma_kernel<64, 2, false>, grid, block, 0, a); break;
+    case 4064: tl.launch(prefix_mfma_kernel<64, 4, false>, grid, block, 0, a); break;
+    case 11128: tl.launch(prefix_mfma_kernel<128, 1, true>, grid, block, 0, a); break;
+    case 12128: tl.launch(prefix_mfma_kernel<128, 2, true>, grid, block, 0, a); break;
+    case 14128: tl.launch(prefix_mfma_kernel<128, 4, true>, grid, block, 0, a); break;
+    case 11064: tl.launch(prefix_mfma_kernel<64, 1, true>, grid, block, 0, a); break;
+    case 12064: tl.launch(prefix_mfma_kernel<64, 2, true>, grid, block, 0, a); break;
+    case 14064: tl.launch(prefix_mfma_kernel<64, 4, true>, grid, block, 0, a); break;
     default: return fail(SPKV_E_INVAL, "unsupported prefix tile");
     }
     return check_launch("prefix_mfma_kernel");
@@ -1505,8 +1522,8 @@ spkv_status launch_merge(const Args &a, int d, float *out, float *lse, const Fla
     if (rows == 0) return SPKV_OK;
     dim3 grid((unsigned)((rows + 3) / 4)), block(256);
     TimedLaunch tl(SPKV_KERNEL_MERGE, st);
-    if (d == 128) merge_kernel<128><<<grid, block, 0, st>>>(a, out, lse, fr, fp);
-    else merge_kernel<64><<<grid, block, 0, st>>>(a, out, lse, fr, fp);
+    if (d == 128) tl.launch(merge_kernel<128>, grid, block, 0, a, out, lse, fr, fp);
+    else tl.launch(merge_kernel<64>, grid, block, 0, a, out, lse, fr, fp);
     return check_launch("merge_kernel");
 }
 
@@ -1611,8 +1628,8 @@ spkv_status spkv_hot_write(const void *k_src, const void *v_src, int64_t base, i
     const int ppr = d * esz / 16;
     const int64_t total = lp * hkv * ppr;
     TimedLaunch tl(SPKV_KERNEL_CACHE, (hipStream_t)stream);
-    hot_write_kernel<<<(unsigned)((total + 255) / 256), 256, 0, (hipStream_t)stream>>>(
-        (const u32x4_t *)k_src, (const u32x4_t *)v_src, (u32x4_t *)k_hot, (u32x4_t *)v_hot, base, lp, hkv, ppr);
+    tl.launch(hot_write_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, (const u32x4_t *)k_src,
+              (const u32x4_t *)v_src, (u32x4_t *)k_hot, (u32x4_t *)v_hot, base, lp, hkv, ppr);
     return check_launch("hot_write_kernel");
 }
 
@@ -1628,9 +1645,8 @@ spkv_status spkv_reshape_and_cache(const void *k_new, const void *v_new, const i
     const int pps = hkv * d * esz / 16;
     const int64_t total = (int64_t)n * pps;
     TimedLaunch tl(SPKV_KERNEL_CACHE, (hipStream_t)stream);
-    reshape_and_cache_kernel<<<(unsigned)((total + 255) / 256), 256, 0, (hipStream_t)stream>>>(
-        (const u32x4_t *)k_new, (const u32x4_t *)v_new, slot_mapping, n, (u32x4_t *)k_cold, (u32x4_t *)v_cold,
-        cold_slots, pps);
+    tl.launch(reshape_and_cache_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, (const u32x4_t *)k_new,
+              (const u32x4_t *)v_new, slot_mapping, n, (u32x4_t *)k_cold, (u32x4_t *)v_cold, cold_slots, pps);
     return check_launch("reshape_and_cache_kernel");
 }
 
@@ -1657,9 +1673,9 @@ spkv_status spkv_append_tokens(const void *k_new, const void *v_new, const int32
         }
         TimedLaunch tl(SPKV_KERNEL_CACHE, (hipStream_t)stream);
         const int64_t off = (int64_t)i0 * pps;
-        append_tokens_kernel<<<(unsigned)aa.n, 128, 0, (hipStream_t)stream>>>(
-            (const u32x4_t *)k_new + off, (const u32x4_t *)v_new + off, aa, (u32x4_t *)k_cold, (u32x4_t *)v_cold,
-            cold_slots, pps, tables, max_blocks, lens, num_rows, page_size);
+        tl.launch(append_tokens_kernel, dim3((unsigned)aa.n), dim3(128), 0, (const u32x4_t *)k_new + off,
+                  (const u32x4_t *)v_new + off, aa, (u32x4_t *)k_cold, (u32x4_t *)v_cold, cold_slots, pps, tables,
+                  max_blocks, lens, num_rows, page_size);
         st = check_launch("append_tokens_kernel");
         if (st != SPKV_OK) return st;
     }
@@ -1678,8 +1694,8 @@ spkv_status spkv_copy_blocks(const int32_t *pairs, int32_t n, void *k_cold, void
     const int64_t ppp = (int64_t)page_size * hkv * d * esz / 16;
     const unsigned gx = (unsigned)std::min<int64_t>(64, (ppp + 255) / 256);
     TimedLaunch tl(SPKV_KERNEL_CACHE, (hipStream_t)stream);
-    copy_blocks_kernel<<<dim3(gx, (unsigned)n), 256, 0, (hipStream_t)stream>>>(pairs, (u32x4_t *)k_cold,
-                                                                                (u32x4_t *)v_cold, num_pages, ppp);
+    tl.launch(copy_blocks_kernel, dim3(gx, (unsigned)n), dim3(256), 0, pairs, (u32x4_t *)k_cold, (u32x4_t *)v_cold,
+              num_pages, ppp);
     return check_launch("copy_blocks_kernel");
 }
 
@@ -1690,8 +1706,8 @@ spkv_status spkv_block_table_append(int32_t *tables, int32_t max_blocks, int32_t
     if (n == 0) return SPKV_OK;
     if (!tables || !lens || !rows || !slots) return fail(SPKV_E_INVAL, "block_table_append: null pointer");
     TimedLaunch tl(SPKV_KERNEL_CACHE, (hipStream_t)stream);
-    block_table_append_kernel<<<(unsigned)((n + 255) / 256), 256, 0, (hipStream_t)stream>>>(
-        tables, max_blocks, lens, num_rows, rows, slots, n, page_size);
+    tl.launch(block_table_append_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, tables, max_blocks, lens,
+              num_rows, rows, slots, n, page_size);
     return check_launch("block_table_append_kernel");
 }
 
@@ -1728,8 +1744,8 @@ spkv_status spkv_merge_states(const float *o_a, const float *lse_a, const float 
     if (head_dim > 256 || 256 % head_dim) return fail(SPKV_E_INVAL, "merge_states: head_dim must divide 256");
     const int64_t total = rows * head_dim;
     TimedLaunch tl(SPKV_KERNEL_MERGE, (hipStream_t)stream);
-    merge2_kernel<<<(unsigned)((total + 255) / 256), 256, 0, (hipStream_t)stream>>>(o_a, lse_a, o_b, lse_b, o, lse,
-                                                                                    rows, head_dim);
+    tl.launch(merge2_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, o_a, lse_a, o_b, lse_b, o, lse, rows,
+              head_dim);
     return check_launch("merge2_kernel");
 }
 
