@@ -52,6 +52,9 @@ def parse():
                     help="measured HBM traffic per launch (written by shared_prefix_paged_amd/profile_step.py)")
     ap.add_argument("--sweep-lp", default=None, metavar="L1,L2,...",
                     help="time cascade and dense attention at each prefix length (C3 crossover sweep) and exit")
+    ap.add_argument("--sweep-batch", default=None, metavar="B1,B2,...",
+                    help="time cascade and dense attention at each number of requests sharing the prefix "
+                         "(at the configuration's or --lp's prefix length) and exit")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-MiB device buffer 5 times (counter calibration) and exit")
     return ap.parse_args()
@@ -72,8 +75,10 @@ def copy_probe(mib: int) -> int:
 
 def sweep_lp(args) -> int:
     """Attention time of both backends (forced) and the dispatcher's choice at
-    each prefix length; one JSON line.  Same workload recipe at every length
-    (the configuration's batch, heads and suffix lengths)."""
+    each prefix length (--sweep-lp) or at each number of requests sharing the
+    prefixes (--sweep-batch, at the configuration's or --lp's prefix length);
+    one JSON line.  Same workload recipe at every point (the configuration's
+    heads and suffix-length distribution)."""
     import numpy as np
     import torch
     import workloads as W
@@ -85,15 +90,22 @@ def sweep_lp(args) -> int:
     dev = torch.device("cuda:0")
     cfg0 = W.CONFIGS[args.config]
     rows = []
-    for lp in [int(x) for x in args.sweep_lp.split(",")]:
-        wl = W.make_workload(cfg0, prefix_len=lp, extra_steps=4)
+    if args.sweep_batch:
+        points = [(args.lp, int(x)) for x in args.sweep_batch.split(",")]
+    else:
+        points = [(int(x), None) for x in args.sweep_lp.split(",")]
+    for lp, nb in points:
+        wl = W.make_workload(cfg0, prefix_len=lp, batch=nb, extra_steps=4)
         cfg = wl.cfg
         st = setup_single_step(wl, device=dev)
         B = wl.batch
         out = torch.empty((B, cfg.num_q_heads, cfg.head_dim), dtype=torch.float32, device=dev)
         lse = torch.empty((B, cfg.num_q_heads), dtype=torch.float32, device=dev)
         ws = torch.empty(st.batch.workspace_size(), dtype=torch.uint8, device=dev)
-        rec = {"lp": lp, "kv_tokens": int(sum(wl.prefix_len_of(b) + int(wl.suffix_len[b]) for b in range(B)))}
+        G = cfg.num_q_heads // cfg.num_kv_heads
+        rec = {"lp": int(max(wl.group_prefix_len)) if len(wl.group_prefix_len) else 0, "batch": B,
+               "m_eff": int(max(np.bincount(wl.group_of[wl.group_of >= 0])) * G) if (wl.group_of >= 0).any() else 0,
+               "kv_tokens": int(sum(wl.prefix_len_of(b) + int(wl.suffix_len[b]) for b in range(B)))}
         for name, mode in (("cascade", A.SPKV_MODE_FORCE_CASCADE), ("dense", A.SPKV_MODE_FORCE_DENSE),
                            ("dispatch", A.SPKV_MODE_PER_GROUP)):
             params = R.default_params(mode)
@@ -115,11 +127,12 @@ def sweep_lp(args) -> int:
         rows.append(rec)
         del st, ws, out, lse
         torch.cuda.empty_cache()
-    cross = [r["lp"] for r in rows if r["best"] == "cascade"]
-    print(json.dumps({"metric": "attention time per step, cascade vs dense, by prefix length",
-                      "unit": "us", "config": {"workload": f"{args.config} recipe, Lp swept", "batch": B,
+    key = "batch" if args.sweep_batch else "lp"
+    cross = [r[key] for r in rows if r["best"] == "cascade"]
+    print(json.dumps({"metric": f"attention time per step, cascade vs dense, by {'batch' if key == 'batch' else 'prefix length'}",
+                      "unit": "us", "config": {"workload": f"{args.config} recipe, {key} swept",
                                                "steps_per_point": max(1, args.steps)},
-                      "rows": rows, "cascade_wins_from_lp": min(cross) if cross else None,
+                      "rows": rows, f"cascade_wins_from_{key}": min(cross) if cross else None,
                       "dispatch_agrees": all(r["dispatch_choice"] == r["best"] for r in rows)}), flush=True)
     return 0
 
@@ -157,7 +170,7 @@ def main():
     args = parse()
     if args.copy_probe:
         return copy_probe(args.copy_probe)
-    if args.sweep_lp:
+    if args.sweep_lp or args.sweep_batch:
         return sweep_lp(args)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "

@@ -310,6 +310,8 @@ typedef struct spkv_dispatch_params {
     double  flat_gbps;             /* effective bandwidth of the flat pass over the prefix */
     double  prefix_gbps;           /* effective bandwidth of the prefix contraction */
     double  prefix_tflops;         /* effective bf16 MFMA rate of the prefix contraction */
+    double  row_cost_ns;           /* cascade cost per query row of a group that takes it
+                                      (its prefix partial states: written, then merged) */
 } spkv_dispatch_params;
 
 /* Defaults fitted on MI355X (see the design notes for the fit). */

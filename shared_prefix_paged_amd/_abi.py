@@ -40,7 +40,7 @@ class spkv_kv(C.Structure):
 
 class spkv_dispatch_params(C.Structure):
     _fields_ = [("mode", c_i32), ("min_group_requests", c_i32), ("fixed_cost_us", c_f64),
-                ("flat_gbps", c_f64), ("prefix_gbps", c_f64), ("prefix_tflops", c_f64)]
+                ("flat_gbps", c_f64), ("prefix_gbps", c_f64), ("prefix_tflops", c_f64), ("row_cost_ns", c_f64)]
 
 
 class spkv_plan_info(C.Structure):

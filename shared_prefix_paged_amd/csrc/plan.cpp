@@ -333,19 +333,22 @@ spkv_status spkv_plan_parts(const spkv_batch *batch, const int32_t *cascade, int
 
 void spkv_dispatch_params_default(spkv_dispatch_params *p) {
     if (!p) return;
-    // Fitted on MI355X from the prefix-length sweeps of the 8B-shaped (B = 64,
-    // M = 256) and 32B-shaped (B = 256, M = 1280) workloads with the MFMA
-    // paged pass: the flat pass re-reads a shared prefix at ~10 TB/s (the
-    // re-reads are mostly cache hits), the prefix contraction runs at
-    // ~420 TFLOP/s, and taking the cascade path at all costs ~18 us per step
-    // (the prefix launch and its partial states); crossover between Lp = 512
-    // and 1024 at both shapes.
+    // Fitted on MI355X to the cascade-vs-flat sweeps of the 8B-shaped (Hq 32,
+    // Hkv 8) and 32B-shaped (Hq 10, Hkv 2) layers: prefix length 64 .. 32768
+    // at 64 and 256 requests, and 1 .. 256 requests sharing a 4096- or
+    // 16384-token prefix.  The flat pass re-reads a shared prefix at ~10 TB/s
+    // (the re-reads are mostly cache hits); the cascade path costs ~7.4 us per
+    // step (the prefix launch) plus ~3.9 ns per query row of the groups that
+    // take it (their partial states, written and merged).  The prefix
+    // contraction's own rates matter little near the crossover; they are
+    // those of the kernel at the 8B shape.
     p->mode = SPKV_MODE_PER_GROUP;
     p->min_group_requests = 2;
-    p->fixed_cost_us = 18.0;
+    p->fixed_cost_us = 7.4;
     p->flat_gbps = 10000.0;
     p->prefix_gbps = 4000.0;
     p->prefix_tflops = 420.0;
+    p->row_cost_ns = 3.9;
 }
 
 spkv_status spkv_dispatch(const spkv_batch *b, const spkv_dispatch_params *prm, int32_t *cascade_out) {
@@ -375,11 +378,13 @@ spkv_status spkv_dispatch(const spkv_batch *b, const spkv_dispatch_params *prm, 
     }
     if (prm->flat_gbps <= 0 || prm->prefix_gbps <= 0 || prm->prefix_tflops <= 0)
         return fail(SPKV_E_INVAL, "dispatch: rates must be positive");
+    if (prm->row_cost_ns < 0) return fail(SPKV_E_INVAL, "dispatch: negative row cost");
     // A group's benefit from cascade is the time the flat pass spends re-reading
-    // its prefix for every member, minus its prefix contraction.  The fixed
-    // cost is paid once per step by whichever groups take cascade, so the set
-    // of groups with a positive benefit goes cascade exactly when their total
-    // benefit exceeds it (this minimises the modelled step time).
+    // its prefix for every member, minus its prefix contraction and the cost of
+    // its query rows' extra partial states.  The fixed cost is paid once per
+    // step by whichever groups take cascade, so the set of groups with a
+    // positive benefit goes cascade exactly when their total benefit exceeds it
+    // (this minimises the modelled step time).
     double total = 0.0;
     for (int g = 0; g < ng; ++g) {
         cascade_out[g] = 0;
@@ -391,7 +396,8 @@ spkv_status spkv_dispatch(const spkv_batch *b, const spkv_dispatch_params *prm, 
         const double t_flat = n * lp * kvb / (prm->flat_gbps * 1e3);                    // us
         const double t_bytes = lp * kvb / (prm->prefix_gbps * 1e3);
         const double t_flops = 4.0 * m_eff * lp * b->head_dim * b->num_kv_heads / (prm->prefix_tflops * 1e6);
-        const double benefit = t_flat - std::max(t_bytes, t_flops);
+        const double t_rows = prm->row_cost_ns * (double)n * b->num_q_heads * 1e-3;
+        const double benefit = t_flat - std::max(t_bytes, t_flops) - t_rows;
         if (benefit > 0.0) {
             cascade_out[g] = 1;
             total += benefit;

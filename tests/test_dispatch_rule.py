@@ -11,6 +11,7 @@ import torch
 
 from shared_prefix_paged_amd import _abi as A
 from shared_prefix_paged_amd import runtime as R
+from shared_prefix_paged_amd import InvalidArgument
 
 
 def batch_of(group_of, group_len, hkv=8, hq=32, d=128, dtype="bf16"):
@@ -22,18 +23,20 @@ def batch_of(group_of, group_len, hkv=8, hq=32, d=128, dtype="bf16"):
     return R.DecodeBatch(q, list(group_of), bases, list(group_len), tables, lens, 1, hkv)
 
 
-def params(fixed, flat_gbps=10000.0, prefix_gbps=4000.0, prefix_tflops=420.0, min_req=2):
+def params(fixed, flat_gbps=10000.0, prefix_gbps=4000.0, prefix_tflops=420.0, min_req=2, row_ns=0.0):
     p = R.default_params(A.SPKV_MODE_PER_GROUP)
     p.fixed_cost_us, p.flat_gbps, p.prefix_gbps, p.prefix_tflops = fixed, flat_gbps, prefix_gbps, prefix_tflops
     p.min_group_requests = min_req
+    p.row_cost_ns = row_ns
     return p
 
 
-def benefit_us(n, lp, hkv=8, hq=32, d=128, flat_gbps=10000.0, prefix_gbps=4000.0, prefix_tflops=420.0):
+def benefit_us(n, lp, hkv=8, hq=32, d=128, flat_gbps=10000.0, prefix_gbps=4000.0, prefix_tflops=420.0,
+               row_ns=0.0):
     kvb = 2 * hkv * d * 2
     t_flat = n * lp * kvb / (flat_gbps * 1e3)
     t_c = max(lp * kvb / (prefix_gbps * 1e3), 4.0 * n * (hq // hkv) * lp * d * hkv / (prefix_tflops * 1e6))
-    return t_flat - t_c
+    return t_flat - t_c - row_ns * n * hq * 1e-3
 
 
 def test_one_group_needs_benefit_above_fixed_cost():
@@ -67,8 +70,31 @@ def test_float32_and_forced_modes():
     assert list(R.dispatch(bt, R.default_params(A.SPKV_MODE_FORCE_CASCADE))) == [1]
 
 
-@pytest.mark.parametrize("lp,expect", [(256, 0), (512, 0), (1024, 1), (16384, 1)])
-def test_default_constants_on_the_swept_shapes(lp, expect):
-    # the 8B-shaped layer (B = 64) at the swept prefix lengths: cascade from Lp = 1024
-    bt = batch_of([0] * 64, [lp])
+def test_row_cost_counts_per_member_row():
+    # the per-row term can turn a group's benefit negative; it scales with the members
+    b = benefit_us(16, 2048)
+    per_row = b / (16 * 32) * 1e3          # ns per row that cancels the benefit exactly
+    bt = batch_of([0] * 16, [2048])
+    assert list(R.dispatch(bt, params(fixed=0.0, row_ns=0.9 * per_row))) == [1]
+    assert list(R.dispatch(bt, params(fixed=0.0, row_ns=1.1 * per_row))) == [0]
+    with pytest.raises(InvalidArgument):
+        R.dispatch(bt, params(fixed=0.0, row_ns=-1.0))
+
+
+# Measured on MI355X (attention time per step, forced cascade vs forced flat):
+# which backend was faster at each swept point; the defaults must pick it
+# wherever the two differ by more than 2 us.
+SWEPT = [
+    # (Hq, Hkv, requests, Lp, cascade faster)
+    (32, 8, 64, 256, 0), (32, 8, 64, 512, 0), (32, 8, 64, 1024, 1), (32, 8, 64, 16384, 1),
+    (10, 2, 256, 512, 0), (10, 2, 256, 1024, 1), (10, 2, 256, 4096, 1),
+    (32, 8, 1, 16384, 0), (32, 8, 4, 16384, 1), (32, 8, 8, 16384, 1),
+    (32, 8, 4, 4096, 0), (32, 8, 16, 4096, 1),
+    (10, 2, 2, 16384, 0), (10, 2, 8, 16384, 1), (10, 2, 16, 4096, 0), (10, 2, 64, 4096, 1),
+]
+
+
+@pytest.mark.parametrize("hq,hkv,n,lp,expect", SWEPT)
+def test_default_constants_on_the_swept_shapes(hq, hkv, n, lp, expect):
+    bt = batch_of([0] * n, [lp], hkv=hkv, hq=hq)
     assert list(R.dispatch(bt, R.default_params(A.SPKV_MODE_PER_GROUP))) == [expect]
