@@ -55,6 +55,11 @@ def parse():
     ap.add_argument("--sweep-batch", default=None, metavar="B1,B2,...",
                     help="time cascade and dense attention at each number of requests sharing the prefix "
                          "(at the configuration's or --lp's prefix length) and exit")
+    ap.add_argument("--layout-study", action="store_true",
+                    help="time the prefix storage layouts (HOT slab cascade / HOT slab flat / private COLD copies) and exit")
+    ap.add_argument("--layout-batch", type=int, default=256, help="requests sharing the prefix in --layout-study")
+    ap.add_argument("--layout-variant", default=None, choices=["hot_cascade", "hot_flat", "private_flat"],
+                    help="only this variant of --layout-study (one per counter run)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-MiB device buffer 5 times (counter calibration) and exit")
     return ap.parse_args()
@@ -137,6 +142,107 @@ def sweep_lp(args) -> int:
     return 0
 
 
+def layout_study(args) -> int:
+    """The storage layout in isolation, at B requests sharing an Lp-token
+    prefix (Llama-3.1-8B layer shape): the prefix stored once in the HOT slab
+    and read once by the prefix contraction (cascade); stored once but
+    re-read for every request by the paged pass (flat over the shared rows);
+    and copied into every request's own COLD pages (flat over private copies,
+    the layout of a pool without a shared level).  Warm and cold-cache
+    attention times and algorithmic bytes; one JSON line.  Timing only: pool
+    contents are random on the device (the paths are parity-tested on the
+    oracle's inputs elsewhere)."""
+    import numpy as np
+    import torch
+    from shared_prefix_paged_amd import runtime as R
+    from shared_prefix_paged_amd import _abi as A
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    B, Hq, Hkv, d = args.layout_batch, 32, 8, 128
+    Lp = args.lp or 8192
+    kvb = 2 * Hkv * d * 2
+    rng = np.random.Generator(np.random.PCG64(105))
+    ls = rng.integers(256, 2048, size=B, endpoint=True).astype(np.int64)   # COLD suffix per request
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(105)
+    q = torch.randn((B, Hq, d), generator=gen, device=dev).to(torch.bfloat16)
+
+    def build(private: bool):
+        lengths = ls + (Lp if private else 0)
+        pages = int(lengths.sum()) + 32 * B
+        cp = R.ColdPool(pages, 1, rng.permutation(pages).astype(np.int32))   # shuffled P = 1 slots
+        seqs = [cp.seq_new() for _ in range(B)]
+        for t in range(int(lengths.max())):
+            cp.append_batch([s for s, n in zip(seqs, lengths) if n > t])
+        tables, lens = cp.block_tables(seqs, int(lengths.max()))
+        pools = R.KVPools.allocate(1 if private else Lp, pages, Hkv, d, torch.bfloat16, dev)
+        for t in (pools.k_hot, pools.v_hot, pools.k_cold, pools.v_cold):
+            t.normal_(generator=gen)
+        if private:
+            batch = R.DecodeBatch(q, [-1] * B, [], [], tables, lens, 1, Hkv)
+        else:
+            batch = R.DecodeBatch(q, [0] * B, [0], [Lp], tables, lens, 1, Hkv)
+        return cp, pools, batch
+
+    variants = {"hot_cascade": (False, A.SPKV_MODE_FORCE_CASCADE),
+                "hot_flat": (False, A.SPKV_MODE_FORCE_DENSE),
+                "private_flat": (True, A.SPKV_MODE_FORCE_DENSE)}
+    pick = [args.layout_variant] if args.layout_variant else list(variants)
+    scratch = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device=dev)
+    clean = torch.zeros(args.flush_mib << 20, dtype=torch.uint8, device=dev)
+    attn_ids = (A.SPKV_KERNEL_PREFIX, A.SPKV_KERNEL_FLAT, A.SPKV_KERNEL_MERGE)
+    kname = {A.SPKV_KERNEL_PREFIX: "prefix_mfma", A.SPKV_KERNEL_FLAT: "flat_paged", A.SPKV_KERNEL_MERGE: "merge"}
+    res = {}
+    built = {}
+    for name in pick:
+        private, mode = variants[name]
+        if private not in built:
+            built.clear()
+            torch.cuda.empty_cache()
+            built[private] = build(private)
+        cp, pools, batch = built[private]
+        params = R.default_params(mode)
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+        ws = torch.empty(batch.workspace_size(), dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            R.decode_step(batch, pools, params, ws, out, lse)
+        torch.cuda.synchronize()
+        with R.KernelTimer() as kt:
+            for _ in range(args.steps):
+                R.decode_step(batch, pools, params, ws, out, lse)
+            torch.cuda.synchronize()
+            per = {k: kt.read(k) for k in attn_ids}
+        warm = 1e3 * sum(v[0] for v in per.values()) / args.steps
+        cold = []
+        for i in range(args.cold_runs):
+            scratch.fill_(i & 1)
+            clean.view(torch.int64).sum()
+            torch.cuda.synchronize()
+            with R.KernelTimer() as kc:
+                R.decode_step(batch, pools, params, ws, out, lse)
+                torch.cuda.synchronize()
+                cold.append(1e3 * sum(kc.read(k)[0] for k in attn_ids))
+        assert torch.isfinite(out).all()
+        tokens = int(B * Lp + ls.sum())
+        stored = (Lp if not private else B * Lp) * kvb            # prefix bytes held in HBM
+        read = (Lp if mode == A.SPKV_MODE_FORCE_CASCADE else B * Lp) * kvb + int(ls.sum()) * kvb
+        res[name] = {"warm_us": round(warm, 2), "cold_median_us": round(float(np.median(cold)), 2) if cold else None,
+                     "kernels_us": {kname[k]: round(1e3 * v[0] / max(1, v[1]), 2) for k, v in per.items() if v[1]},
+                     "kv_bytes_read": read, "prefix_bytes_stored": stored,
+                     "kv_tokens_per_s_warm": round(tokens / (warm * 1e-6), 1)}
+        print(f"[layout] {name}: {json.dumps(res[name])}", file=sys.stderr, flush=True)
+        del ws, out, lse
+    print(json.dumps({"metric": "attention time per step by prefix storage layout", "unit": "us",
+                      "config": {"workload": f"B={B} requests sharing Lp={Lp}, Hq={Hq}, Hkv={Hkv}, d={d}, bf16, "
+                                             "Ls~U[256, 2048], shuffled P = 1 COLD slots",
+                                 "steps": args.steps, "cold_runs": args.cold_runs,
+                                 "flush_bytes": args.flush_mib << 20},
+                      "variants": res}), flush=True)
+    return 0
+
+
 def source_digest() -> str:
     """Digest of the sources that decide what the kernels read and write."""
     import hashlib
@@ -172,6 +278,8 @@ def main():
         return copy_probe(args.copy_probe)
     if args.sweep_lp or args.sweep_batch:
         return sweep_lp(args)
+    if args.layout_study:
+        return layout_study(args)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
               "this build has no multi-GPU path.", file=sys.stderr)

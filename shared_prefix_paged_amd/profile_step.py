@@ -20,6 +20,11 @@ launch), ``profiles/<config>_<mode>_counters.md`` (MFMA and LDS counters)
 and updates ``profiles/traffic.json``, which bench.py reads for its roofline
 ``traffic`` field while the kernel sources are unchanged.  Raw rocprofv3 output
 stays in --out.  This script itself never touches the GPU.
+
+With ``--layout`` it profiles ``bench.py --layout-study`` instead: the study's
+warm and cold times (one plain run), then ``--pmc FETCH_SIZE`` over each
+storage variant alone and over the copy probe, giving the HBM bytes each
+layout reads per step; writes ``profiles/layout_study.md``.
 """
 from __future__ import annotations
 
@@ -79,6 +84,50 @@ def counter_means(files, counter):
     return {k: (sums[k] / counts[k], counts[k]) for k in sums}
 
 
+def layout_profile(a, prof_dir):
+    bench = os.path.join(ROOT, "bench.py")
+    study = [bench, "--layout-study", "--steps", "10", "--cold-runs", "10"]
+    print(f"[profile] layout study: {' '.join(study)}", flush=True)
+    r = subprocess.run([sys.executable] + study, cwd=ROOT, stdout=subprocess.PIPE, stderr=subprocess.DEVNULL,
+                       text=True, timeout=400)
+    if r.returncode != 0:
+        raise RuntimeError(f"layout study exited {r.returncode}")
+    times = json.loads(r.stdout.strip().splitlines()[-1])
+    c_copy, f_copy = rocprof(["--pmc", "FETCH_SIZE"], a.out, "fetch_size_copy", [bench, "--copy-probe", str(COPY_MIB)],
+                             limit=120)
+    kib, _ = max(counter_means(f_copy, "FETCH_SIZE").values(), key=lambda v: v[0])
+    factor = (COPY_MIB << 20) / (kib * 1024.0)
+    rows, cmds = [], [c_copy]
+    for v, rec in times["variants"].items():
+        c, f = rocprof(["--pmc", "FETCH_SIZE"], a.out, f"fetch_size_{v}",
+                       [bench, "--layout-study", "--layout-variant", v, "--steps", "3", "--cold-runs", "0"], limit=240)
+        cmds.append(c)
+        m = counter_means(f, "FETCH_SIZE")
+        per_step = sum(m[k][0] for k in KERNELS.values() if k in m) * 1024 * factor
+        rows.append((v, rec, per_step))
+    rel = lambda c: " ".join(os.path.relpath(x, ROOT) if x.startswith(ROOT) else x for x in c)
+    md = ["# Prefix storage layout in isolation", "",
+          f"Workload: {times['config']['workload']}. The same decode-step attention with the shared prefix",
+          "(1) stored once in the HOT slab and read once by the prefix contraction (cascade), (2) stored once in",
+          "the HOT slab but re-read for every request by the paged pass (flat), (3) copied into every request's own",
+          "COLD pages (flat over private copies: a pool without a shared level). Warm: mean of the attention kernels'",
+          f"event durations over {times['config']['steps']} back-to-back steps; cold: median over",
+          f"{times['config']['cold_runs']} runs, each after a {times['config']['flush_bytes'] >> 20} MiB flush.",
+          "HBM read per step: FETCH_SIZE of the attention kernels (one rocprofv3 run per variant), scaled by the",
+          f"same counter over a {COPY_MIB} MiB device copy ({factor * 1024:.1f} bytes per KiB read).", "",
+          "| variant | prefix bytes stored | algorithmic K/V bytes read | HBM read (FETCH_SIZE) | warm us | cold us | "
+          "kernels (warm, us) |", "|---|---|---|---|---|---|---|"]
+    for v, rec, hbm in rows:
+        ks = ", ".join(f"{k} {t}" for k, t in rec["kernels_us"].items())
+        md.append(f"| {v} | {rec['prefix_bytes_stored'] / 1e6:.1f} MB | {rec['kv_bytes_read'] / 1e9:.3f} GB | "
+                  f"{hbm / 1e9:.3f} GB | {rec['warm_us']} | {rec['cold_median_us']} | {ks} |")
+    md += ["", "Commands: the study (repo root) and the counter runs (from /tmp, TMPDIR=/tmp):", "", "```",
+           "python " + rel(study)] + [rel(c) for c in cmds] + ["```", ""]
+    open(os.path.join(prof_dir, "layout_study.md"), "w").write("\n".join(md) + "\n")
+    print(json.dumps({v: {"hbm_read_bytes": int(h), "warm_us": rec["warm_us"]} for v, rec, h in rows}), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--config", default="C1")
@@ -87,10 +136,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "profile"), help="raw rocprofv3 output")
     ap.add_argument("--prof-dir", default=os.path.join(ROOT, "profiles"), help="where the summaries go")
+    ap.add_argument("--layout", action="store_true", help="profile bench.py --layout-study instead of the step")
     a = ap.parse_args()
     os.makedirs(a.out, exist_ok=True)
     prof_dir = os.path.abspath(a.prof_dir)
     os.makedirs(prof_dir, exist_ok=True)
+    if a.layout:
+        return layout_profile(a, prof_dir)
     bench = os.path.join(ROOT, "bench.py")
     run = [bench, "--config", a.config, "--mode", a.mode, "--no-cpu-baseline", "--cold-runs", "0"]
     name = f"{a.config.lower()}_{a.mode}"
