@@ -18,6 +18,7 @@ one GPU.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -55,6 +56,8 @@ def parse():
     ap.add_argument("--sweep-batch", default=None, metavar="B1,B2,...",
                     help="time cascade and dense attention at each number of requests sharing the prefix "
                          "(at the configuration's or --lp's prefix length) and exit")
+    ap.add_argument("--layers", type=int, default=1,
+                    help="with L > 1: a decode step over L layers (per-layer pools, shared slots); own JSON line")
     ap.add_argument("--layout-study", action="store_true",
                     help="time the prefix storage layouts (HOT slab cascade / HOT slab flat / private COLD copies) and exit")
     ap.add_argument("--layout-batch", type=int, default=256, help="requests sharing the prefix in --layout-study")
@@ -76,6 +79,14 @@ def copy_probe(mib: int) -> int:
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
     return 0
+
+
+def quiet_gc() -> None:
+    """Collect once, then keep every object alive so far out of later
+    collections: a full collection over the setup's objects otherwise stalls
+    the host for tens of ms inside a timed region (the GPU queue runs dry)."""
+    gc.collect()
+    gc.freeze()
 
 
 def sweep_lp(args) -> int:
@@ -114,6 +125,7 @@ def sweep_lp(args) -> int:
         for name, mode in (("cascade", A.SPKV_MODE_FORCE_CASCADE), ("dense", A.SPKV_MODE_FORCE_DENSE),
                            ("dispatch", A.SPKV_MODE_PER_GROUP)):
             params = R.default_params(mode)
+            quiet_gc()
             for _ in range(3):
                 _, _, choice = R.decode_step(st.batch, st.pools, params, ws, out, lse)
             torch.cuda.synchronize()
@@ -206,6 +218,7 @@ def layout_study(args) -> int:
         out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
         lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
         ws = torch.empty(batch.workspace_size(), dtype=torch.uint8, device=dev)
+        quiet_gc()
         for _ in range(3):
             R.decode_step(batch, pools, params, ws, out, lse)
         torch.cuda.synchronize()
@@ -240,6 +253,107 @@ def layout_study(args) -> int:
                                  "steps": args.steps, "cold_runs": args.cold_runs,
                                  "flush_bytes": args.flush_mib << 20},
                       "variants": res}), flush=True)
+    return 0
+
+
+def multi_layer(args) -> int:
+    """A decode step over L layers of one model: per-layer HOT slabs and COLD
+    pools (the same slots in every layer), one host append per step, then per
+    layer the K/V write and the attention call.  The step touches L times one
+    layer's K/V, far more than the caches hold, so nothing is reused from the
+    previous step.  One JSON line: KV tokens attended per second over all
+    layers, and per-layer times."""
+    import numpy as np
+    import torch
+    import workloads as W
+    from shared_prefix_paged_amd import runtime as R
+    from shared_prefix_paged_amd import _abi as A
+    from hip_setup import setup_single_step, to_device
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    L = args.layers
+    total_steps = args.warmup + 2 * args.steps + 1
+    wl = W.make_workload(W.CONFIGS[args.config], prefix_len=args.lp, page_size=args.page_size,
+                         extra_steps=max(32, total_steps + 1))
+    cfg = wl.cfg
+    B, Hq, Hkv, d, P = wl.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.page_size
+    st = setup_single_step(wl, device=dev, max_blocks=(int(wl.suffix_len.max()) + total_steps + P - 1) // P + 1)
+    batch, cold = st.batch, st.cold
+    layers = [st.pools]
+    for _ in range(1, L):                        # the same contents at other addresses
+        p0 = st.pools
+        pl = R.KVPools.allocate(p0.hot_capacity, p0.cold_slots, Hkv, d, p0.k_cold.dtype, dev)
+        for dst, src in ((pl.k_hot, p0.k_hot), (pl.v_hot, p0.v_hot), (pl.k_cold, p0.k_cold), (pl.v_cold, p0.v_cold)):
+            dst.copy_(src)
+        layers.append(pl)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(106)
+    qs = [torch.randn((B, Hq, d), generator=gen, device=dev).to(layers[0].k_cold.dtype) for _ in range(L)]
+    kv_new = []
+    for s_ in range(total_steps):
+        dr = W.step_draws(cfg, s_, B)
+        kv_new.append((to_device(dr.k_new, cfg.dtype, dev), to_device(dr.v_new, cfg.dtype, dev)))
+    seqs = np.asarray(st.seqs, dtype=np.int32)
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    ws = torch.empty(batch.workspace_size(), dtype=torch.uint8, device=dev)
+    params = R.default_params(A.SPKV_MODE_PER_GROUP)
+    lp_of = np.array([wl.prefix_len_of(b) for b in range(B)], dtype=np.int64)
+    mb = batch.max_blocks
+    state = {"i": 0}
+
+    def one_step():
+        i = state["i"]
+        slots, cows = cold.append_batch(seqs)
+        k, v = kv_new[i]
+        for li, pl in enumerate(layers):
+            if cows:
+                R.copy_blocks(torch.tensor(cows, dtype=torch.int32, device=dev), pl.k_cold, pl.v_cold,
+                              cold.num_pages, P, Hkv, d)
+            # layer 0 also appends to the (shared) device block tables and lengths
+            R.append_tokens(k, v, slots, pl.k_cold, pl.v_cold, pl.cold_slots, P, Hkv, d,
+                            tables=batch.tables if li == 0 else None, max_blocks=mb if li == 0 else 0,
+                            lens=batch.lens if li == 0 else None)
+        batch.lens_h += 1
+        for li, pl in enumerate(layers):
+            batch.struct.q = qs[li].data_ptr()
+            R.decode_step(batch, pl, params, ws, out, lse)
+        state["i"] = i + 1
+        return L * int(np.sum(lp_of + batch.lens_h))
+
+    quiet_gc()
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    tokens = 0
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        tokens += one_step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    with R.KernelTimer() as kt:
+        for _ in range(args.steps):
+            one_step()
+        torch.cuda.synchronize()
+        per = {name: kt.read(k) for name, k in (("prefix_mfma", A.SPKV_KERNEL_PREFIX), ("flat_paged", A.SPKV_KERNEL_FLAT),
+                                                ("merge", A.SPKV_KERNEL_MERGE), ("append", A.SPKV_KERNEL_CACHE))}
+    assert torch.isfinite(out).all()
+    print(json.dumps({
+        "metric": f"decode-step attention over {L} layers, KV-tokens/s", "value": round(tokens / wall, 1),
+        "unit": "KV-tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(1e3 * wall / args.steps, 4), "gpu_ms_per_step": round(gpu_ms / args.steps, 4),
+        "us_per_layer": round(1e3 * gpu_ms / args.steps / L, 2), "higher_is_better": True, "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name} layer shape x {L} layers (per-layer HOT slab and COLD pool, shared slots)",
+                   "layers": L, "batch": B, "prefix_len": [int(x) for x in wl.group_prefix_len], "page_size": P},
+        "kernels_avg_us": {k: round(1e3 * v[0] / v[1], 2) for k, v in per.items() if v[1]},
+        "hbm_bytes_held": int(sum(t.numel() * t.element_size() for pl in layers
+                                  for t in (pl.k_hot, pl.v_hot, pl.k_cold, pl.v_cold)))}), flush=True)
     return 0
 
 
@@ -280,6 +394,8 @@ def main():
         return sweep_lp(args)
     if args.layout_study:
         return layout_study(args)
+    if args.layers > 1:
+        return multi_layer(args)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
               "this build has no multi-GPU path.", file=sys.stderr)
@@ -349,6 +465,7 @@ def main():
         state["i"] = i + 1
         return int(np.sum(lp_of + batch.lens_h))                     # logical KV tokens attended
 
+    quiet_gc()
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
