@@ -763,12 +763,13 @@ __global__ __launch_bounds__(256, (BF16 ? 2 : (G <= 6 ? 4 : 3))) void flat_kerne
     // First request whose tokens reach past s0: the number of requests that
     // end at or before s0 (offs is non-decreasing), counted in one pass
     // instead of a chain of dependent loads.
+    constexpr int NQW = (spkv::kFlatArgReqs + 63) / 64;
+    int ends[NQW];
+#pragma unroll
+    for (int j = 0; j < NQW; ++j) ends[j] = fl.offs[min(lane + 64 * j, fl.nreq - 1) + 1];   // all loads in flight
     int i = 0;
 #pragma unroll
-    for (int j = 0; j < (spkv::kFlatArgReqs + 63) / 64; ++j) {
-        const int idx = lane + 64 * j;
-        i += __popcll(__ballot(idx < fl.nreq && fl.offs[idx + 1] <= s0));
-    }
+    for (int j = 0; j < NQW; ++j) i += __popcll(__ballot(lane + 64 * j < fl.nreq && ends[j] <= s0));
     const int slot0 = part == kPartRest ? a.prefix_splits : 0;
     for (; i < fl.nreq; ++i) {
         const int64_t o0 = fl.offs[i], o1 = fl.offs[i + 1];
