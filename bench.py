@@ -2,11 +2,14 @@
 """Decode-step benchmark of HOT/COLD cascade attention on one MI355X.
 
 One step = the whole hot path over one batch: one COLD append per request
-(host allocator), copy-on-write page copies (none without forks), one launch
-that writes the step's K/V at their slots and appends to the device block
-tables (slots travel in the launch), per-step dispatch, then cascade
-attention (bf16 MFMA prefix contraction over the HOT slab, paged suffix pass
-over COLD, log-sum-exp merge).  Inputs are seeded synthetic tensors already resident in HBM.
+(host allocator), copy-on-write page copies (none without forks), per-step
+dispatch, then cascade attention (bf16 MFMA prefix contraction over the HOT
+slab, paged suffix pass over COLD, log-sum-exp merge) with the step's new
+K/V fused in: the paged pass reads each request's new token from the step's
+K/V tensor, and the merge lands it in its slot and advances the device block
+tables and lengths (spkv_decode_step_append; --separate-append uses one
+spkv_append_tokens launch before spkv_decode_step instead).  Inputs are
+seeded synthetic tensors already resident in HBM.
 
 Default workload: the Llama-3.1-8B-shaped layer (B = 64, Hq = 32, Hkv = 8,
 d = 128, bf16, Lp = 16384, Ls ~ U[256, 2048] growing by one token per step,
@@ -56,6 +59,8 @@ def parse():
     ap.add_argument("--sweep-batch", default=None, metavar="B1,B2,...",
                     help="time cascade and dense attention at each number of requests sharing the prefix "
                          "(at the configuration's or --lp's prefix length) and exit")
+    ap.add_argument("--separate-append", action="store_true",
+                    help="append the step's K/V with its own launch (spkv_append_tokens) before the decode step")
     ap.add_argument("--layers", type=int, default=1,
                     help="with L > 1: a decode step over L layers (per-layer pools, shared slots); own JSON line")
     ap.add_argument("--layout-study", action="store_true",
@@ -446,6 +451,7 @@ def main():
     params = R.default_params(mode)
     lp_of = np.array([wl.prefix_len_of(b) for b in range(B)], dtype=np.int64)
     state = {"i": 0, "choice": None}
+    separate = args.separate_append or cfg.dtype != "bf16"     # the fused step is bf16 only
 
     def one_step(flush=None):
         i = state["i"]
@@ -453,14 +459,18 @@ def main():
         if cows:
             R.copy_blocks(torch.tensor(cows, dtype=torch.int32, device=dev), pools.k_cold, pools.v_cold,
                           cold.num_pages, P, Hkv, d)
-        # new K/V to their slots + device block tables, one launch (slots travel in the launch)
-        R.append_tokens(k_steps[i], v_steps[i], slots, pools.k_cold, pools.v_cold, pools.cold_slots, P, Hkv, d,
-                        tables=batch.tables, max_blocks=mb, lens=batch.lens)
+        if separate:
+            # new K/V to their slots + device block tables, one launch (slots travel in the launch)
+            R.append_tokens(k_steps[i], v_steps[i], slots, pools.k_cold, pools.v_cold, pools.cold_slots, P, Hkv, d,
+                            tables=batch.tables, max_blocks=mb, lens=batch.lens)
         batch.lens_h += 1                                            # host mirror of the lengths
         batch.struct.q = q_steps[i].data_ptr()
         if flush is not None:
             flush()                                                  # outside the event window
-        _, _, choice = R.decode_step(batch, pools, params, ws, out, lse)
+        if separate:
+            _, _, choice = R.decode_step(batch, pools, params, ws, out, lse)
+        else:
+            _, _, choice = R.decode_step_append(batch, pools, params, ws, k_steps[i], v_steps[i], slots, out, lse)
         state["choice"] = choice
         state["i"] = i + 1
         return int(np.sum(lp_of + batch.lens_h))                     # logical KV tokens attended
@@ -573,7 +583,8 @@ def main():
                 pf += 4.0 * len(members) * Hq * int(lp) * d
         prefix_b.append(pb)
         prefix_f.append(pf)
-        merge_b.append(part_bytes + ppart + rows * (d + 1) * 4)
+        # (fused step: the merge also reads the new tokens' K/V and writes them to their slots)
+        merge_b.append(part_bytes + ppart + rows * (d + 1) * 4 + (0 if separate else 2 * B * kvb))
     flat_bytes, prefix_bytes = float(np.mean(flat_b)), float(np.mean(prefix_b))
     prefix_flops, merge_bytes = float(np.mean(prefix_f)), float(np.mean(merge_b))
 
@@ -643,6 +654,7 @@ def main():
             "batch": B, "prefix_len": [int(x) for x in wl.group_prefix_len], "page_size": P,
             "slots": "contiguous" if args.contiguous else "shuffled",
             "backend": ("cascade" if cascade else "dense"), "mode": args.mode,
+            "append": "separate launch" if separate else "fused into the step",
         },
         "gpu_ms_per_step": round(gpu_ms / args.steps, 4),
         "attention_us_per_step": round(attn_us, 2),

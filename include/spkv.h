@@ -327,6 +327,24 @@ spkv_status spkv_decode_step(const spkv_batch *batch, const spkv_kv *kv, const s
                              float *out, float *lse, void *ws, size_t ws_bytes, void *stream,
                              int32_t *cascade_out);
 
+/* The step's appends fused into the decode step ([PKV] How it works, steps
+ * 1-3, then the step as above): the same results, pools, block tables and
+ * lengths as spkv_append_tokens(k_new, v_new, host_slots, rows 0..B-1, ...,
+ * block_tables, cold_lens) followed by spkv_decode_step, with one launch
+ * fewer.  The paged pass reads request b's new token from row b of k_new /
+ * v_new ([B, Hkv, d], device); the merge then writes it to COLD slot
+ * host_slots[b] (host [B], the allocator's output) and advances the device
+ * block table and length.  batch->host_cold_lens must already count the new
+ * token; the device cold_lens and block tables must not.  bf16 only.
+ * Returns SPKV_E_INVAL, before any launch, for a slot outside
+ * [0, cold_slots), a length whose new token has no block-table column, a
+ * COLD pool with Hkv * cold_slots >= 2^30, or float32 data.  Run
+ * spkv_copy_blocks for the step's copy-on-write pairs first. */
+spkv_status spkv_decode_step_append(const spkv_batch *batch, const spkv_kv *kv,
+                                    const spkv_dispatch_params *params, const void *k_new, const void *v_new,
+                                    const int32_t *host_slots, float *out, float *lse, void *ws,
+                                    size_t ws_bytes, void *stream, int32_t *cascade_out);
+
 /* ======================================================================
  * Plan inspection and kernel timing (measurement support).
  * ==================================================================== */

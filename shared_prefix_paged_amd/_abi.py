@@ -90,6 +90,8 @@ SIGNATURES = {
     "spkv_dispatch_params_default": (None, [P_params]),
     "spkv_dispatch": (c_i32, [P_batch, P_params, P_i32]),
     "spkv_decode_step": (c_i32, [P_batch, P_kv, P_params, c_vp, c_vp, c_vp, c_sz, c_vp, P_i32]),
+    "spkv_decode_step_append": (c_i32, [P_batch, P_kv, P_params, c_vp, c_vp, P_i32, c_vp, c_vp, c_vp, c_sz, c_vp,
+                                        P_i32]),
     "spkv_plan_query": (c_i32, [P_batch, P_i32, C.POINTER(spkv_plan_info)]),
     "spkv_plan_parts": (c_i32, [P_batch, P_i32, P_i32, P_i32]),
     "spkv_timing_enable": (c_i32, [c_i32]),

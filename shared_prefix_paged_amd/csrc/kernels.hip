@@ -72,6 +72,12 @@ struct Args {
     int32_t flat_tau, prefix_tau, prefix_granule;
     int32_t prefix_mode;    // 0: no prefix partials; 1: MFMA split rule; 2: paged prefix pass
     GroupMask cascade;
+    // Append mode (the step's new tokens not yet in the pools): every request
+    // has one COLD token more than cold_lens counts, the last one, whose K/V
+    // rows are row b of k_new / v_new [B, Hkv, d].
+    const void *k_new;
+    const void *v_new;
+    int32_t append;
 };
 
 __device__ __forceinline__ bool mask_get(const GroupMask &m, int g) { return (m.bits[g >> 5] >> (g & 31)) & 1u; }
@@ -109,7 +115,7 @@ __device__ __forceinline__ Req req_geo(const Args &a, int b) {
         }
         r.casc = mask_get(a.cascade, r.g);
     }
-    int ls = ld_const(a.cold_lens + b);
+    int ls = ld_const(a.cold_lens + b) + a.append;
     const int64_t cap = (int64_t)a.max_blocks * a.page_size;
     r.ls = ls < 0 ? 0 : (ls > cap ? (int)cap : ls);
     if (a.cold_slots < a.page_size) r.ls = 0;   // no COLD page to read
@@ -539,7 +545,7 @@ __device__ __forceinline__ float sum_of_groups(float v) {
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
-template <int D, int G>
+template <int D, int G, bool APP>
 __device__ __forceinline__ void attend_range_mfma(const Args &a, const Req &r, int b, int h, int t0, int t1,
                                                   int slot, int lane, char *ring, uint32_t ring_off) {
     using F = FlatMfmaGeom<D>;
@@ -555,6 +561,8 @@ __device__ __forceinline__ void attend_range_mfma(const Args &a, const Req &r, i
     const char *vhot = (const char *)a.v_hot;
     const char *kcold = (const char *)a.k_cold;
     const char *vcold = (const char *)a.v_cold;
+    const int64_t knew_from_cold = APP ? (int64_t)((uintptr_t)a.k_new - (uintptr_t)a.k_cold) : 0;
+    const int64_t vnew_from_cold = APP ? (int64_t)((uintptr_t)a.v_new - (uintptr_t)a.v_cold) : 0;
     const int32_t *table = a.tables + (int64_t)b * a.max_blocks;
     const int64_t num_pages = a.cold_slots / a.page_size;
     const uint32_t hot_row0 = (uint32_t)(r.base * a.Hkv + (int64_t)h * r.lp);
@@ -566,8 +574,11 @@ __device__ __forceinline__ void attend_range_mfma(const Args &a, const Req &r, i
     auto lane_token = [&](int nb) { return min(t0 + 64 * nb + lane, t1 - 1); };
     auto first_entry = [&](int nb) { return (max(t0 + 64 * nb, r.lp) - r.lp) / a.page_size; };
     auto block_has_cold = [&](int nb) { return t0 + 64 * nb < t1 && t0 + 64 * nb + 63 >= r.lp; };
+    // Row codes: bit 31 HOT slab row; else, in append mode, bit 30 marks the
+    // new token (row b * Hkv + h of k_new / v_new); else a COLD slot row.
     auto code_of = [&](int t, int32_t entry) -> uint32_t {
         if (t < r.lp) return 0x80000000u | (hot_row0 + (uint32_t)t);
+        if (APP && t == r.lp + r.ls - 1) return 0x40000000u | (uint32_t)(b * a.Hkv + h);
         int64_t page = entry;
         page = page < 0 ? 0 : (page >= num_pages ? num_pages - 1 : page);
         return (uint32_t)((page * a.page_size + (t - r.lp) % a.page_size) * a.Hkv + h);
@@ -637,9 +648,19 @@ __device__ __forceinline__ void attend_range_mfma(const Args &a, const Req &r, i
             const int ti = (j % SPB) * TOK + F::RPI * i + lane / F::CPR;   // token inside its 64-block
             const uint32_t c = (uint32_t)__shfl((int)code, ti, 64);
             const bool hot = c >> 31;
-            const int64_t off = (int64_t)(c & 0x7fffffffu) * F::ROWB;
-            dma16_at((hot ? khot : kcold) + off + ksrc[i], dst + 1024u * i);
-            dma16_at((hot ? vhot : vcold) + off + vsrc[i], dst + F::OPB + 1024u * i);
+            // the new token: its row of k_new / v_new, reached from the COLD
+            // base by a per-lane distance (selects, no divergent branch)
+            if constexpr (APP) {   // per-lane selects, no branch: one copy of the issue code
+                const bool nw = !hot & (((c >> 30) & 1u) != 0u);
+                const int64_t off = (int64_t)(c & (hot ? 0x7fffffffu : 0x3fffffffu)) * F::ROWB;
+                const int64_t kd = nw ? knew_from_cold : 0, vd = nw ? vnew_from_cold : 0;
+                dma16_at((hot ? khot : kcold) + off + kd + ksrc[i], dst + 1024u * i);
+                dma16_at((hot ? vhot : vcold) + off + vd + vsrc[i], dst + F::OPB + 1024u * i);
+            } else {
+                const int64_t off = (int64_t)(c & 0x7fffffffu) * F::ROWB;
+                dma16_at((hot ? khot : kcold) + off + ksrc[i], dst + 1024u * i);
+                dma16_at((hot ? vhot : vcold) + off + vsrc[i], dst + F::OPB + 1024u * i);
+            }
         }
     };
 
@@ -745,7 +766,7 @@ __device__ __forceinline__ void attend_range_mfma(const Args &a, const Req &r, i
 // the LDS ring (4 x 8.25 KB per block of 4 waves) admits 4 blocks per CU.
 // bf16: the LDS ring (4 x 8 KB per wave for d = 128) admits one or two
 // blocks per CU, so registers are not the limit.
-template <bool BF16, int D, int G>
+template <bool BF16, int D, int G, bool APP = false>
 __global__ __launch_bounds__(256, (BF16 ? 2 : (G <= 6 ? 4 : 3))) void flat_kernel(Args a, int part, FlatLaunch fl) {
     extern __shared__ __attribute__((aligned(1024))) char flat_smem[];
     const int k = blockIdx.x;
@@ -785,7 +806,7 @@ __global__ __launch_bounds__(256, (BF16 ? 2 : (G <= 6 ? 4 : 3))) void flat_kerne
         const int t0 = lo + (int)(lo_s - o0);
         const int t1 = min(hi, lo + (int)(hi_s - o0));   // device data shorter than the plan: clamp
         if (t1 <= t0) continue;
-        if constexpr (BF16) attend_range_mfma<D, G>(a, r, b, h, t0, t1, slot0 + slot, lane, ring, ring_off);
+        if constexpr (BF16) attend_range_mfma<D, G, APP>(a, r, b, h, t0, t1, slot0 + slot, lane, ring, ring_off);
         else attend_range<BF16, D, G>(a, r, b, h, t0, t1, slot0 + slot, lane, ring, ring_off);
     }
 }
@@ -1159,15 +1180,55 @@ __global__ __launch_bounds__(64 * W * KH) void prefix_mfma_kernel(Args a) {
 // holds partial k's weight exp2(lse_k - max); then each wave-wide load brings
 // PPW partial rows (LPP lanes x 16 bytes each), several loads in flight.
 // ---------------------------------------------------------------------------
-template <int D>
+// The step's new COLD slots of one sub-batch (append mode): slot of request
+// fr.b0 + i.  Checked on the host (in range, room in the block table).
+struct AppendSlots {
+    int32_t slots[spkv::kFlatArgReqs];
+};
+
+// APPEND: the merge launch also lands the step's new tokens, which the paged
+// pass read from k_new / v_new: every reader of the pools, block tables and
+// lengths has finished by now (same stream), so extra blocks copy each
+// request's K/V rows into its slot and advance its block table and length,
+// as spkv_append_tokens does.
+template <int D, bool APPEND = false>
 __global__ __launch_bounds__(256) void merge_kernel(Args a, float *out, float *lse_out, FlatLaunch fr,
-                                                    FlatLaunch fp) {
+                                                    FlatLaunch fp, AppendSlots ap) {
     constexpr int LPP = D / 4;      // lanes per partial row (float4 each)
     constexpr int PPW = 64 / LPP;   // partial rows per wave-wide load
     constexpr int BATCH = 40 / PPW; // wave-wide loads in flight (40 partials)
     constexpr int SMALL = 16 / PPW; // the same for rows of at most 16 partials
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: geometry by scalar loads
     const int lane = threadIdx.x & 63;
+    if constexpr (APPEND) {
+        // Blocks past the merge's own land the new tokens, one wave per
+        // request, beside the merging waves: each copies the request's K/V
+        // rows into its slot and advances its block table and length.  Every
+        // reader of these (the paged pass; this kernel reads none) is done.
+        const int64_t merge_blocks = ((int64_t)fr.nreq * a.Hq + 3) / 4;
+        if ((int64_t)blockIdx.x >= merge_blocks) {
+            const int i = (int)(((int64_t)blockIdx.x - merge_blocks) * 4 + wave);
+            if (i >= fr.nreq) return;
+            const int b = fr.b0 + i;
+            const int64_t slot = ap.slots[i];
+            const int pieces = a.Hkv * D * 2 / 16;   // 16-byte pieces of one token's K (or V) row
+            const u32x4_t *kn = (const u32x4_t *)a.k_new + (int64_t)b * pieces;
+            const u32x4_t *vn = (const u32x4_t *)a.v_new + (int64_t)b * pieces;
+            u32x4_t *kc = (u32x4_t *)a.k_cold + slot * pieces;
+            u32x4_t *vc = (u32x4_t *)a.v_cold + slot * pieces;
+            for (int q = lane; q < pieces; q += 64) {
+                kc[q] = kn[q];
+                vc[q] = vn[q];
+            }
+            if (lane == 0) {
+                int32_t *lens = (int32_t *)a.cold_lens;
+                const int len = lens[b];
+                ((int32_t *)a.tables)[(int64_t)b * a.max_blocks + len / a.page_size] = (int32_t)(slot / a.page_size);
+                lens[b] = len + 1;
+            }
+            return;
+        }
+    }
     const int64_t row = (int64_t)fr.b0 * a.Hq + (int64_t)blockIdx.x * 4 + wave;
     if (row >= (int64_t)(fr.b0 + fr.nreq) * a.Hq) return;
     const int b = (int)(row / a.Hq);
@@ -1458,6 +1519,16 @@ spkv_status launch_flat_g(const Args &a, int part, const FlatLaunch &f, dim3 gri
     static const hipError_t attr = hipFuncSetAttribute((const void *)flat_kernel<BF16, D, G>,
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, spkv::kLdsPerCU);
     if (attr != hipSuccess) return fail(SPKV_E_HIP, std::string("flat_kernel LDS limit: ") + hipGetErrorString(attr));
+    if constexpr (BF16) {
+        if (a.append) {   // the step's new tokens come from k_new / v_new
+            static const hipError_t attr2 = hipFuncSetAttribute(
+                (const void *)flat_kernel<BF16, D, G, true>, hipFuncAttributeMaxDynamicSharedMemorySize, spkv::kLdsPerCU);
+            if (attr2 != hipSuccess)
+                return fail(SPKV_E_HIP, std::string("flat_kernel LDS limit: ") + hipGetErrorString(attr2));
+            tl.launch(flat_kernel<BF16, D, G, true>, grid, block, lds, a, part, f);
+            return check_launch("flat_kernel");
+        }
+    }
     tl.launch(flat_kernel<BF16, D, G>, grid, block, lds, a, part, f);
     return check_launch("flat_kernel");
 }
@@ -1518,13 +1589,21 @@ spkv_status launch_prefix(const Args &a, const Plan &p, int d, hipStream_t st) {
 }
 
 spkv_status launch_merge(const Args &a, int d, float *out, float *lse, const FlatLaunch &fr, const FlatLaunch &fp,
-                         hipStream_t st) {
+                         const int32_t *append_slots, hipStream_t st) {
     const int64_t rows = (int64_t)fr.nreq * a.Hq;
     if (rows == 0) return SPKV_OK;
     dim3 grid((unsigned)((rows + 3) / 4)), block(256);
     TimedLaunch tl(SPKV_KERNEL_MERGE, st);
-    if (d == 128) tl.launch(merge_kernel<128>, grid, block, 0, a, out, lse, fr, fp);
-    else tl.launch(merge_kernel<64>, grid, block, 0, a, out, lse, fr, fp);
+    AppendSlots ap{};
+    if (append_slots) {
+        for (int i = 0; i < fr.nreq; ++i) ap.slots[i] = append_slots[fr.b0 + i];
+        grid.x += (unsigned)((fr.nreq + 3) / 4);   // the new-token waves
+        if (d == 128) tl.launch(merge_kernel<128, true>, grid, block, 0, a, out, lse, fr, fp, ap);
+        else tl.launch(merge_kernel<64, true>, grid, block, 0, a, out, lse, fr, fp, ap);
+    } else {
+        if (d == 128) tl.launch(merge_kernel<128>, grid, block, 0, a, out, lse, fr, fp, ap);
+        else tl.launch(merge_kernel<64>, grid, block, 0, a, out, lse, fr, fp, ap);
+    }
     return check_launch("merge_kernel");
 }
 
@@ -1567,8 +1646,15 @@ Args make_args(const spkv_batch *b, const spkv_kv *kv, const Plan &p, void *ws) 
     return a;
 }
 
+// The step's new tokens, in append mode (spkv_decode_step_append).
+struct AppendIn {
+    const void *k_new;
+    const void *v_new;
+    const int32_t *slots;   // host [B]
+};
+
 spkv_status run_decode(const spkv_batch *b, const spkv_kv *kv, const int32_t *cascade, float *out, float *lse,
-                       void *ws, size_t ws_bytes, void *stream) {
+                       void *ws, size_t ws_bytes, void *stream, const AppendIn *app = nullptr) {
     spkv_status st = spkv::validate_batch(b, kv);
     if (st != SPKV_OK) return st;
     if (!kv) return fail(SPKV_E_INVAL, "null kv");
@@ -1580,6 +1666,11 @@ spkv_status run_decode(const spkv_batch *b, const spkv_kv *kv, const int32_t *ca
     if (!ws || ws_bytes < (size_t)p.ws_bytes)
         return fail(SPKV_E_INVAL, "workspace too small: need " + std::to_string(p.ws_bytes) + " bytes");
     Args a = make_args(b, kv, p, ws);
+    if (app) {
+        a.append = 1;
+        a.k_new = app->k_new;
+        a.v_new = app->v_new;
+    }
     hipStream_t hs = (hipStream_t)stream;
     const bool bf16 = b->dtype == SPKV_DTYPE_BF16;
     // The paged (HBM-bound) pass runs first, the prefix contraction (MFMA-
@@ -1601,7 +1692,8 @@ spkv_status run_decode(const spkv_batch *b, const spkv_kv *kv, const int32_t *ca
     }
     static const FlatLaunch kNone{};
     for (size_t i = 0; i < p.flat.size(); ++i) {
-        st = launch_merge(a, b->head_dim, out, lse, p.flat[i], p.prefix_as_flat && p.run_prefix ? p.pflat[i] : kNone, hs);
+        st = launch_merge(a, b->head_dim, out, lse, p.flat[i], p.prefix_as_flat && p.run_prefix ? p.pflat[i] : kNone,
+                          app ? app->slots : nullptr, hs);
         if (st != SPKV_OK) return st;
     }
     return SPKV_OK;
@@ -1735,6 +1827,36 @@ spkv_status spkv_decode_step(const spkv_batch *batch, const spkv_kv *kv, const s
     if (cascade_out)
         for (int g = 0; g < batch->num_groups; ++g) cascade_out[g] = choice[(size_t)g];
     return run_decode(batch, kv, choice.data(), out, lse, ws, ws_bytes, stream);
+}
+
+spkv_status spkv_decode_step_append(const spkv_batch *batch, const spkv_kv *kv, const spkv_dispatch_params *params,
+                                    const void *k_new, const void *v_new, const int32_t *host_slots, float *out,
+                                    float *lse, void *ws, size_t ws_bytes, void *stream, int32_t *cascade_out) {
+    spkv_status st = spkv::validate_batch(batch, kv);
+    if (st != SPKV_OK) return st;
+    if (!kv) return fail(SPKV_E_INVAL, "null kv");
+    if (batch->dtype != SPKV_DTYPE_BF16) return fail(SPKV_E_INVAL, "decode_step_append: bf16 only");
+    if (batch->batch > 0 && (!k_new || !v_new || !host_slots || !batch->host_cold_lens))
+        return fail(SPKV_E_INVAL, "decode_step_append: null new-token argument");
+    if (kv->cold_slots * (int64_t)batch->num_kv_heads >= ((int64_t)1 << 30))
+        return fail(SPKV_E_INVAL, "decode_step_append: COLD pool too large (Hkv * cold_slots >= 2^30)");
+    for (int i = 0; i < batch->batch; ++i) {
+        const int64_t slot = host_slots[i];
+        const int64_t len = batch->host_cold_lens[i];
+        if (slot < 0 || slot >= kv->cold_slots)
+            return fail(SPKV_E_INVAL, "decode_step_append: slot " + std::to_string(slot) + " of request " +
+                                          std::to_string(i) + " outside the COLD pool");
+        if (len < 1 || (len - 1) / batch->page_size >= batch->max_blocks)
+            return fail(SPKV_E_INVAL, "decode_step_append: no block-table column for the new token of request " +
+                                          std::to_string(i));
+    }
+    std::vector<int32_t> choice((size_t)std::max(1, batch->num_groups), 0);
+    st = spkv_dispatch(batch, params, choice.data());
+    if (st != SPKV_OK) return st;
+    if (cascade_out)
+        for (int g = 0; g < batch->num_groups; ++g) cascade_out[g] = choice[(size_t)g];
+    const AppendIn app{k_new, v_new, host_slots};
+    return run_decode(batch, kv, choice.data(), out, lse, ws, ws_bytes, stream, &app);
 }
 
 spkv_status spkv_merge_states(const float *o_a, const float *lse_a, const float *o_b, const float *lse_b, float *o,

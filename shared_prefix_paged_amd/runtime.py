@@ -380,6 +380,21 @@ def decode_step(batch: DecodeBatch, kv: KVPools, params: A.spkv_dispatch_params,
     return out, lse, choice[:batch.num_groups]
 
 
+def decode_step_append(batch: DecodeBatch, kv: KVPools, params: A.spkv_dispatch_params, ws, k_new, v_new,
+                       slots: np.ndarray, out=None, lse=None, stream=None):
+    """spkv_decode_step_append: the step's appends (one token per request,
+    K/V rows [B, Hkv, d] on the device, host slots [B]) fused into the decode
+    step.  batch.lens_h must already count the new token; the device lengths
+    and block tables must not (the call advances them)."""
+    out, lse = _outputs(batch, out, lse)
+    choice = np.zeros(max(batch.num_groups, 1), np.int32)
+    slots = np.ascontiguousarray(slots, dtype=np.int32)
+    check(lib.spkv_decode_step_append(C.byref(batch.struct), C.byref(kv.struct), C.byref(params), _dp(k_new),
+                                      _dp(v_new), _ptr(slots, C.c_int32), _dp(out), _dp(lse), _dp(ws), ws.numel(),
+                                      stream_handle(stream), _ptr(choice, C.c_int32)))
+    return out, lse, choice[:batch.num_groups]
+
+
 def merge_states(o_a, lse_a, o_b, lse_b, out=None, lse=None, stream=None):
     torch = _torch()
     rows, d = o_a.shape
