@@ -545,6 +545,11 @@ __device__ __forceinline__ float sum_of_groups(float v) {
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
+// APP (append mode): request b's new token, the last of its [HOT ; COLD]
+// tokens, is not in the pools yet (the merge launch lands it).  The piece that
+// ends with it loads the head's K/V rows of the token from k_new / v_new at
+// its start and, once its last stage has landed, writes them over the token's
+// row of that stage in LDS (the token's DMA lanes fetched a placeholder row).
 template <int D, int G, bool APP>
 __device__ __forceinline__ void attend_range_mfma(const Args &a, const Req &r, int b, int h, int t0, int t1,
                                                   int slot, int lane, char *ring, uint32_t ring_off) {
@@ -561,8 +566,6 @@ __device__ __forceinline__ void attend_range_mfma(const Args &a, const Req &r, i
     const char *vhot = (const char *)a.v_hot;
     const char *kcold = (const char *)a.k_cold;
     const char *vcold = (const char *)a.v_cold;
-    const int64_t knew_from_cold = APP ? (int64_t)((uintptr_t)a.k_new - (uintptr_t)a.k_cold) : 0;
-    const int64_t vnew_from_cold = APP ? (int64_t)((uintptr_t)a.v_new - (uintptr_t)a.v_cold) : 0;
     const int32_t *table = a.tables + (int64_t)b * a.max_blocks;
     const int64_t num_pages = a.cold_slots / a.page_size;
     const uint32_t hot_row0 = (uint32_t)(r.base * a.Hkv + (int64_t)h * r.lp);
@@ -574,11 +577,10 @@ __device__ __forceinline__ void attend_range_mfma(const Args &a, const Req &r, i
     auto lane_token = [&](int nb) { return min(t0 + 64 * nb + lane, t1 - 1); };
     auto first_entry = [&](int nb) { return (max(t0 + 64 * nb, r.lp) - r.lp) / a.page_size; };
     auto block_has_cold = [&](int nb) { return t0 + 64 * nb < t1 && t0 + 64 * nb + 63 >= r.lp; };
-    // Row codes: bit 31 HOT slab row; else, in append mode, bit 30 marks the
-    // new token (row b * Hkv + h of k_new / v_new); else a COLD slot row.
+    // Row codes: bit 31 HOT slab row, else a COLD slot row.
     auto code_of = [&](int t, int32_t entry) -> uint32_t {
         if (t < r.lp) return 0x80000000u | (hot_row0 + (uint32_t)t);
-        if (APP && t == r.lp + r.ls - 1) return 0x40000000u | (uint32_t)(b * a.Hkv + h);
+        if (APP && t == r.lp + r.ls - 1) return (uint32_t)h;   // placeholder: slot 0, replaced in LDS
         int64_t page = entry;
         page = page < 0 ? 0 : (page >= num_pages ? num_pages - 1 : page);
         return (uint32_t)((page * a.page_size + (t - r.lp) % a.page_size) * a.Hkv + h);
@@ -612,6 +614,16 @@ __device__ __forceinline__ void attend_range_mfma(const Args &a, const Req &r, i
         int32_t entry = 0;
         if (t >= r.lp) entry = table[max(0, min((t - r.lp) / a.page_size, a.max_blocks - 1))];
         code = code_of(t, entry);
+    }
+    // The new token's K/V rows of this head: lane c < CPR holds 16-byte chunk c.
+    const bool lands = APP && t1 == r.lp + r.ls;   // this piece ends with the new token
+    u32x4_t new_k = {0, 0, 0, 0}, new_v = {0, 0, 0, 0};
+    if constexpr (APP) {
+        if (lands && lane < F::CPR) {
+            const int64_t src = ((int64_t)b * a.Hkv + h) * F::CPR + lane;
+            new_k = ((const u32x4_t *)a.k_new)[src];
+            new_v = ((const u32x4_t *)a.v_new)[src];
+        }
     }
 #pragma unroll
     for (int s = 0; s < KS; ++s) asm volatile("" ::"v"(__builtin_bit_cast(u32x4_t, qb[s])));
@@ -648,19 +660,9 @@ __device__ __forceinline__ void attend_range_mfma(const Args &a, const Req &r, i
             const int ti = (j % SPB) * TOK + F::RPI * i + lane / F::CPR;   // token inside its 64-block
             const uint32_t c = (uint32_t)__shfl((int)code, ti, 64);
             const bool hot = c >> 31;
-            // the new token: its row of k_new / v_new, reached from the COLD
-            // base by a per-lane distance (selects, no divergent branch)
-            if constexpr (APP) {   // per-lane selects, no branch: one copy of the issue code
-                const bool nw = !hot & (((c >> 30) & 1u) != 0u);
-                const int64_t off = (int64_t)(c & (hot ? 0x7fffffffu : 0x3fffffffu)) * F::ROWB;
-                const int64_t kd = nw ? knew_from_cold : 0, vd = nw ? vnew_from_cold : 0;
-                dma16_at((hot ? khot : kcold) + off + kd + ksrc[i], dst + 1024u * i);
-                dma16_at((hot ? vhot : vcold) + off + vd + vsrc[i], dst + F::OPB + 1024u * i);
-            } else {
-                const int64_t off = (int64_t)(c & 0x7fffffffu) * F::ROWB;
-                dma16_at((hot ? khot : kcold) + off + ksrc[i], dst + 1024u * i);
-                dma16_at((hot ? vhot : vcold) + off + vsrc[i], dst + F::OPB + 1024u * i);
-            }
+            const int64_t off = (int64_t)(c & 0x7fffffffu) * F::ROWB;
+            dma16_at((hot ? khot : kcold) + off + ksrc[i], dst + 1024u * i);
+            dma16_at((hot ? vhot : vcold) + off + vsrc[i], dst + F::OPB + 1024u * i);
         }
     };
 
@@ -742,6 +744,15 @@ __device__ __forceinline__ void attend_range_mfma(const Args &a, const Req &r, i
             } else {
                 wait_vm_lds<0>();
             }
+            if (APP && lands && j == n_st - 1 && lane < F::CPR) {
+                // the last stage has landed (every DMA waited for): the new
+                // token's row, at its swizzled chunk positions, over the placeholder
+                typedef u32x4_t __attribute__((address_space(3))) *lds_u32x4_ptr;
+                const int rn = (t1 - 1) - t0 - j * TOK;
+                const uint32_t row = ring_off + (uint32_t)(st * F::STAGEB + rn * F::ROWB);
+                *(lds_u32x4_ptr)(uintptr_t)(row + (kswz<D>(rn, lane) << 4)) = new_k;
+                *(lds_u32x4_ptr)(uintptr_t)(row + F::OPB + (vswz<D>(rn, lane) << 4)) = new_v;
+            }
             compute(j, st);
         }
     }
@@ -761,6 +772,12 @@ __device__ __forceinline__ void attend_range_mfma(const Args &a, const Req &r, i
         if (q == 0) a.lse_part[prow] = lt > 0.f ? m_run + __log2f(lt) : -INFINITY;
     }
 }
+
+// The step's new COLD slots of one sub-batch (append mode): slot of request
+// b0 + i.  Checked on the host (in range, room in the block table).
+struct AppendSlots {
+    int32_t slots[spkv::kFlatArgReqs];
+};
 
 // Occupancy, float32: 4 waves per SIMD (<= 128 VGPRs) up to G = 6, 3 above;
 // the LDS ring (4 x 8.25 KB per block of 4 waves) admits 4 blocks per CU.
@@ -1180,12 +1197,6 @@ __global__ __launch_bounds__(64 * W * KH) void prefix_mfma_kernel(Args a) {
 // holds partial k's weight exp2(lse_k - max); then each wave-wide load brings
 // PPW partial rows (LPP lanes x 16 bytes each), several loads in flight.
 // ---------------------------------------------------------------------------
-// The step's new COLD slots of one sub-batch (append mode): slot of request
-// fr.b0 + i.  Checked on the host (in range, room in the block table).
-struct AppendSlots {
-    int32_t slots[spkv::kFlatArgReqs];
-};
-
 // APPEND: the merge launch also lands the step's new tokens, which the paged
 // pass read from k_new / v_new: every reader of the pools, block tables and
 // lengths has finished by now (same stream), so extra blocks copy each
@@ -1515,12 +1526,12 @@ spkv_status check_launch(const char *what) {
 // Dynamic LDS above 64 KB is granted per kernel once its limit is raised.
 template <bool BF16, int D, int G>
 spkv_status launch_flat_g(const Args &a, int part, const FlatLaunch &f, dim3 grid, dim3 block, size_t lds,
-                          TimedLaunch &tl) {
+                          const int32_t *append_slots, TimedLaunch &tl) {
     static const hipError_t attr = hipFuncSetAttribute((const void *)flat_kernel<BF16, D, G>,
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, spkv::kLdsPerCU);
     if (attr != hipSuccess) return fail(SPKV_E_HIP, std::string("flat_kernel LDS limit: ") + hipGetErrorString(attr));
     if constexpr (BF16) {
-        if (a.append) {   // the step's new tokens come from k_new / v_new
+        if (append_slots) {   // append mode: the step's new tokens come from k_new / v_new
             static const hipError_t attr2 = hipFuncSetAttribute(
                 (const void *)flat_kernel<BF16, D, G, true>, hipFuncAttributeMaxDynamicSharedMemorySize, spkv::kLdsPerCU);
             if (attr2 != hipSuccess)
@@ -1534,31 +1545,32 @@ spkv_status launch_flat_g(const Args &a, int part, const FlatLaunch &f, dim3 gri
 }
 
 template <bool BF16, int D>
-spkv_status launch_flat_d(const Args &a, int part, const FlatLaunch &f, int head_groups, hipStream_t st) {
+spkv_status launch_flat_d(const Args &a, int part, const FlatLaunch &f, int head_groups,
+                          const int32_t *append_slots, hipStream_t st) {
     const int waves = a.Hkv < kFlatWavesMax ? a.Hkv : kFlatWavesMax;
     dim3 grid(f.blocks, head_groups), block(64 * waves);
     const size_t lds = (size_t)waves * (BF16 ? FlatMfmaGeom<D>::WAVEB : FlatGeom<BF16, D>::WAVEB);
     TimedLaunch tl(SPKV_KERNEL_FLAT, st);
     switch (a.G) {
-    case 1: return launch_flat_g<BF16, D, 1>(a, part, f, grid, block, lds, tl);
-    case 2: return launch_flat_g<BF16, D, 2>(a, part, f, grid, block, lds, tl);
-    case 3: return launch_flat_g<BF16, D, 3>(a, part, f, grid, block, lds, tl);
-    case 4: return launch_flat_g<BF16, D, 4>(a, part, f, grid, block, lds, tl);
-    case 5: return launch_flat_g<BF16, D, 5>(a, part, f, grid, block, lds, tl);
-    case 6: return launch_flat_g<BF16, D, 6>(a, part, f, grid, block, lds, tl);
-    case 7: return launch_flat_g<BF16, D, 7>(a, part, f, grid, block, lds, tl);
-    case 8: return launch_flat_g<BF16, D, 8>(a, part, f, grid, block, lds, tl);
+    case 1: return launch_flat_g<BF16, D, 1>(a, part, f, grid, block, lds, append_slots, tl);
+    case 2: return launch_flat_g<BF16, D, 2>(a, part, f, grid, block, lds, append_slots, tl);
+    case 3: return launch_flat_g<BF16, D, 3>(a, part, f, grid, block, lds, append_slots, tl);
+    case 4: return launch_flat_g<BF16, D, 4>(a, part, f, grid, block, lds, append_slots, tl);
+    case 5: return launch_flat_g<BF16, D, 5>(a, part, f, grid, block, lds, append_slots, tl);
+    case 6: return launch_flat_g<BF16, D, 6>(a, part, f, grid, block, lds, append_slots, tl);
+    case 7: return launch_flat_g<BF16, D, 7>(a, part, f, grid, block, lds, append_slots, tl);
+    case 8: return launch_flat_g<BF16, D, 8>(a, part, f, grid, block, lds, append_slots, tl);
     default: return fail(SPKV_E_INVAL, "unsupported GQA group size");
     }
 }
 
 spkv_status launch_flat(const Args &a, bool bf16, int d, int part, const FlatLaunch &f, int head_groups,
-                        hipStream_t st) {
+                        const int32_t *append_slots, hipStream_t st) {
     if (f.blocks <= 0 || a.B == 0) return SPKV_OK;
-    if (bf16) return d == 128 ? launch_flat_d<true, 128>(a, part, f, head_groups, st)
-                              : launch_flat_d<true, 64>(a, part, f, head_groups, st);
-    return d == 128 ? launch_flat_d<false, 128>(a, part, f, head_groups, st)
-                    : launch_flat_d<false, 64>(a, part, f, head_groups, st);
+    if (bf16) return d == 128 ? launch_flat_d<true, 128>(a, part, f, head_groups, append_slots, st)
+                              : launch_flat_d<true, 64>(a, part, f, head_groups, append_slots, st);
+    return d == 128 ? launch_flat_d<false, 128>(a, part, f, head_groups, nullptr, st)
+                    : launch_flat_d<false, 64>(a, part, f, head_groups, nullptr, st);
 }
 
 spkv_status launch_prefix(const Args &a, const Plan &p, int d, hipStream_t st) {
@@ -1680,10 +1692,11 @@ spkv_status run_decode(const spkv_batch *b, const spkv_kv *kv, const int32_t *ca
     // both paged passes.
     for (size_t i = 0; i < p.flat.size(); ++i) {
         if (p.run_prefix && !bf16) {
-            st = launch_flat(a, false, b->head_dim, kPartPrefix, p.pflat[i], p.flat_head_groups, hs);
+            st = launch_flat(a, false, b->head_dim, kPartPrefix, p.pflat[i], p.flat_head_groups, nullptr, hs);
             if (st != SPKV_OK) return st;
         }
-        st = launch_flat(a, bf16, b->head_dim, kPartRest, p.flat[i], p.flat_head_groups, hs);
+        st = launch_flat(a, bf16, b->head_dim, kPartRest, p.flat[i], p.flat_head_groups, app ? app->slots : nullptr,
+                         hs);
         if (st != SPKV_OK) return st;
     }
     if (p.run_prefix && bf16) {
