@@ -76,7 +76,7 @@ class GpuMultiStep:
                             torch.from_numpy(np.asarray(slots, np.int32)).to(self.dev), self.pools.k_cold,
                             self.pools.v_cold, self.pools.cold_slots, cfg.num_kv_heads, cfg.head_dim)
 
-    def step(self, k_new, v_new):
+    def step(self, k_new, v_new, write=True):
         s = self.step_index
         cfg = self.wl.cfg
         if s == self.fork_step:
@@ -103,7 +103,8 @@ class GpuMultiStep:
         if cows:
             R.copy_blocks(torch.tensor(cows, dtype=torch.int32, device=self.dev), self.pools.k_cold,
                           self.pools.v_cold, self.wl.num_cold_pages, self.P, cfg.num_kv_heads, cfg.head_dim)
-        self.write(k_new, v_new, slots)
+        if write:
+            self.write(k_new, v_new, slots)
         self.step_index += 1
         return live, np.asarray(slots), [tuple(c) for c in cows]
 
@@ -116,7 +117,12 @@ class GpuMultiStep:
                              tables, lens, self.P, self.wl.cfg.num_kv_heads), tables, lens
 
 
-def run(wl, P, check_rows, modes=(A.SPKV_MODE_PER_GROUP, A.SPKV_MODE_BATCH_GLOBAL), steps=32, seed=5):
+def run(wl, P, check_rows, modes=(A.SPKV_MODE_PER_GROUP, A.SPKV_MODE_BATCH_GLOBAL), steps=32, seed=5,
+        fused=False):
+    """fused: the step's tokens are not written beforehand; every attention
+    call is spkv_decode_step_append from the pre-append device lengths (the
+    block-table entry it writes is already the allocator's, so rewriting it,
+    and landing the same token again for the next mode, changes nothing)."""
     sim = MultiStepSim(wl, page_size=P)
     gpu = GpuMultiStep(wl, P)
     rng = np.random.default_rng(seed)
@@ -127,7 +133,7 @@ def run(wl, P, check_rows, modes=(A.SPKV_MODE_PER_GROUP, A.SPKV_MODE_BATCH_GLOBA
             n_live -= len(sim.fork_parents)
         dr = W.step_draws(wl.cfg, s, n_live)
         rec = sim.step(dr.k_new, dr.v_new)
-        live, slots, cows = gpu.step(dr.k_new, dr.v_new)
+        live, slots, cows = gpu.step(dr.k_new, dr.v_new, write=not fused)
         assert live == rec.live, f"step {s}: live sets differ"
         np.testing.assert_array_equal(slots, np.asarray(rec.slots), err_msg=f"step {s} slots")
         assert cows == [tuple(c) for c in rec.cows], f"step {s} copy-on-write pairs"
@@ -141,8 +147,16 @@ def run(wl, P, check_rows, modes=(A.SPKV_MODE_PER_GROUP, A.SPKV_MODE_BATCH_GLOBA
         for mode in modes:
             out = torch.empty((len(live), wl.cfg.num_q_heads, wl.cfg.head_dim), dtype=torch.float32, device=gpu.dev)
             lse = torch.empty((len(live), wl.cfg.num_q_heads), dtype=torch.float32, device=gpu.dev)
-            _, _, choice = R.decode_step(batch, gpu.pools, R.default_params(mode), ws, out, lse)
+            if fused:
+                batch.lens -= 1                                  # the device view before the append
+                k_new, v_new = (to_device(x, wl.cfg.dtype, gpu.dev) for x in (dr.k_new, dr.v_new))
+                _, _, choice = R.decode_step_append(batch, gpu.pools, R.default_params(mode), ws, k_new, v_new,
+                                                    slots, out, lse)
+            else:
+                _, _, choice = R.decode_step(batch, gpu.pools, R.default_params(mode), ws, out, lse)
             torch.cuda.synchronize()
+            if fused:
+                np.testing.assert_array_equal(batch.lens.cpu().numpy(), lens, err_msg=f"step {s} device lengths")
             choices_seen[mode].add(tuple(int(c) for c in choice))
             e_o, e_l, rel = errors(out, lse, ref_o, ref_l, rows=rows)
             assert e_o <= TOL_O and e_l <= TOL_L and rel <= TOL_REL, \
@@ -175,6 +189,13 @@ def small_workload(seed=21):
 def test_multistep_small_all_rows(P):
     note(f"[gpu] multistep small P={P}")
     run(small_workload(), P, lambda n, rng: list(range(n)))
+
+
+@pytest.mark.parametrize("P", [1, 16])
+def test_multistep_small_fused_appends(P):
+    # forks, releases and copy-on-write with the appends fused into the step
+    note(f"[gpu] multistep small fused P={P}")
+    run(small_workload(), P, lambda n, rng: list(range(n)), fused=True)
 
 
 @pytest.mark.timeout(600)
