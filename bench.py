@@ -63,6 +63,9 @@ def parse():
                     help="append the step's K/V with its own launch (spkv_append_tokens) before the decode step")
     ap.add_argument("--layers", type=int, default=1,
                     help="with L > 1: a decode step over L layers (per-layer pools, shared slots); own JSON line")
+    ap.add_argument("--admission-sweep", default=None, metavar="F1,F2,...",
+                    help="time the multi-agent batch with the HOT pool at each fraction of the total prefix "
+                         "length (groups that do not fit fall back to COLD) and exit")
     ap.add_argument("--layout-study", action="store_true",
                     help="time the prefix storage layouts (HOT slab cascade / HOT slab flat / private COLD copies) and exit")
     ap.add_argument("--layout-batch", type=int, default=256, help="requests sharing the prefix in --layout-study")
@@ -362,6 +365,92 @@ def multi_layer(args) -> int:
     return 0
 
 
+def admission_sweep(args) -> int:
+    """HOT admission under pressure, at the multi-agent shape (8 prefix groups
+    x 16 requests, Lp_g ~ U[2048, 16384], Ls ~ U[128, 4096], the Llama-3.1-8B
+    layer): the HOT pool holds a fraction f of the groups' total prefix
+    length; groups are admitted first fit in group order, and a group that
+    does not fit keeps its prefix in every member's own COLD pages (the COLD
+    fallback) and takes the flat pass.  Per f: groups admitted, prefix bytes
+    stored, attention time per step (per-group dispatch, warm), KV tokens/s.
+    One JSON line.  Timing only: pool contents are random on the device."""
+    import numpy as np
+    import torch
+    import workloads as W
+    from shared_prefix_paged_amd import runtime as R
+    from shared_prefix_paged_amd import _abi as A
+    from shared_prefix_paged_amd import OutOfMemory
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    cfg = W.CONFIGS["C4"]
+    B, Hq, Hkv, d, ng = cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.num_groups
+    kvb = 2 * Hkv * d * 2
+    rng = np.random.Generator(np.random.PCG64(cfg.seed))    # the recipe's first draws: prefix, then suffix lengths
+    lp = rng.integers(*cfg.prefix_range, size=ng, endpoint=True).astype(np.int64)
+    ls = rng.integers(*cfg.suffix_range, size=B, endpoint=True).astype(np.int64)
+    gof0 = np.minimum(np.arange(B) // (B // ng), ng - 1)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(107)
+    q = torch.randn((B, Hq, d), generator=gen, device=dev).to(torch.bfloat16)
+    params = R.default_params(A.SPKV_MODE_PER_GROUP)
+    rows = []
+    for f in [float(x) for x in args.admission_sweep.split(",")]:
+        cap = int(f * int(lp.sum()))
+        hot = R.HotPool(max(cap, 1))
+        bases = {}
+        for g in range(ng):
+            try:
+                bases[g] = hot.alloc(int(lp[g]))
+            except OutOfMemory:
+                pass                                         # COLD fallback for this group
+        admitted = sorted(bases)
+        gid = {g: i for i, g in enumerate(admitted)}
+        group_of = [gid.get(int(g), -1) for g in gof0]
+        lengths = np.array([ls[b] + (0 if int(gof0[b]) in bases else lp[gof0[b]]) for b in range(B)], np.int64)
+        pages = int(lengths.sum()) + 32 * B
+        cp = R.ColdPool(pages, 1, rng.permutation(pages).astype(np.int32))
+        seqs = [cp.seq_new() for _ in range(B)]
+        for t in range(int(lengths.max())):
+            cp.append_batch([sq for sq, n in zip(seqs, lengths) if n > t])
+        tables, lens = cp.block_tables(seqs, int(lengths.max()))
+        pools = R.KVPools.allocate(max(cap, 1), pages, Hkv, d, torch.bfloat16, dev)
+        for t in (pools.k_hot, pools.v_hot, pools.k_cold, pools.v_cold):
+            t.normal_(generator=gen)
+        batch = R.DecodeBatch(q, group_of, [bases[g] for g in admitted], [int(lp[g]) for g in admitted], tables,
+                              lens, 1, Hkv)
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+        ws = torch.empty(batch.workspace_size(), dtype=torch.uint8, device=dev)
+        quiet_gc()
+        for _ in range(3):
+            _, _, choice = R.decode_step(batch, pools, params, ws, out, lse)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            R.decode_step(batch, pools, params, ws, out, lse)
+        e1.record()
+        torch.cuda.synchronize()
+        us = 1e3 * e0.elapsed_time(e1) / args.steps
+        assert torch.isfinite(out).all()
+        tokens = int(lengths.sum() + sum(lp[g] for g in gof0 if int(g) in bases))
+        rec = {"hot_fraction": f, "groups_admitted": len(admitted), "groups_cascade": int(np.sum(choice)),
+               "hot_prefix_bytes": int(sum(lp[g] for g in admitted) * kvb),
+               "private_prefix_bytes": int(sum(lp[gof0[b]] for b in range(B) if int(gof0[b]) not in bases) * kvb),
+               "attention_us": round(us, 2), "kv_tokens_per_s": round(tokens / (us * 1e-6), 1)}
+        print(f"[admission] {json.dumps(rec)}", file=sys.stderr, flush=True)
+        rows.append(rec)
+        del batch, pools, ws, out, lse, cp, hot
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "attention time per step by HOT pool size (COLD fallback for groups that do not fit)",
+                      "unit": "us", "config": {"workload": f"{cfg.name} lengths: B={B}, {ng} groups, Hq={Hq}, "
+                                                           f"Hkv={Hkv}, d={d}, bf16, shuffled P = 1 slots",
+                                               "prefix_lengths": [int(x) for x in lp], "steps": args.steps},
+                      "rows": rows}), flush=True)
+    return 0
+
+
 def source_digest() -> str:
     """Digest of the sources that decide what the kernels read and write."""
     import hashlib
@@ -401,6 +490,8 @@ def main():
         return layout_study(args)
     if args.layers > 1:
         return multi_layer(args)
+    if args.admission_sweep:
+        return admission_sweep(args)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
               "this build has no multi-GPU path.", file=sys.stderr)
