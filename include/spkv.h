@@ -349,7 +349,8 @@ spkv_status spkv_decode_step_append(const spkv_batch *batch, const spkv_kv *kv,
  * Plan inspection and kernel timing (measurement support).
  * ==================================================================== */
 typedef struct spkv_plan_info {
-    int32_t flat_chunk;            /* tokens per range of the paged pass (stream-K; largest sub-batch) */
+    int32_t flat_chunk;            /* virtual tokens per range of the paged pass (stream-K; largest
+                                      sub-batch; flat_head_tokens count before each non-empty request) */
     int32_t flat_splits;           /* max paged-pass partials of one request (<= flat_split_cap) */
     int32_t prefix_chunk;          /* base keys per prefix work item (bf16 MFMA pass) */
     int32_t prefix_splits;         /* max prefix partials per row */
@@ -359,7 +360,8 @@ typedef struct spkv_plan_info {
     int64_t prefix_items;          /* non-empty prefix work items */
     int64_t workspace_bytes;       /* bytes this plan uses */
     int32_t flat_split_cap;        /* bound on the paged-pass partials of one request */
-    int32_t flat_granule;          /* reserved (0) */
+    int32_t flat_head_tokens;      /* start cost of one (range, request) piece in tokens: ranges are cut
+                                      with this many virtual tokens before each non-empty request */
     int32_t prefix_split_cap;      /* per group: chunk = roundup(max(prefix_chunk, ceil(Lp / cap)), granule) */
     int32_t prefix_granule;
     int32_t prefix_key_halves;     /* 2: each prefix work item's key chunk is split over two wave sets whose

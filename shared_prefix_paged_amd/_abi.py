@@ -47,7 +47,7 @@ class spkv_plan_info(C.Structure):
     _fields_ = [("flat_chunk", c_i32), ("flat_splits", c_i32), ("prefix_chunk", c_i32), ("prefix_splits", c_i32),
                 ("prefix_waves", c_i32), ("prefix_mtiles", c_i32), ("flat_items", c_i64),
                 ("prefix_items", c_i64), ("workspace_bytes", c_i64), ("flat_split_cap", c_i32),
-                ("flat_granule", c_i32), ("prefix_split_cap", c_i32), ("prefix_granule", c_i32),
+                ("flat_head_tokens", c_i32), ("prefix_split_cap", c_i32), ("prefix_granule", c_i32),
                 ("prefix_key_halves", c_i32)]
 
 

@@ -29,6 +29,11 @@ constexpr int kPrefixSplitCap = 64;    // partials per row from the prefix pass
 constexpr int kPrefixKeyTile = 32;     // keys per MFMA tile in the prefix kernel
 constexpr int kFlatWaves = 4;          // KV heads (one wave each) per flat block
 constexpr int kFlatMinTokens = 64;     // shortest flat range per block
+// Start cost of one (range, request) piece of the paged pass, in tokens: the
+// ranges are cut with this many virtual tokens before each non-empty request,
+// so a range that crosses request boundaries gets fewer real tokens (a new
+// piece waits for its geometry, block-table and first ring fill).
+constexpr int kFlatHeadTokens = 48;
 constexpr int kFlatWaveSlots = 16;     // resident flat waves per CU (128 VGPRs), float32 pass
 constexpr int kFlatMfmaTokens = 16;    // tokens per ring stage of the bf16 (MFMA) paged pass
 constexpr int kFlatMfmaStages = 4;     // ring stages per wave of the bf16 paged pass
@@ -44,7 +49,9 @@ struct GroupMask {
 // kFlatArgReqs requests.  Its tokens - every request's range of
 // [HOT prefix ; COLD suffix] concatenated in request order - are cut into
 // `blocks` equal ranges per group of up to kFlatWaves KV heads (stream-K), so
-// every block carries the same number of tokens whatever the request lengths.
+// every block carries the same work whatever the request lengths: the cut is
+// made in virtual tokens, kFlatHeadTokens of them before each non-empty
+// request, so each piece's start cost counts against its range.
 // Passed by value as a kernel argument: blocks find their requests with a few
 // scalar loads and no index pass.
 constexpr int kFlatArgReqs = 256;
@@ -53,11 +60,14 @@ struct FlatLaunch {
     int32_t nreq;                      // requests in it
     int32_t blocks;                    // ranges per head group (grid x)
     int32_t max_parts;                 // bound on partial states per request
-    int64_t total;                     // tokens of the sub-batch
-    int32_t offs[kFlatArgReqs + 1];    // exclusive prefix sums of the request lengths
+    int64_t total;                     // virtual tokens of the sub-batch
+    int32_t head;                      // virtual tokens before each non-empty request
+    int32_t offs[kFlatArgReqs + 1];    // exclusive prefix sums of the virtual request lengths
+                                       // (head + length, 0 for an empty request); request i's
+                                       // tokens are [offs[i] + head, offs[i + 1])
 };
 
-// Range (block) index containing token x when T tokens are cut into nb
+// Range (block) index containing virtual token x when T are cut into nb
 // ranges [floor(k*T/nb), floor((k+1)*T/nb)).
 SPKV_HD inline int range_of(int64_t x, int64_t T, int nb) {
     int k = (int)((x * nb) / T);
@@ -67,7 +77,7 @@ SPKV_HD inline int range_of(int64_t x, int64_t T, int nb) {
 
 // Partial states written for request i of a flat launch, and its first range.
 SPKV_HD inline int flat_parts(const FlatLaunch &f, int i, int *first) {
-    const int64_t o0 = f.offs[i], o1 = f.offs[i + 1];
+    const int64_t o0 = (int64_t)f.offs[i] + f.head, o1 = f.offs[i + 1];
     if (f.blocks <= 0 || o1 <= o0) {
         *first = 0;
         return 0;
@@ -81,7 +91,7 @@ SPKV_HD inline int flat_parts(const FlatLaunch &f, int i, int *first) {
 struct Plan {
     GroupMask cascade;        // bit g set: group g takes the prefix contraction
     int32_t num_groups;
-    int32_t flat_chunk;       // tokens per flat block (largest sub-batch)
+    int32_t flat_chunk;       // virtual tokens per flat range (largest sub-batch)
     int32_t flat_splits;      // partial slots per row reserved for the flat pass
     int32_t prefix_chunk;     // base tau for the prefix pass (multiple of kPrefixKeyTile)
     int32_t prefix_splits;    // grid x of the prefix kernel

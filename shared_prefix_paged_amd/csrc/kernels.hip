@@ -810,7 +810,7 @@ __global__ __launch_bounds__(256, (BF16 ? 2 : (G <= 6 ? 4 : 3))) void flat_kerne
     for (int j = 0; j < NQW; ++j) i += __popcll(__ballot(lane + 64 * j < fl.nreq && ends[j] <= s0));
     const int slot0 = part == kPartRest ? a.prefix_splits : 0;
     for (; i < fl.nreq; ++i) {
-        const int64_t o0 = fl.offs[i], o1 = fl.offs[i + 1];
+        const int64_t o0 = (int64_t)fl.offs[i] + fl.head, o1 = fl.offs[i + 1];
         if (o0 >= s1) break;
         const int64_t lo_s = s0 > o0 ? s0 : o0, hi_s = s1 < o1 ? s1 : o1;
         if (hi_s <= lo_s) continue;

@@ -90,10 +90,11 @@ spkv_status validate_batch(const spkv_batch *b, const spkv_kv *kv) {
 static inline bool mask_get(const GroupMask &m, int g) { return (m.bits[g >> 5] >> (g & 31)) & 1u; }
 
 // Stream-K launches of one paged pass over per-request lengths L (sub-batches
-// of at most kFlatArgReqs requests).  Each launch gets as many equal token
-// ranges per head group as one full round of resident blocks, no shorter than
-// kFlatMinTokens, and few enough that no request spans more than
-// kFlatSplitCap ranges.
+// of at most kFlatArgReqs requests).  Each launch gets as many equal ranges of
+// virtual tokens (kFlatHeadTokens before each non-empty request, then its
+// tokens) per head group as one full round of resident blocks, no more than
+// one per kFlatMinTokens real tokens, and few enough that no request spans
+// more than kFlatSplitCap ranges.
 static std::vector<FlatLaunch> plan_flat(const std::vector<int64_t> &L, int head_groups, int blocks_per_cu,
                                          int32_t num_cus) {
     std::vector<FlatLaunch> out;
@@ -103,11 +104,14 @@ static std::vector<FlatLaunch> plan_flat(const std::vector<int64_t> &L, int head
         FlatLaunch f{};
         f.b0 = b0;
         f.nreq = std::min(kFlatArgReqs, B - b0);
-        int64_t T = 0, max_len = 0;
+        int64_t T = 0, max_len = 0, real = 0;
+        f.head = kFlatHeadTokens;
         for (int i = 0; i < f.nreq; ++i) {
             f.offs[i] = (int32_t)T;
-            T += L[(size_t)(b0 + i)];
-            max_len = std::max<int64_t>(max_len, L[(size_t)(b0 + i)]);
+            const int64_t l = L[(size_t)(b0 + i)];
+            T += l > 0 ? l + f.head : 0;
+            real += l;
+            max_len = std::max<int64_t>(max_len, l);
         }
         f.offs[f.nreq] = (int32_t)T;
         f.total = T;
@@ -115,7 +119,7 @@ static std::vector<FlatLaunch> plan_flat(const std::vector<int64_t> &L, int head
             out.push_back(f);
             continue;
         }
-        int64_t nb = std::min<int64_t>(resident, (T + kFlatMinTokens - 1) / kFlatMinTokens);
+        int64_t nb = std::min<int64_t>(resident, (real + kFlatMinTokens - 1) / kFlatMinTokens);
         nb = std::max<int64_t>(nb, 1);
         auto parts = [&](int64_t n) { return (max_len + T / n - 1) / (T / n) + 1; };
         while (nb > 1 && parts(nb) > kFlatSplitCap) nb = std::max<int64_t>(1, nb * 3 / 4);
@@ -159,6 +163,8 @@ spkv_status make_plan(const spkv_batch *b, const int32_t *cascade, int32_t num_c
         }
         p->flat = plan_flat(L, p->flat_head_groups, flat_blocks_per_cu(bf16, D, hpb), num_cus);
     }
+    for (const auto &f : p->flat)
+        if (f.total >= (int64_t(1) << 31)) return fail(SPKV_E_INVAL, "a paged-pass sub-batch exceeds 2^31 tokens");
     p->flat_splits = 0;
     p->flat_chunk = 0;
     for (const auto &f : p->flat) {
@@ -214,6 +220,8 @@ spkv_status make_plan(const spkv_batch *b, const int32_t *cascade, int32_t num_c
             L[(size_t)i] = (g >= 0 && mask_get(p->cascade, g)) ? b->host_hot_len[g] : 0;
         }
         p->pflat = plan_flat(L, p->flat_head_groups, flat_blocks_per_cu(false, D, hpb), num_cus);
+        for (const auto &f : p->pflat)
+            if (f.total >= (int64_t(1) << 31)) return fail(SPKV_E_INVAL, "a paged-pass sub-batch exceeds 2^31 tokens");
         p->prefix_splits = 0;
         p->prefix_chunk = 0;
         for (const auto &f : p->pflat) {
@@ -291,7 +299,7 @@ spkv_status spkv_plan_query(const spkv_batch *batch, const int32_t *cascade, spk
     out->prefix_items = p.prefix_items;
     out->workspace_bytes = p.ws_bytes;
     out->flat_split_cap = kFlatSplitCap;
-    out->flat_granule = 0;
+    out->flat_head_tokens = kFlatHeadTokens;
     out->prefix_split_cap = kPrefixSplitCap;
     out->prefix_granule = kPrefixKeyTile;
     out->prefix_key_halves = p.prefix_key_halves;

@@ -1,8 +1,10 @@
 """Host planning of the paged pass (CPU only): the per-request partial-state
 counts reported by spkv_plan_parts equal those of the stream-K definition -
-a sub-batch's tokens, concatenated in request order, cut into `blocks` equal
-ranges [floor(k*T/n), floor((k+1)*T/n)), one partial per (range, request)
-overlap - recomputed here by brute force over token indices."""
+a sub-batch's tokens, concatenated in request order with `head` virtual
+tokens (owned by no request) before each non-empty request, cut into
+`blocks` equal ranges [floor(k*T/n), floor((k+1)*T/n)), one partial per
+(range, request) overlap of real tokens - recomputed here by brute force over
+token indices."""
 import numpy as np
 import pytest
 import torch
@@ -19,16 +21,30 @@ def batch_of(lens, groups, group_len, hkv=8, hq=32, d=128, page=1):
     return R.DecodeBatch(q, groups, bases, group_len, tables, lens, page, hkv)
 
 
-def brute_force_parts(L, nb):
-    """Partial count per request when sum(L) tokens are cut into nb equal ranges."""
-    T = int(np.sum(L))
-    owner = np.repeat(np.arange(len(L)), L)              # request of every token
+def brute_force_parts(L, nb, head=0):
+    """Partial count per request when the virtual token sequence (head
+    unowned tokens, then the request's own, for each non-empty request) is cut
+    into nb equal ranges."""
+    owner = [np.concatenate([np.full(head, -1), np.full(l, r)]) for r, l in enumerate(L) if l > 0]
+    owner = np.concatenate(owner).astype(np.int64) if owner else np.zeros(0, np.int64)
+    T = len(owner)
     parts = np.zeros(len(L), np.int64)
     for k in range(nb):
         lo, hi = (T * k) // nb, (T * (k + 1)) // nb
         for r in np.unique(owner[lo:hi]):
-            parts[r] += 1
+            if r >= 0:
+                parts[r] += 1
     return parts
+
+
+def test_brute_force_without_head_is_plain_stream_k():
+    # head = 0: equal ranges over the real tokens; a request of 10 tokens over
+    # ranges of 4 spans 3 or 4 of them depending on where it starts
+    assert list(brute_force_parts([10, 6], 4)) == [3, 2]
+    # head = 2: virtual sequence [-,-,0x10,-,-,1x6] of 20 cut into 4 ranges of 5
+    assert list(brute_force_parts([10, 6], 4, head=2)) == [3, 2]
+    # an empty request gets no head and no partial
+    assert list(brute_force_parts([3, 0, 3], 2, head=3)) == [1, 0, 1]
 
 
 @pytest.mark.parametrize("seed", [0, 1, 2])
@@ -49,7 +65,8 @@ def test_flat_parts_match_equal_range_definition(seed):
         head_groups = -(-8 // 4)
         nb = int(info.flat_items) // head_groups
         assert nb >= 1
-        np.testing.assert_array_equal(flat, brute_force_parts(L, nb))
+        assert info.flat_head_tokens >= 0
+        np.testing.assert_array_equal(flat, brute_force_parts(L, nb, info.flat_head_tokens))
         assert flat.max() <= info.flat_splits <= info.flat_split_cap
         for b in range(B):
             g = groups[b]
