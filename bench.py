@@ -763,8 +763,9 @@ def main():
 
 
 def cpu_baseline(wl, budget_s: float, threads=None):
-    """The oracle, untuned, on the host cores: fp64 attention per request until
-    the budget is spent.  threads=1 limits the BLAS pools to one thread."""
+    """The oracle, untuned, on the host cores: fp64 attention per request,
+    cycling over the workload's requests, until the budget is spent.
+    threads=1 limits the BLAS pools to one thread."""
     import contextlib
     from oracle.attention import decode_reference
     limit = contextlib.nullcontext()
@@ -779,15 +780,15 @@ def cpu_baseline(wl, budget_s: float, threads=None):
     done, tokens, t0 = 0, 0, time.perf_counter()
     order = list(range(wl.batch))
     with limit:
-        while done < len(order) and time.perf_counter() - t0 < budget_s:
-            b = order[done]
+        while done == 0 or time.perf_counter() - t0 < budget_s:
+            b = order[done % len(order)]
             decode_reference(wl, rows=[b])
             tokens += wl.prefix_len_of(b) + int(wl.suffix_len[b])
             done += 1
     el = time.perf_counter() - t0
     return {"value": round(tokens / el, 1), "unit": "KV-tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{done} of {wl.batch} requests of the same workload (all query heads, "
-                      f"prefix + suffix), fp64 numpy, {el:.1f} s"}
+            "sample": f"{done} requests ({done / wl.batch:.2f} passes over the {wl.batch} requests of the same "
+                      f"workload, all query heads, prefix + suffix), fp64 numpy, {el:.1f} s"}
 
 
 if __name__ == "__main__":
