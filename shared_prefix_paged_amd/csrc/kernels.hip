@@ -773,10 +773,15 @@ __device__ __forceinline__ void attend_range_mfma(const Args &a, const Req &r, i
     }
 }
 
-// The step's new COLD slots of one sub-batch (append mode): slot of request
-// b0 + i.  Checked on the host (in range, room in the block table).
-struct AppendSlots {
+// Per-request host data of one sub-batch's merge, in its kernel arguments
+// (entry i is request b0 + i):
+//  - slots: the step's new COLD slot (append mode), checked on the host (in
+//    range, room in the block table);
+//  - prefix_np: partial states of the MFMA prefix pass, from the host copies
+//    of the group arrays, so no merging wave waits on a geometry load.
+struct MergeRows {
     int32_t slots[spkv::kFlatArgReqs];
+    uint8_t prefix_np[spkv::kFlatArgReqs];
 };
 
 // Occupancy, float32: 4 waves per SIMD (<= 128 VGPRs) up to G = 6, 3 above;
@@ -1204,7 +1209,7 @@ __global__ __launch_bounds__(64 * W * KH) void prefix_mfma_kernel(Args a) {
 // as spkv_append_tokens does.
 template <int D, bool APPEND = false>
 __global__ __launch_bounds__(256) void merge_kernel(Args a, float *out, float *lse_out, FlatLaunch fr,
-                                                    FlatLaunch fp, AppendSlots ap) {
+                                                    FlatLaunch fp, MergeRows ap) {
     constexpr int LPP = D / 4;      // lanes per partial row (float4 each)
     constexpr int PPW = 64 / LPP;   // partial rows per wave-wide load
     constexpr int BATCH = 40 / PPW; // wave-wide loads in flight (40 partials)
@@ -1246,9 +1251,7 @@ __global__ __launch_bounds__(256) void merge_kernel(Args a, float *out, float *l
     const int i = b - fr.b0;
     int np = 0, first;
     if (a.prefix_mode == 1) {
-        const Req r = req_geo(a, b);
-        if (r.g >= 0 && r.casc && r.lp > 0)
-            np = spkv::splits_for(r.lp, spkv::chunk_for(r.lp, a.prefix_tau, spkv::kPrefixSplitCap, a.prefix_granule));
+        np = ap.prefix_np[i];
     } else if (a.prefix_mode == 2) {
         np = flat_parts(fp, i, &first);
     }
@@ -1601,12 +1604,14 @@ spkv_status launch_prefix(const Args &a, const Plan &p, int d, hipStream_t st) {
 }
 
 spkv_status launch_merge(const Args &a, int d, float *out, float *lse, const FlatLaunch &fr, const FlatLaunch &fp,
-                         const int32_t *append_slots, hipStream_t st) {
+                         const int32_t *append_slots, const uint8_t *prefix_np, hipStream_t st) {
     const int64_t rows = (int64_t)fr.nreq * a.Hq;
     if (rows == 0) return SPKV_OK;
     dim3 grid((unsigned)((rows + 3) / 4)), block(256);
     TimedLaunch tl(SPKV_KERNEL_MERGE, st);
-    AppendSlots ap{};
+    MergeRows ap{};
+    if (prefix_np)
+        for (int i = 0; i < fr.nreq; ++i) ap.prefix_np[i] = prefix_np[fr.b0 + i];
     if (append_slots) {
         for (int i = 0; i < fr.nreq; ++i) ap.slots[i] = append_slots[fr.b0 + i];
         grid.x += (unsigned)((fr.nreq + 3) / 4);   // the new-token waves
@@ -1704,9 +1709,23 @@ spkv_status run_decode(const spkv_batch *b, const spkv_kv *kv, const int32_t *ca
         if (st != SPKV_OK) return st;
     }
     static const FlatLaunch kNone{};
+    // Prefix partials per request (MFMA prefix pass): the split rule of the
+    // prefix kernel applied to the host copies (validated by the plan).
+    std::vector<uint8_t> prefix_np;
+    if (a.prefix_mode == 1) {
+        prefix_np.assign((size_t)b->batch, 0);
+        for (int r = 0; r < b->batch; ++r) {
+            const int g = b->host_group_of[r];
+            if (g < 0 || g >= b->num_groups || !((p.cascade.bits[g >> 5] >> (g & 31)) & 1u)) continue;
+            const int lp = b->host_hot_len[g];
+            if (lp <= 0) continue;
+            const int n = spkv::splits_for(lp, spkv::chunk_for(lp, a.prefix_tau, spkv::kPrefixSplitCap, a.prefix_granule));
+            prefix_np[(size_t)r] = (uint8_t)std::min(n, spkv::kPrefixSplitCap);
+        }
+    }
     for (size_t i = 0; i < p.flat.size(); ++i) {
         st = launch_merge(a, b->head_dim, out, lse, p.flat[i], p.prefix_as_flat && p.run_prefix ? p.pflat[i] : kNone,
-                          app ? app->slots : nullptr, hs);
+                          app ? app->slots : nullptr, prefix_np.empty() ? nullptr : prefix_np.data(), hs);
         if (st != SPKV_OK) return st;
     }
     return SPKV_OK;
