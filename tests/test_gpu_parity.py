@@ -74,6 +74,16 @@ def small_cases():
         "bf16_d64_halves_ragged": lambda: W.make_custom(
             batch=11, num_q_heads=8, num_kv_heads=1, head_dim=64, dtype="bf16", group_prefix_len=[545, 7],
             group_of=[0] * 9 + [1, 1], suffix_len=[3, 70, 1, 5, 9, 130, 2, 33, 64, 17, 8], seed=23),
+        # more requests than one paged-pass launch takes (256): two sub-batches,
+        # each with its own stream-K split and merge launch
+        "bf16_two_sub_batches": lambda: W.make_custom(
+            batch=300, num_q_heads=8, num_kv_heads=2, head_dim=128, dtype="bf16", group_prefix_len=[96, 31, 700],
+            group_of=[int(g) for g in np.random.default_rng(24).integers(-1, 3, 300)],
+            suffix_len=[int(x) for x in np.random.default_rng(25).integers(1, 90, 300)], seed=24),
+        "f32_two_sub_batches": lambda: W.make_custom(
+            batch=260, num_q_heads=4, num_kv_heads=1, head_dim=64, dtype="f32", group_prefix_len=[50, 130],
+            group_of=[int(g) for g in np.random.default_rng(26).integers(-1, 2, 260)],
+            suffix_len=[int(x) for x in np.random.default_rng(27).integers(1, 40, 260)], seed=25),
     }
 
 
