@@ -78,6 +78,10 @@ struct Args {
     const void *k_new;
     const void *v_new;
     int32_t append;
+    // Set when no request's paged-pass tokens include HOT slab rows: every
+    // K/V row the bf16 paged pass reads is then a private COLD row, read once
+    // per step, and is loaded with the non-temporal hint.
+    int32_t cold_nt;
 };
 
 __device__ __forceinline__ bool mask_get(const GroupMask &m, int g) { return (m.bits[g >> 5] >> (g & 31)) & 1u; }
@@ -220,6 +224,20 @@ __device__ __forceinline__ void dma16_at(const void *addr, uint32_t lds_base) {
 }
 
 // 4 bytes per lane: lane l's dword (at gbase + voff) lands at lds_base + 4 * l.
+// The same with the non-temporal hint, for rows that are read once per step.
+__device__ __forceinline__ void dma16_at_nt(const void *addr, uint32_t lds_base) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off nt\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(addr), "s"(lds_base)
+        : "memory");
+}
+
 __device__ __forceinline__ void dma4(const void *gbase, uint32_t voff, uint32_t lds_base) {
     uint32_t saved;
     asm volatile(
@@ -550,7 +568,7 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 // ends with it loads the head's K/V rows of the token from k_new / v_new at
 // its start and, once its last stage has landed, writes them over the token's
 // row of that stage in LDS (the token's DMA lanes fetched a placeholder row).
-template <int D, int G, bool APP>
+template <int D, int G, bool APP, bool NT>
 __device__ __forceinline__ void attend_range_mfma(const Args &a, const Req &r, int b, int h, int t0, int t1,
                                                   int slot, int lane, char *ring, uint32_t ring_off) {
     using F = FlatMfmaGeom<D>;
@@ -661,8 +679,13 @@ __device__ __forceinline__ void attend_range_mfma(const Args &a, const Req &r, i
             const uint32_t c = (uint32_t)__shfl((int)code, ti, 64);
             const bool hot = c >> 31;
             const int64_t off = (int64_t)(c & 0x7fffffffu) * F::ROWB;
-            dma16_at((hot ? khot : kcold) + off + ksrc[i], dst + 1024u * i);
-            dma16_at((hot ? vhot : vcold) + off + vsrc[i], dst + F::OPB + 1024u * i);
+            if constexpr (NT) {   // the launch reads COLD rows only
+                dma16_at_nt(kcold + off + ksrc[i], dst + 1024u * i);
+                dma16_at_nt(vcold + off + vsrc[i], dst + F::OPB + 1024u * i);
+            } else {
+                dma16_at((hot ? khot : kcold) + off + ksrc[i], dst + 1024u * i);
+                dma16_at((hot ? vhot : vcold) + off + vsrc[i], dst + F::OPB + 1024u * i);
+            }
         }
     };
 
@@ -788,7 +811,7 @@ struct MergeRows {
 // the LDS ring (4 x 8.25 KB per block of 4 waves) admits 4 blocks per CU.
 // bf16: the LDS ring (4 x 8 KB per wave for d = 128) admits one or two
 // blocks per CU, so registers are not the limit.
-template <bool BF16, int D, int G, bool APP = false>
+template <bool BF16, int D, int G, bool APP = false, bool NT = false>
 __global__ __launch_bounds__(256, (BF16 ? 2 : (G <= 6 ? 4 : 3))) void flat_kernel(Args a, int part, FlatLaunch fl) {
     extern __shared__ __attribute__((aligned(1024))) char flat_smem[];
     const int k = blockIdx.x;
@@ -828,7 +851,7 @@ __global__ __launch_bounds__(256, (BF16 ? 2 : (G <= 6 ? 4 : 3))) void flat_kerne
         const int t0 = lo + (int)(lo_s - o0);
         const int t1 = min(hi, lo + (int)(hi_s - o0));   // device data shorter than the plan: clamp
         if (t1 <= t0) continue;
-        if constexpr (BF16) attend_range_mfma<D, G, APP>(a, r, b, h, t0, t1, slot0 + slot, lane, ring, ring_off);
+        if constexpr (BF16) attend_range_mfma<D, G, APP, NT>(a, r, b, h, t0, t1, slot0 + slot, lane, ring, ring_off);
         else attend_range<BF16, D, G>(a, r, b, h, t0, t1, slot0 + slot, lane, ring, ring_off);
     }
 }
@@ -1527,24 +1550,28 @@ spkv_status check_launch(const char *what) {
 }
 
 // Dynamic LDS above 64 KB is granted per kernel once its limit is raised.
+template <bool BF16, int D, int G, bool APP, bool NT>
+spkv_status launch_flat_k(const Args &a, int part, const FlatLaunch &f, dim3 grid, dim3 block, size_t lds,
+                          TimedLaunch &tl) {
+    static const hipError_t attr = hipFuncSetAttribute((const void *)flat_kernel<BF16, D, G, APP, NT>,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, spkv::kLdsPerCU);
+    if (attr != hipSuccess) return fail(SPKV_E_HIP, std::string("flat_kernel LDS limit: ") + hipGetErrorString(attr));
+    tl.launch(flat_kernel<BF16, D, G, APP, NT>, grid, block, lds, a, part, f);
+    return check_launch("flat_kernel");
+}
+
+// bf16: append mode (the step's new tokens come from k_new / v_new) and the
+// streaming hint select the instantiation.
 template <bool BF16, int D, int G>
 spkv_status launch_flat_g(const Args &a, int part, const FlatLaunch &f, dim3 grid, dim3 block, size_t lds,
                           const int32_t *append_slots, TimedLaunch &tl) {
-    static const hipError_t attr = hipFuncSetAttribute((const void *)flat_kernel<BF16, D, G>,
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, spkv::kLdsPerCU);
-    if (attr != hipSuccess) return fail(SPKV_E_HIP, std::string("flat_kernel LDS limit: ") + hipGetErrorString(attr));
     if constexpr (BF16) {
-        if (append_slots) {   // append mode: the step's new tokens come from k_new / v_new
-            static const hipError_t attr2 = hipFuncSetAttribute(
-                (const void *)flat_kernel<BF16, D, G, true>, hipFuncAttributeMaxDynamicSharedMemorySize, spkv::kLdsPerCU);
-            if (attr2 != hipSuccess)
-                return fail(SPKV_E_HIP, std::string("flat_kernel LDS limit: ") + hipGetErrorString(attr2));
-            tl.launch(flat_kernel<BF16, D, G, true>, grid, block, lds, a, part, f);
-            return check_launch("flat_kernel");
-        }
+        if (append_slots)
+            return a.cold_nt ? launch_flat_k<BF16, D, G, true, true>(a, part, f, grid, block, lds, tl)
+                             : launch_flat_k<BF16, D, G, true, false>(a, part, f, grid, block, lds, tl);
+        if (a.cold_nt) return launch_flat_k<BF16, D, G, false, true>(a, part, f, grid, block, lds, tl);
     }
-    tl.launch(flat_kernel<BF16, D, G>, grid, block, lds, a, part, f);
-    return check_launch("flat_kernel");
+    return launch_flat_k<BF16, D, G, false, false>(a, part, f, grid, block, lds, tl);
 }
 
 template <bool BF16, int D>
@@ -1687,6 +1714,18 @@ spkv_status run_decode(const spkv_batch *b, const spkv_kv *kv, const int32_t *ca
         a.append = 1;
         a.k_new = app->k_new;
         a.v_new = app->v_new;
+    }
+    // Streaming hint for the paged pass: only when it re-reads no HOT slab
+    // (no member of a group that skips the prefix contraction).  A slab's
+    // rows re-read by many requests' pieces are served by the caches, and
+    // the non-temporal COLD reads slowed such steps down.
+    a.cold_nt = 1;
+    for (int r = 0; r < b->batch; ++r) {
+        const int g = b->host_group_of[r];
+        if (g >= 0 && g < b->num_groups && !((p.cascade.bits[g >> 5] >> (g & 31)) & 1u) && b->host_hot_len[g] > 0) {
+            a.cold_nt = 0;
+            break;
+        }
     }
     hipStream_t hs = (hipStream_t)stream;
     const bool bf16 = b->dtype == SPKV_DTYPE_BF16;
