@@ -122,11 +122,14 @@ void        spkv_cold_destroy(spkv_cold *cold);
 /* New empty sequence; ids are issued 0, 1, 2, ... and never reused. */
 spkv_status spkv_seq_new(spkv_cold *cold, int32_t *seq_out);
 
-/* For i in 0..n-1, in array order, reserve the slot of one more token of
- * seqs[i] ([PKV] Code, append):
- *   off = len % P; if off == 0 take a new page; else if the last page is
- *   shared (refcount > 1) take a new page, drop one reference to the old one
- *   and report the copy-on-write pair (old, new); slot = last_page * P + off.
+/* For i in 0..n-1, in array order, give token number len of seqs[i] its
+ * slot ([PKV] How it works and Code: append with copy-on-write).  That token
+ * belongs to page len / P of the sequence, at row len % P.  A sequence only
+ * writes into a page it holds alone, so a page is taken from the free stack
+ * when the token starts a new page, or when its page is still shared with
+ * another sequence after a fork; in the second case the shared page loses one
+ * reference, the new page replaces it in the table and (old, new) is reported
+ * as a copy-on-write pair (the caller copies the page before writing).
  * slots_out[n] receives the slots; cow_pairs_out[2*k], [2*k+1] the k-th
  * (src, dst) pair (at most n pairs), *n_cow_out their count, *n_done_out the
  * appends that completed.  Stops at the first failure (SPKV_E_NOMEM or

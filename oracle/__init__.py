@@ -17,5 +17,8 @@ Modules
 
 Pinned by tests in ``tests/test_oracle_*.py`` against values and closed forms
 fixed by the pages and by mathematics (see each module's header for what pins
-it).  Functions with no such pin say "parity unpinned".
+it).  Every function here has such a pin.  What stays unpinned is a reading,
+not a function: the HOT pool's eviction tie-break beyond least recently
+released first (lower base on equal ticks, which cannot occur since ticks are
+unique) has no value on the pages to check against.
 """

@@ -84,20 +84,20 @@ class ColdPool:
         self.seqs: Dict[int, Seq] = {}
         self.next_id = 0
 
-    # -- block primitives ------------------------------------------------
-    def _alloc(self) -> Optional[int]:
-        if not self.free:
-            return None
-        b = self.free.pop()
-        self.ref[b] = 1
-        return b
+    # -- page ownership ----------------------------------------------------
+    def _take_page(self) -> int:
+        """Hand out the page on top of the free stack, owned once."""
+        page = self.free.pop()
+        self.ref[page] = 1
+        return page
 
-    def _decref(self, b: int) -> None:
-        if self.ref[b] <= 0:
-            raise StateError(f"decref of free page {b}")
-        self.ref[b] -= 1
-        if self.ref[b] == 0:
-            self.free.append(b)
+    def _drop_page(self, page: int) -> None:
+        """One owner fewer; a page nobody owns goes back on the free stack."""
+        if self.ref[page] <= 0:
+            raise StateError(f"decref of free page {page}")
+        self.ref[page] -= 1
+        if self.ref[page] == 0:
+            self.free.append(page)
 
     def num_free(self) -> int:
         return len(self.free)
@@ -116,28 +116,33 @@ class ColdPool:
         return sid
 
     def append(self, sid: int) -> Tuple[int, Optional[Tuple[int, int]]]:
-        """Reserve the slot of one more token; returns (slot, cow pair or None)."""
+        """Slot of the sequence's next token; returns (slot, copy-on-write pair or None).
+
+        The token at position ``length`` lives in page ``length // P`` of the
+        sequence, row ``length % P``.  The sequence must hold that page alone
+        before the token is written: a page it does not have yet, or one that
+        a fork still shares, is replaced by a page from the free stack (the
+        shared page keeps its other owners and the caller copies its rows).
+        """
         s = self._seq(sid)
         P = self.page_size
-        off = s.length % P
+        page_index, row = divmod(s.length, P)
+        starts_page = page_index == len(s.table)
+        shared = not starts_page and self.ref[s.table[page_index]] > 1
         cow = None
-        if off == 0:
-            b = self._alloc()
-            if b is None:
-                raise OutOfMemory("COLD pool exhausted")
-            s.table.append(b)
-        else:
-            last = s.table[-1]
-            if self.ref[last] > 1:
-                nb = self._alloc()
-                if nb is None:
-                    raise OutOfMemory("COLD pool exhausted (copy-on-write)")
-                self._decref(last)
-                s.table[-1] = nb
-                cow = (last, nb)
-        slot = s.table[-1] * P + off
+        if starts_page or shared:
+            if not self.free:
+                raise OutOfMemory("COLD pool exhausted" + (" (copy-on-write)" if shared else ""))
+            page = self._take_page()
+            if shared:
+                old = s.table[page_index]
+                s.table[page_index] = page
+                self._drop_page(old)
+                cow = (old, page)
+            else:
+                s.table.append(page)
         s.length += 1
-        return slot, cow
+        return s.table[page_index] * P + row, cow
 
     def append_batch(self, seqs: List[int]):
         """Single appends in array order; stops at the first failure.
@@ -155,20 +160,20 @@ class ColdPool:
         return slots, cows, len(seqs), None
 
     def fork(self, sid: int) -> int:
+        """A new sequence with the same history: every page gains an owner."""
         s = self._seq(sid)
-        for b in s.table:
-            self.ref[b] += 1
         nid = self.seq_new()
         self.seqs[nid] = Seq(list(s.table), s.length)
+        for page in s.table:
+            self.ref[page] += 1
         return nid
 
     def release(self, sid: int) -> None:
+        """The sequence gives up every page it owns (in table order) and its id."""
         s = self._seq(sid)
-        for b in s.table:
-            self._decref(b)
-        s.table = []
-        s.length = 0
-        s.live = False
+        for page in s.table:
+            self._drop_page(page)
+        s.table, s.length, s.live = [], 0, False
 
     # -- views -------------------------------------------------------------
     def block_table(self, sid: int) -> List[int]:

@@ -20,9 +20,18 @@ All arithmetic is float64 on the exact input values (bf16 bit patterns are
 widened exactly).  A matrix product from numpy serves as a step; nothing is
 blocked, fused or reordered beyond the definition.
 
+``attend_shared_prefix`` and ``decode_reference_grouped`` compute the same
+definition for many rows that share one prefix: the prefix scores of all rows
+come from one matrix product, each row's suffix scores from its own tokens,
+and every row still takes one max and one normaliser over all of its tokens.
+They exist so that every row of a full-size configuration can be checked in
+seconds (the prefix is widened to float64 once per group, not per request).
+
 Pinned by ``tests/test_oracle_attention.py``: closed forms (Q = 0, constant V,
 one token, token counting, a needle key), 50-digit brute force on tiny inputs,
-cascade = flat, page-size and slot-permutation invariance, merge identities.
+cascade = flat, page-size and slot-permutation invariance, merge identities;
+the grouped forms by the same closed forms and by agreement with the per-row
+form on drawn workloads.
 """
 from __future__ import annotations
 
@@ -65,6 +74,73 @@ def attend(q_rows: np.ndarray, k_parts: Sequence[np.ndarray], v_parts: Sequence[
         num += e.T @ v
         den += e.sum(axis=0)
     return num / den[:, None], m + np.log(den)
+
+
+def attend_shared_prefix(q_rows: np.ndarray, prefix_k, prefix_v, suffix_parts, scale: float):
+    """Rows that share one prefix, each with its own suffix tokens.
+
+    q_rows [R, d]; prefix_k / prefix_v [Lp, d] or None; suffix_parts is a list
+    of (row slice, k [Ls, d], v [Ls, d]) covering every row once (float64).
+    Row r attends to the prefix tokens followed by its own suffix tokens.
+    Returns O [R, d], LSE [R].
+    """
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    R, d = q_rows.shape
+    m = np.full(R, NEG_INF)
+    sp = None
+    if prefix_k is not None and prefix_k.shape[0] > 0:
+        sp = scale * (q_rows @ prefix_k.T)                       # [R, Lp]
+        m = np.max(sp, axis=1)
+    ss = []
+    for rows, k, v in suffix_parts:
+        s = scale * (q_rows[rows] @ k.T)                         # [r, Ls]
+        ss.append(s)
+        if s.shape[1]:
+            m[rows] = np.maximum(m[rows], np.max(s, axis=1))
+    empty = np.isneginf(m)
+    m_use = np.where(empty, 0.0, m)
+    num = np.zeros((R, d))
+    den = np.zeros(R)
+    if sp is not None:
+        e = np.exp(sp - m_use[:, None])
+        num += e @ prefix_v
+        den += e.sum(axis=1)
+    for (rows, k, v), s in zip(suffix_parts, ss):
+        if s.shape[1] == 0:
+            continue
+        e = np.exp(s - m_use[rows][:, None])
+        num[rows] += e @ v
+        den[rows] += e.sum(axis=1)
+    den_use = np.where(empty, 1.0, den)
+    out = np.where(empty[:, None], 0.0, num / den_use[:, None])
+    lse = np.where(empty, NEG_INF, m_use + np.log(den_use))
+    return out, lse
+
+
+def decode_reference_grouped(wl, scale: float = None):
+    """Every row of a drawn workload, group by group (same values as decode_reference)."""
+    cfg = wl.cfg
+    dt, G = cfg.dtype, cfg.group_size
+    hkv = cfg.num_kv_heads
+    scale = (1.0 / np.sqrt(cfg.head_dim)) if scale is None else scale
+    B, Hq, d = wl.q.shape
+    out = np.zeros((B, Hq, d))
+    lse = np.full((B, Hq), NEG_INF)
+    groups = sorted(set(int(g) for g in wl.group_of))
+    for g in groups:
+        members = [int(b) for b in np.flatnonzero(wl.group_of == g)]
+        pk = widen(wl.prefix_k[g], dt) if g >= 0 else None
+        pv = widen(wl.prefix_v[g], dt) if g >= 0 else None
+        suffix = [tuple(widen(x, dt) for x in wl.suffix_kv(b)) for b in members]
+        for h in range(hkv):
+            q = np.concatenate([widen(wl.q[b, h * G:(h + 1) * G], dt) for b in members])
+            parts = [(slice(i * G, (i + 1) * G), sk[:, h], sv[:, h]) for i, (sk, sv) in enumerate(suffix)]
+            o, l = attend_shared_prefix(q, None if pk is None else pk[:, h], None if pv is None else pv[:, h],
+                                        parts, scale)
+            for i, b in enumerate(members):
+                out[b, h * G:(h + 1) * G] = o[i * G:(i + 1) * G]
+                lse[b, h * G:(h + 1) * G] = l[i * G:(i + 1) * G]
+    return out, lse
 
 
 def merge(o_a: np.ndarray, lse_a: np.ndarray, o_b: np.ndarray, lse_b: np.ndarray):

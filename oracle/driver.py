@@ -29,6 +29,12 @@ with its own prefix; the paper's heterogeneous multi-agent setting, Section
     are copied, then the new tokens are written;
   * attention covers every live request.
 At the end every live request is released and unreferenced slabs evicted.
+
+Pinned by ``tests/test_oracle_driver.py`` (refcounts against live tables, HOT
+refcounts against live members, histories built from the draws, the fork and
+release schedule, teardown, and both reference forms against the flat oracle)
+and, for the single step, by the page-size and slot-order invariance and the
+pool-mirror pins.
 """
 from __future__ import annotations
 
@@ -38,7 +44,7 @@ from typing import Dict, List, Optional
 import numpy as np
 
 from .alloc import ColdPool, HotPool
-from .attention import attend, widen, NEG_INF
+from .attention import attend, attend_shared_prefix, widen, NEG_INF
 from .pools import PoolMirror
 
 
@@ -234,6 +240,34 @@ class MultiStepSim:
                 ks = ([pk[g][0][:, h]] if g >= 0 else []) + [sk[:, h]]
                 vs = ([pk[g][1][:, h]] if g >= 0 else []) + [sv[:, h]]
                 out[i, r], lse[i, r] = attend(qb[r], ks, vs, scale)
+        return out, lse
+
+    def reference_grouped(self, live: List[int], q: np.ndarray, scale: float = None):
+        """The same values for every live request, each group's prefix widened
+        once and attended by all of its members' rows together."""
+        wl = self.wl
+        cfg = wl.cfg
+        dt, G, hkv = cfg.dtype, cfg.group_size, cfg.num_kv_heads
+        scale = (1.0 / np.sqrt(cfg.head_dim)) if scale is None else scale
+        n, Hq, d = q.shape
+        out = np.zeros((n, Hq, d))
+        lse = np.full((n, Hq), NEG_INF)
+        by_group: Dict[int, List[int]] = {}
+        for i, b in enumerate(live):
+            by_group.setdefault(self.group_of[b], []).append(i)
+        for g, idx in sorted(by_group.items()):
+            pk = widen(wl.prefix_k[g], dt) if g >= 0 else None
+            pv = widen(wl.prefix_v[g], dt) if g >= 0 else None
+            suffix = [(widen(np.concatenate(self.hist_k[live[i]], axis=0), dt),
+                       widen(np.concatenate(self.hist_v[live[i]], axis=0), dt)) for i in idx]
+            for h in range(hkv):
+                qr = np.concatenate([widen(q[i, h * G:(h + 1) * G], dt) for i in idx])
+                parts = [(slice(j * G, (j + 1) * G), sk[:, h], sv[:, h]) for j, (sk, sv) in enumerate(suffix)]
+                o, l = attend_shared_prefix(qr, None if pk is None else pk[:, h], None if pv is None else pv[:, h],
+                                            parts, scale)
+                for j, i in enumerate(idx):
+                    out[i, h * G:(h + 1) * G] = o[j * G:(j + 1) * G]
+                    lse[i, h * G:(h + 1) * G] = l[j * G:(j + 1) * G]
         return out, lse
 
     def finish(self) -> int:

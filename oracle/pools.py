@@ -13,9 +13,14 @@ Layouts (design readings of the pages, also listed in the design notes):
 Storage keeps the input representation (bf16 bit patterns as uint16, or
 float32) so device pools can be compared byte for byte.
 
-Pinned by ``tests/test_oracle_pools.py``: the page's worked block-table
-example (tokens 0-15 in block 3, 16-31 in block 0, 32-40 in block 4) and a
-hand-computed HOT offset; paged gathers reproduce the drawn logical tokens.
+Pinned by ``tests/test_oracle_pools.py``: the "Paged KV cache" page's
+block-table picture written and read back through the mirror (tokens 0-15 in
+block 3, 16-31 in block 0, 32-40 in block 4), a hand-computed HOT offset and
+slab placement, a hand-worked two-page ``copy_blocks`` (pair order, all heads),
+slots outside the pool skipped, and the copy-on-write invariant: after fork +
+append at page size 16 the pre-fork rows and the HOT slab are byte-identical.
+``tests/test_oracle_attention.py`` also checks that attention read back
+through the mirror equals attention over the drawn tokens.
 """
 from __future__ import annotations
 

@@ -54,34 +54,65 @@ spkv_cold::Seq *live_seq(spkv_cold *c, int32_t id) {
     return &c->seqs[id];
 }
 
-// One append; on failure nothing has changed.
+// Where the next token of a sequence goes.  Token t belongs to page t / P of
+// the sequence at row t % P.  A sequence writes only into pages it owns
+// alone: when that page does not exist yet (t starts a page) or is still
+// referenced by another sequence (after a fork), a page must come off the
+// free stack first; in the second case the shared page is swapped for the new
+// one, whose first rows the caller fills with a copy of the old page.
+struct NextSlot {
+    int32_t page_index = 0;   // position in the sequence's table
+    int32_t row = 0;          // row inside the page
+    bool needs_page = false;  // a page comes off the free stack
+    int32_t replaced = -1;    // shared page being swapped out, or -1
+};
+
+NextSlot next_slot(const spkv_cold *c, const spkv_cold::Seq &s) {
+    NextSlot n;
+    n.page_index = s.len / c->page_size;
+    n.row = s.len % c->page_size;
+    if (n.page_index == (int32_t)s.table.size()) {
+        n.needs_page = true;
+    } else {
+        const int32_t cur = s.table[(size_t)n.page_index];
+        if (c->ref[(size_t)cur] > 1) {
+            n.needs_page = true;
+            n.replaced = cur;
+        }
+    }
+    return n;
+}
+
+int32_t take_page(spkv_cold *c) {
+    const int32_t pg = c->stack.back();
+    c->stack.pop_back();
+    c->ref[(size_t)pg] = 1;
+    return pg;
+}
+
+// Reserve a slot for the token at position len of sequence id.  The decision
+// is made first and checked against the free stack, then applied in one go,
+// so a failure (no free page) leaves every piece of state untouched.
 spkv_status cold_append_one(spkv_cold *c, int32_t id, int32_t *slot, int32_t *cow_src, int32_t *cow_dst) {
     spkv_cold::Seq *s = live_seq(c, id);
     if (!s) return fail(SPKV_E_STATE, "append: unknown or released sequence " + std::to_string(id));
-    const int32_t P = c->page_size;
-    const int32_t off = s->len % P;
+    const NextSlot n = next_slot(c, *s);
+    if (n.needs_page && c->stack.empty())
+        return fail(SPKV_E_NOMEM, n.replaced >= 0 ? "COLD pool exhausted (copy-on-write)" : "COLD pool exhausted");
     *cow_src = -1;
     *cow_dst = -1;
-    if (off == 0) {
-        if (c->stack.empty()) return fail(SPKV_E_NOMEM, "COLD pool exhausted");
-        int32_t pg = c->stack.back();
-        c->stack.pop_back();
-        c->ref[pg] = 1;
-        s->table.push_back(pg);
-    } else {
-        int32_t last = s->table.back();
-        if (c->ref[last] > 1) {
-            if (c->stack.empty()) return fail(SPKV_E_NOMEM, "COLD pool exhausted (copy-on-write)");
-            int32_t pg = c->stack.back();
-            c->stack.pop_back();
-            c->ref[pg] = 1;
-            c->ref[last] -= 1;     // stays >= 1: it was shared
-            s->table.back() = pg;
-            *cow_src = last;
-            *cow_dst = pg;
+    if (n.needs_page) {
+        const int32_t fresh = take_page(c);
+        if (n.replaced >= 0) {
+            s->table[(size_t)n.page_index] = fresh;
+            c->ref[(size_t)n.replaced] -= 1;   // still >= 1: another sequence holds it
+            *cow_src = n.replaced;
+            *cow_dst = fresh;
+        } else {
+            s->table.push_back(fresh);
         }
     }
-    *slot = s->table.back() * P + off;
+    *slot = s->table[(size_t)n.page_index] * c->page_size + n.row;
     s->len += 1;
     return SPKV_OK;
 }

@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import workloads as W
-from oracle.attention import attend, merge, decode_reference, cascade_reference, widen, NEG_INF
+from oracle.attention import attend, merge, decode_reference, cascade_reference, widen, NEG_INF, attend_shared_prefix, decode_reference_grouped
 from oracle.driver import run_single_step, paged_reference
 
 
@@ -195,3 +195,40 @@ def test_page_size_and_slot_shuffle_invariance():
         np.testing.assert_array_equal(o, outs[0][0])
         np.testing.assert_array_equal(l, outs[0][1])
     np.testing.assert_allclose(outs[0][0], logical[0], atol=1e-13)
+
+
+# --- the grouped form (one prefix product for all rows of a group) ------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_grouped_equals_per_row(dtype):
+    # Catches: a row taking another member's suffix, a max taken over the
+    # prefix only, or the -1 group (no prefix) given a prefix.
+    wl = multi_group_workload(dtype)
+    o, l = decode_reference(wl)
+    og, lg = decode_reference_grouped(wl)
+    np.testing.assert_allclose(og, o, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lg, l, rtol=0, atol=1e-12)
+
+
+def test_grouped_closed_forms():
+    # Q = 0: every row's output is the mean of its prefix + suffix V rows and
+    # its LSE is ln(Lp + Ls) (rows of one group have different suffixes).
+    rng = np.random.default_rng(1)
+    lp, d = 9, 4
+    pk, pv = rng.standard_normal((lp, d)), rng.standard_normal((lp, d))
+    suf = [(slice(0, 2), rng.standard_normal((3, d)), rng.standard_normal((3, d))),
+           (slice(2, 3), rng.standard_normal((0, d)), rng.standard_normal((0, d))),
+           (slice(3, 5), rng.standard_normal((7, d)), rng.standard_normal((7, d)))]
+    o, l = attend_shared_prefix(np.zeros((5, d)), pk, pv, suf, 0.5)
+    for rows, k, v in suf:
+        allv = np.concatenate([pv, v])
+        np.testing.assert_allclose(o[rows], np.broadcast_to(allv.mean(axis=0), o[rows].shape), atol=1e-14)
+        np.testing.assert_allclose(l[rows], np.log(lp + k.shape[0]), atol=1e-14)
+    # Needle in the suffix of row 3 only: key 8*q for a unit q dominates that row.
+    q = np.zeros((5, d)); q[3, 0] = 1.0
+    suf[2][1][4] = 8.0 * q[3]
+    o, l = attend_shared_prefix(q, pk, pv, suf, 1.0)
+    assert np.max(np.abs(o[3] - suf[2][2][4])) < 5e-2
+    # No prefix and no suffix: the empty state.
+    o, l = attend_shared_prefix(np.ones((1, d)), None, None, [(slice(0, 1), np.zeros((0, d)), np.zeros((0, d)))], 1.0)
+    assert np.all(o == 0) and np.isneginf(l[0])
