@@ -199,10 +199,12 @@ spkv_status spkv_copy_blocks(const int32_t *pairs, int32_t n, void *k_cold, void
  * on the device (a fresh page, a copy-on-write replacement or an append into
  * the current page alike).  host_slots and host_rows are host arrays (the
  * allocator's output); their values are copied into the launch at call time,
- * so no upload is needed.  Rows must be distinct within one call; slots
- * outside [0, cold_slots), rows outside [0, num_rows) and entries beyond
- * max_blocks are skipped.  Run spkv_copy_blocks for the step's
- * copy-on-write pairs first: the copy must not overwrite the new token. */
+ * so no upload is needed.  Rows must be distinct within one call.  Returns
+ * SPKV_E_INVAL, before anything is launched, for a slot outside
+ * [0, cold_slots) or (with tables) a row outside [0, num_rows); a block-table
+ * entry that would land beyond max_blocks (a device length, not checked on
+ * the host) is skipped.  Run spkv_copy_blocks for the step's copy-on-write
+ * pairs first: the copy must not overwrite the new token. */
 spkv_status spkv_append_tokens(const void *k_new, const void *v_new, const int32_t *host_slots,
                                const int32_t *host_rows, int32_t n, void *k_cold, void *v_cold, int64_t cold_slots,
                                int32_t *tables, int32_t max_blocks, int32_t *lens, int32_t num_rows,
@@ -228,7 +230,11 @@ spkv_status spkv_block_table_append(int32_t *tables, int32_t max_blocks, int32_t
 /* One decode step's batch.  Requests that share a prefix form a group whose
  * prefix sits in one HOT slab ([GKV] Section 3.4: each prefix records a HOT
  * base or a COLD marker).  A request with group -1 keeps its whole context
- * (prefix included) in the COLD pool ([GKV] Appendix B.10 fallback). */
+ * (prefix included) in the COLD pool ([GKV] Appendix B.10 fallback).
+ * Membership is group_of alone: the library forms each group's member list
+ * (ascending request id) itself, on the host for the plan and on the device
+ * for the prefix contraction, so no separate member list can disagree with it.
+ * The host copies must hold the same values as the device arrays. */
 typedef struct spkv_batch {
     int32_t batch;                 /* B >= 0 */
     int32_t num_q_heads;           /* Hq, a multiple of Hkv, Hq/Hkv <= 8 */
@@ -239,14 +245,11 @@ typedef struct spkv_batch {
     const void *q;                 /* device [B, Hq, d] */
 
     int32_t num_groups;            /* ng, 0..512 */
-    const int32_t *group_of;       /* device [B]: group of request b, or -1 */
-    const int32_t *group_indptr;   /* device [ng+1]: members of g are group_members[indptr[g] .. indptr[g+1]) */
-    const int32_t *group_members;  /* device: request ids; request b appears once, in group group_of[b] */
+    const int32_t *group_of;       /* device [B]: group of request b in [0, ng), or -1 */
     const int64_t *hot_base;       /* device [ng]: slab base (token slot) */
     const int32_t *hot_len;        /* device [ng]: prefix length Lp_g >= 0; one head's slab
                                       (Lp_g * d * element size) must stay below 4 GiB */
-    const int32_t *host_group_of;     /* host copies of group_of and of the three group arrays above */
-    const int32_t *host_group_indptr;
+    const int32_t *host_group_of;  /* host copies of group_of, hot_base and hot_len */
     const int64_t *host_hot_base;
     const int32_t *host_hot_len;
 

@@ -25,10 +25,8 @@ class spkv_cold_info(C.Structure):
 class spkv_batch(C.Structure):
     _fields_ = [("batch", c_i32), ("num_q_heads", c_i32), ("num_kv_heads", c_i32), ("head_dim", c_i32),
                 ("dtype", c_i32), ("scale", c_f32), ("q", c_vp),
-                ("num_groups", c_i32), ("group_of", c_vp), ("group_indptr", c_vp), ("group_members", c_vp),
-                ("hot_base", c_vp), ("hot_len", c_vp),
-                ("host_group_of", c_vp), ("host_group_indptr", c_vp), ("host_hot_base", c_vp),
-                ("host_hot_len", c_vp),
+                ("num_groups", c_i32), ("group_of", c_vp), ("hot_base", c_vp), ("hot_len", c_vp),
+                ("host_group_of", c_vp), ("host_hot_base", c_vp), ("host_hot_len", c_vp),
                 ("page_size", c_i32), ("max_blocks", c_i32), ("block_tables", c_vp), ("cold_lens", c_vp),
                 ("host_cold_lens", c_vp)]
 

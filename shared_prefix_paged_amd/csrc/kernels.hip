@@ -51,8 +51,6 @@ struct Args {
     float scale_log2;
     int32_t ng;
     const int32_t *group_of;
-    const int32_t *indptr;
-    const int32_t *members;
     const int64_t *hot_base;
     const int32_t *hot_len;
     int32_t page_size, max_blocks;
@@ -679,9 +677,9 @@ __device__ __forceinline__ void attend_range_mfma(const Args &a, const Req &r, i
             const uint32_t c = (uint32_t)__shfl((int)code, ti, 64);
             const bool hot = c >> 31;
             const int64_t off = (int64_t)(c & 0x7fffffffu) * F::ROWB;
-            if constexpr (NT) {   // the launch reads COLD rows only
-                dma16_at_nt(kcold + off + ksrc[i], dst + 1024u * i);
-                dma16_at_nt(vcold + off + vsrc[i], dst + F::OPB + 1024u * i);
+            if constexpr (NT) {   // the host found no HOT row in this launch; the pool select stays
+                dma16_at_nt((hot ? khot : kcold) + off + ksrc[i], dst + 1024u * i);
+                dma16_at_nt((hot ? vhot : vcold) + off + vsrc[i], dst + F::OPB + 1024u * i);
             } else {
                 dma16_at((hot ? khot : kcold) + off + ksrc[i], dst + 1024u * i);
                 dma16_at((hot ? vhot : vcold) + off + vsrc[i], dst + F::OPB + 1024u * i);
@@ -934,12 +932,7 @@ __global__ __launch_bounds__(64 * W * KH) void prefix_mfma_kernel(Args a) {
     const int64_t base = a.hot_base[g];
     const int lp = a.hot_len[g];
     if (lp <= 0 || base < 0 || base + lp > a.hot_capacity) return;
-    int m0 = a.indptr[g], m1 = a.indptr[g + 1];
-    m0 = max(0, min(m0, a.B));
-    m1 = max(m0, min(m1, a.B));
-    const int M = (m1 - m0) * a.G;
     const int mt = blockIdx.y;
-    if (mt * 32 * W >= M) return;
     const int chunk = spkv::chunk_for(lp, a.prefix_tau, spkv::kPrefixSplitCap, NT);
     const int nsplit = spkv::splits_for(lp, chunk);
     const int s = blockIdx.x;
@@ -1015,17 +1008,52 @@ __global__ __launch_bounds__(64 * W * KH) void prefix_mfma_kernel(Args a) {
     };
 
     // Prologue.  The compiler waits for its own loads with vmcnt(0), which
-    // also covers every DMA in flight, so the member index and Q (loads it
+    // also covers every DMA in flight, so the group scan and Q (loads it
     // tracks) are read while only tile 0 is in flight, and tiles 1 .. STAGES-2
     // follow once Q has landed.
     if (ntiles > 0) issue(0, 0);
+
+    // The group's members are the requests whose group_of is g, in ascending
+    // id ([GKV] Section 3.4); query row r of the group belongs to member r / G.
+    // One scan of group_of (64 requests per wave-wide load, several loads in
+    // flight) counts the members and writes the ids this wave's 32 rows need,
+    // member ranks [kw0, kw0 + kWin), to its LDS window.
+    constexpr int kWin = 40;                   // >= 32 rows / G + 1 members
+    __shared__ int32_t member_win[W * KH][kWin];
+    int32_t *win = member_win[wave_id];
+    const int kw0 = (mt * 32 * W + wave * 32) / a.G;
+    int count = 0;                             // wave-uniform
+    for (int c0 = 0; c0 < a.B; c0 += 256) {
+        int gv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = c0 + 64 * u + lane;
+            gv[u] = i < a.B ? a.group_of[i] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const bool mine = gv[u] == g;
+            const uint64_t m = __ballot(mine);
+            const int rank = count + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            if (mine && rank >= kw0 && rank < kw0 + kWin) win[rank - kw0] = c0 + 64 * u + lane;
+            count += __popcll(m);
+        }
+    }
+    const int M = count * a.G;
+    if (mt * 32 * W >= M) {                    // block-uniform: every wave counted the same members
+        wait_vmcnt<0>();                       // tile 0's DMA has landed before the LDS is released
+        return;
+    }
+    __builtin_amdgcn_wave_barrier();           // the window's writes (other lanes) before its reads
+    asm volatile("" ::: "memory");
 
     // This lane's query row (column of S^T / O^T).
     const int row = mt * 32 * W + wave * 32 + col;
     const bool row_ok = row < M;
     int qb = 0, qj = 0;
     if (row_ok) {
-        const int mb = a.members[m0 + row / a.G];
+        const int mb = win[row / a.G - kw0];
         qb = max(0, min(mb, a.B - 1));
         qj = h * a.G + row % a.G;
     }
@@ -1662,8 +1690,6 @@ Args make_args(const spkv_batch *b, const spkv_kv *kv, const Plan &p, void *ws) 
     a.scale_log2 = b->scale * kLog2e;
     a.ng = b->num_groups;
     a.group_of = b->group_of;
-    a.indptr = b->group_indptr;
-    a.members = b->group_members;
     a.hot_base = b->hot_base;
     a.hot_len = b->hot_len;
     a.page_size = b->page_size;
@@ -1826,6 +1852,15 @@ spkv_status spkv_append_tokens(const void *k_new, const void *v_new, const int32
     if (!k_new || !v_new || !host_slots || !k_cold || !v_cold)
         return fail(SPKV_E_INVAL, "append_tokens: null pointer");
     if (tables && !lens) return fail(SPKV_E_INVAL, "append_tokens: tables without lens");
+    for (int32_t i = 0; i < n; ++i) {
+        if (host_slots[i] < 0 || host_slots[i] >= cold_slots)
+            return fail(SPKV_E_INVAL, "append_tokens: slot " + std::to_string(host_slots[i]) + " of token " +
+                                          std::to_string(i) + " outside the COLD pool");
+        const int32_t r = host_rows ? host_rows[i] : i;
+        if (tables && (r < 0 || r >= num_rows))
+            return fail(SPKV_E_INVAL, "append_tokens: row " + std::to_string(r) + " of token " + std::to_string(i) +
+                                          " outside [0, num_rows)");
+    }
     const int esz = dtype == SPKV_DTYPE_BF16 ? 2 : 4;
     const int pps = hkv * d * esz / 16;
     for (int32_t i0 = 0; i0 < n; i0 += kAppendArgTokens) {

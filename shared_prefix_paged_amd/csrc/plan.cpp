@@ -51,21 +51,14 @@ spkv_status validate_batch(const spkv_batch *b, const spkv_kv *kv) {
     if (B > 0 && (!b->q || !b->group_of || !b->cold_lens || !b->host_cold_lens || !b->host_group_of))
         return fail(SPKV_E_INVAL, "q, group_of, cold_lens and their host copies are required");
     if (B > 0 && b->max_blocks > 0 && !b->block_tables) return fail(SPKV_E_INVAL, "block_tables is required");
-    if (ng > 0 && (!b->group_indptr || !b->group_members || !b->hot_base || !b->hot_len ||
-                   !b->host_group_indptr || !b->host_hot_base || !b->host_hot_len))
+    if (ng > 0 && (!b->hot_base || !b->hot_len || !b->host_hot_base || !b->host_hot_len))
         return fail(SPKV_E_INVAL, "group arrays (device and host) are required when num_groups > 0");
-    if (ng > 0) {
-        if (b->host_group_indptr[0] != 0) return fail(SPKV_E_INVAL, "group_indptr[0] must be 0");
-        for (int g = 0; g < ng; ++g) {
-            if (b->host_group_indptr[g + 1] < b->host_group_indptr[g])
-                return fail(SPKV_E_INVAL, "group_indptr must be non-decreasing");
-            if (b->host_hot_len[g] < 0 || b->host_hot_base[g] < 0) return fail(SPKV_E_INVAL, "negative hot_base/hot_len");
-            if ((int64_t)b->host_hot_len[g] * b->head_dim * 4 >= (int64_t(1) << 32))
-                return fail(SPKV_E_INVAL, "group " + std::to_string(g) + " prefix longer than a 4 GiB slab per head");
-            if (kv && b->host_hot_base[g] + b->host_hot_len[g] > kv->hot_capacity)
-                return fail(SPKV_E_INVAL, "group " + std::to_string(g) + " slab exceeds the HOT capacity");
-        }
-        if (b->host_group_indptr[ng] > B) return fail(SPKV_E_INVAL, "more group members than requests");
+    for (int g = 0; g < ng; ++g) {
+        if (b->host_hot_len[g] < 0 || b->host_hot_base[g] < 0) return fail(SPKV_E_INVAL, "negative hot_base/hot_len");
+        if ((int64_t)b->host_hot_len[g] * b->head_dim * 4 >= (int64_t(1) << 32))
+            return fail(SPKV_E_INVAL, "group " + std::to_string(g) + " prefix longer than a 4 GiB slab per head");
+        if (kv && b->host_hot_base[g] + b->host_hot_len[g] > kv->hot_capacity)
+            return fail(SPKV_E_INVAL, "group " + std::to_string(g) + " slab exceeds the HOT capacity");
     }
     for (int i = 0; i < B; ++i) {
         if (b->host_group_of[i] < -1 || b->host_group_of[i] >= ng)
@@ -88,6 +81,15 @@ spkv_status validate_batch(const spkv_batch *b, const spkv_kv *kv) {
 }
 
 static inline bool mask_get(const GroupMask &m, int g) { return (m.bits[g >> 5] >> (g & 31)) & 1u; }
+
+// Requests per group ([GKV] Section 3.4: a request belongs to the group whose
+// prefix it shares), counted from group_of; validated batches only.
+static std::vector<int64_t> member_counts(const spkv_batch *b) {
+    std::vector<int64_t> n((size_t)std::max(0, b->num_groups), 0);
+    for (int i = 0; i < b->batch; ++i)
+        if (b->host_group_of[i] >= 0) n[(size_t)b->host_group_of[i]] += 1;
+    return n;
+}
 
 // Stream-K launches of one paged pass over per-request lengths L (sub-batches
 // of at most kFlatArgReqs requests).  Each launch gets as many equal ranges of
@@ -140,10 +142,11 @@ spkv_status make_plan(const spkv_batch *b, const int32_t *cascade, int32_t num_c
         if (!cascade || cascade[g]) p->cascade.bits[g >> 5] |= 1u << (g & 31);
 
     const bool bf16 = b->dtype == SPKV_DTYPE_BF16;
+    const std::vector<int64_t> members = member_counts(b);
     int64_t prefix_work = 0;        // row tiles x keys of the MFMA prefix pass
     int64_t max_m = 0, max_lp_c = 0;
     for (int g = 0; g < ng; ++g) {
-        const int64_t n = b->host_group_indptr[g + 1] - b->host_group_indptr[g];
+        const int64_t n = members[(size_t)g];
         const int64_t lp = b->host_hot_len[g];
         if (n == 0 || lp == 0 || !mask_get(p->cascade, g)) continue;
         max_m = std::max<int64_t>(max_m, n * G);
@@ -184,7 +187,7 @@ spkv_status make_plan(const spkv_batch *b, const int32_t *cascade, int32_t num_c
         const int64_t mt = 32 * p->prefix_waves;
         p->prefix_mtiles = (int32_t)((max_m + mt - 1) / mt);
         for (int g = 0; g < ng; ++g) {
-            const int64_t n = b->host_group_indptr[g + 1] - b->host_group_indptr[g];
+            const int64_t n = members[(size_t)g];
             const int64_t lp = b->host_hot_len[g];
             if (n == 0 || lp == 0 || !mask_get(p->cascade, g)) continue;
             prefix_work += Hkv * ((n * G + mt - 1) / mt) * lp;
@@ -201,7 +204,7 @@ spkv_status make_plan(const spkv_batch *b, const int32_t *cascade, int32_t num_c
         auto blocks_for = [&](int64_t chunk) {
             int64_t nb = 0;
             for (int g = 0; g < ng; ++g) {
-                const int64_t n = b->host_group_indptr[g + 1] - b->host_group_indptr[g];
+                const int64_t n = members[(size_t)g];
                 const int64_t lp = b->host_hot_len[g];
                 if (n == 0 || lp == 0 || !mask_get(p->cascade, g)) continue;
                 nb += Hkv * ((n * G + mt - 1) / mt) *
@@ -241,7 +244,7 @@ spkv_status make_plan(const spkv_batch *b, const int32_t *cascade, int32_t num_c
     for (const auto &f : p->flat) p->flat_items += (int64_t)f.blocks * p->flat_head_groups;
     for (const auto &f : p->pflat) p->prefix_items += (int64_t)f.blocks * p->flat_head_groups;
     for (int g = 0; g < ng; ++g) {
-        const int64_t n = b->host_group_indptr[g + 1] - b->host_group_indptr[g];
+        const int64_t n = members[(size_t)g];
         const int64_t lp = b->host_hot_len[g];
         if (n == 0 || lp == 0) continue;
         if (mask_get(p->cascade, g)) {
@@ -375,7 +378,7 @@ spkv_status spkv_dispatch(const spkv_batch *b, const spkv_dispatch_params *prm, 
         return SPKV_OK;
     case SPKV_MODE_BATCH_GLOBAL: {
         // One batch-wide shared level: only when every request shares group 0's prefix.
-        const bool all_one = ng == 1 && b->host_group_indptr[1] == b->batch && b->batch > 0;
+        const bool all_one = ng == 1 && b->batch > 0 && member_counts(b)[0] == b->batch;
         for (int g = 0; g < ng; ++g) cascade_out[g] = all_one ? 1 : 0;
         return SPKV_OK;
     }
@@ -393,10 +396,11 @@ spkv_status spkv_dispatch(const spkv_batch *b, const spkv_dispatch_params *prm, 
     // step by whichever groups take cascade, so the set of groups with a
     // positive benefit goes cascade exactly when their total benefit exceeds it
     // (this minimises the modelled step time).
+    const std::vector<int64_t> members = member_counts(b);
     double total = 0.0;
     for (int g = 0; g < ng; ++g) {
         cascade_out[g] = 0;
-        const int64_t n = b->host_group_indptr[g + 1] - b->host_group_indptr[g];
+        const int64_t n = members[(size_t)g];
         const double lp = (double)b->host_hot_len[g];
         if (n < prm->min_group_requests || lp <= 0 || b->dtype != SPKV_DTYPE_BF16) continue;
         // Effective M of the group's prefix contraction (Eq. (2) per group).

@@ -273,10 +273,6 @@ class DecodeBatch:
         self.q = q.contiguous()
         self.group_of_h = np.ascontiguousarray(group_of, dtype=np.int32)
         ng = len(group_len)
-        members = [b for g in range(ng) for b in range(B) if self.group_of_h[b] == g]
-        counts = [int(np.sum(self.group_of_h == g)) for g in range(ng)]
-        self.indptr_h = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
-        self.members_h = np.ascontiguousarray(members, dtype=np.int32)
         self.base_h = np.ascontiguousarray(group_base, dtype=np.int64)
         self.len_h = np.ascontiguousarray(group_len, dtype=np.int32)
         self.tables_h = np.ascontiguousarray(block_tables, dtype=np.int32)
@@ -287,8 +283,6 @@ class DecodeBatch:
             return torch.from_numpy(a.copy() if a.size else np.zeros(1, a.dtype)).to(dev)
 
         self.group_of = up(self.group_of_h)
-        self.indptr = up(self.indptr_h)
-        self.members = up(self.members_h)
         self.base = up(self.base_h)
         self.len = up(self.len_h)
         self.tables = up(self.tables_h.reshape(-1))
@@ -297,10 +291,9 @@ class DecodeBatch:
         self.num_groups = ng
         self.struct = A.spkv_batch(
             int(B), int(Hq), int(num_kv_heads), int(d), dtype_code(q), sc, _dp(self.q),
-            ng, _dp(self.group_of), _dp(self.indptr), _dp(self.members), _dp(self.base), _dp(self.len),
+            ng, _dp(self.group_of), _dp(self.base), _dp(self.len),
             self.group_of_h.ctypes.data if B else None,
-            self.indptr_h.ctypes.data if ng else None, self.base_h.ctypes.data if ng else None,
-            self.len_h.ctypes.data if ng else None,
+            self.base_h.ctypes.data if ng else None, self.len_h.ctypes.data if ng else None,
             int(page_size), self.max_blocks, _dp(self.tables), _dp(self.lens), self.lens_h.ctypes.data)
 
     def workspace_size(self) -> int:

@@ -97,3 +97,48 @@ def test_device_ops_validate_before_touching_the_gpu():
     # zero-sized work is a successful no-op
     assert spkv.spkv_reshape_and_cache(null, null, null, 0, null, null, 4, 1, 64, 0, null) == A.SPKV_OK
     assert spkv.spkv_timing_enable(0) == A.SPKV_OK
+
+
+def test_append_tokens_rejects_bad_slots_and_rows_on_the_host():
+    # [PKV] How it works, step 1: a token is written at its slot; a slot outside
+    # the pool (or a block-table row outside the batch) is an error reported
+    # before anything is launched, not a silently skipped write.
+    import ctypes as C
+    import numpy as np
+    fake = C.c_void_p(16)                      # never dereferenced: the checks come first
+    slots = np.array([0, 7, 8], np.int32)      # 8 is outside an 8-slot pool
+    rows = np.array([0, 1, 2], np.int32)
+    sp = slots.ctypes.data_as(C.POINTER(C.c_int32))
+    rp = rows.ctypes.data_as(C.POINTER(C.c_int32))
+    st = spkv.spkv_append_tokens(fake, fake, sp, rp, 3, fake, fake, 8, None, 0, None, 0, 1, 1, 64, 0, None)
+    assert st == A.SPKV_E_INVAL and "outside the COLD pool" in spkv.lib.spkv_last_error().decode()
+    slots[2] = -1
+    assert spkv.spkv_append_tokens(fake, fake, sp, rp, 3, fake, fake, 8, None, 0, None, 0, 1, 1, 64, 0,
+                                   None) == A.SPKV_E_INVAL
+    slots[2] = 3
+    rows[1] = 5                                # only 3 rows in the tables
+    st = spkv.spkv_append_tokens(fake, fake, sp, rp, 3, fake, fake, 8, fake, 4, fake, 3, 1, 1, 64, 0, None)
+    assert st == A.SPKV_E_INVAL and "row" in spkv.lib.spkv_last_error().decode()
+
+
+def test_group_membership_is_group_of_alone():
+    # [GKV] Section 3.4: a request records which prefix (HOT slab) it shares.
+    # The batch descriptor carries only group_of and the per-group slab arrays;
+    # the library forms member lists itself, so there is no second list that
+    # could disagree with group_of.
+    names = [f[0] for f in A.spkv_batch._fields_]
+    assert "group_of" in names and not any("indptr" in n or "member" in n for n in names)
+    import numpy as np
+    import torch
+    from shared_prefix_paged_amd import runtime as R
+    q = torch.zeros((3, 8, 64), dtype=torch.bfloat16)
+    tables = np.zeros((3, 1), np.int32)
+    for bad in ([0, 2, -1], [0, -2, 1]):       # group 2 does not exist; -2 is not "no group"
+        batch = R.DecodeBatch(q, bad, [0, 10], [10, 5], tables, [1, 1, 1], 1, 2)
+        with pytest.raises(spkv.InvalidArgument):
+            batch.plan()
+    # members counted from group_of: two groups of 2 and 1 requests, cascade planned for both
+    batch = R.DecodeBatch(q, [1, 0, 1], [0, 300], [300, 300], tables, [1, 1, 1], 1, 2)
+    fp, pp = batch.plan_parts()
+    assert list(pp > 0) == [True, True, True]
+

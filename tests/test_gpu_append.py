@@ -75,16 +75,24 @@ def test_append_tokens_matches_separate_ops(P, n, forks):
         np.testing.assert_array_equal(lens[1].cpu().numpy(), l_h)
 
 
-def test_append_tokens_skips_out_of_range_slots():
+def test_append_tokens_rejects_out_of_range_slots():
+    # A slot outside the pool is an error reported before any launch: the
+    # pool is untouched (and a good call afterwards writes normally).
+    from shared_prefix_paged_amd import InvalidArgument
     dev = "cuda"
     hkv, d, P = 1, 64, 1
     k = torch.zeros(8 * hkv * d, dtype=torch.float32, device=dev)
     v = torch.zeros_like(k)
     knew = torch.ones((3, hkv, d), dtype=torch.float32, device=dev)
-    R.append_tokens(knew, knew, np.array([-1, 8, 2], np.int32), k, v, 8, P, hkv, d)
+    for bad in ([-1, 3, 2], [0, 8, 2]):
+        with pytest.raises(InvalidArgument):
+            R.append_tokens(knew, knew, np.array(bad, np.int32), k, v, 8, P, hkv, d)
+    torch.cuda.synchronize()
+    assert k.abs().sum().item() == 0 and v.abs().sum().item() == 0
+    R.append_tokens(knew, knew, np.array([5, 3, 2], np.int32), k, v, 8, P, hkv, d)
     torch.cuda.synchronize()
     kk = k.view(8, d).cpu().numpy()
-    assert kk[2].sum() == d and kk.sum() == d
+    assert kk[[2, 3, 5]].sum() == 3 * d and kk.sum() == 3 * d
 
 
 # ---------------------------------------------------------------------------

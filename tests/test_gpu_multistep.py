@@ -117,20 +117,58 @@ class GpuMultiStep:
                              tables, lens, self.P, self.wl.cfg.num_kv_heads), tables, lens
 
 
+class SharedRows:
+    """Copy-on-write invariant on the device ("Paged KV cache" page, Code:
+    fork shares pages, a write to a shared page goes to a private copy):
+    device copies of the fork parents' pre-fork K/V rows (gathered at their
+    slots) and of the HOT pools, taken just before the forks and compared
+    after every later step."""
+
+    def __init__(self, gpu, parents):
+        self.gpu = gpu
+        P = gpu.P
+        slots = []
+        for b in parents:
+            n, _, nb = gpu.cold.seq_info(b)
+            t, _ = gpu.cold.block_tables([b], nb)
+            slots += [int(t[0][i // P]) * P + i % P for i in range(n)]
+        self.idx = torch.tensor(slots, dtype=torch.int64, device=gpu.dev)
+        self.ref = self.snapshot()
+
+    def snapshot(self):
+        pools = self.gpu.pools
+        row = self.gpu.wl.cfg.num_kv_heads * self.gpu.wl.cfg.head_dim
+        k = pools.k_cold.view(-1, row).index_select(0, self.idx)
+        v = pools.v_cold.view(-1, row).index_select(0, self.idx)
+        return k, v, pools.k_hot.clone(), pools.v_hot.clone()
+
+    def unchanged(self):
+        return all(torch.equal(a, b) for a, b in zip(self.snapshot(), self.ref))
+
+
 def run(wl, P, check_rows, modes=(A.SPKV_MODE_PER_GROUP, A.SPKV_MODE_BATCH_GLOBAL), steps=32, seed=5,
         fused=False):
     """fused: the step's tokens are not written beforehand; every attention
     call is spkv_decode_step_append from the pre-append device lengths (the
     block-table entry it writes is already the allocator's, so rewriting it,
-    and landing the same token again for the next mode, changes nothing)."""
+    and landing the same token again for the next mode, changes nothing).
+    check_rows(step, n_live, rng) -> the rows compared with the oracle (None: all)."""
     sim = MultiStepSim(wl, page_size=P)
     gpu = GpuMultiStep(wl, P)
     rng = np.random.default_rng(seed)
     choices_seen = {m: set() for m in modes}
+    shared = None
     for s in range(steps):
         n_live = len(sim.live) + (len(set(g for g in sim.group_of.values() if g >= 0)) if s == sim.fork_step else 0)
         if s == sim.release_step:
             n_live -= len(sim.fork_parents)
+        if s == sim.fork_step:
+            firsts = {}
+            for b in sorted(sim.live):
+                if sim.group_of[b] >= 0:
+                    firsts.setdefault(sim.group_of[b], b)
+            torch.cuda.synchronize()
+            shared = SharedRows(gpu, sorted(firsts.values()))
         dr = W.step_draws(wl.cfg, s, n_live)
         rec = sim.step(dr.k_new, dr.v_new)
         live, slots, cows = gpu.step(dr.k_new, dr.v_new, write=not fused)
@@ -141,8 +179,11 @@ def run(wl, P, check_rows, modes=(A.SPKV_MODE_PER_GROUP, A.SPKV_MODE_BATCH_GLOBA
         for i, b in enumerate(live):
             t = rec.tables[b]
             assert list(tables[i, :len(t)]) == list(t) and int(lens[i]) == rec.lens[b], f"step {s} request {b}"
-        rows = check_rows(len(live), rng)
-        ref_o, ref_l = sim.reference(live, dr.q, rows=rows)
+        rows = check_rows(s, len(live), rng)
+        if rows is None:
+            ref_o, ref_l = sim.reference_grouped(live, dr.q)
+        else:
+            ref_o, ref_l = sim.reference(live, dr.q, rows=rows)
         ws = R.workspace(batch)
         for mode in modes:
             out = torch.empty((len(live), wl.cfg.num_q_heads, wl.cfg.head_dim), dtype=torch.float32, device=gpu.dev)
@@ -161,8 +202,12 @@ def run(wl, P, check_rows, modes=(A.SPKV_MODE_PER_GROUP, A.SPKV_MODE_BATCH_GLOBA
             e_o, e_l, rel = errors(out, lse, ref_o, ref_l, rows=rows)
             assert e_o <= TOL_O and e_l <= TOL_L and rel <= TOL_REL, \
                 f"step {s} mode {mode}: max_abs {e_o:.2e} lse {e_l:.2e} rel {rel:.2e}"
-        if s % 8 == 0:
-            note(f"[gpu] multistep P={P} step {s}: {len(live)} live, {len(cows)} CoW pairs ok")
+        if shared is not None:
+            torch.cuda.synchronize()
+            assert shared.unchanged(), f"step {s}: a pre-fork row or the HOT slab changed"
+        if s % 8 == 0 or rows is None:
+            note(f"[gpu] multistep P={P} step {s}: {len(live)} live, {len(cows)} CoW pairs, "
+                 f"{'all' if rows is None else len(rows)} rows ok")
     evicted_o = sim.finish()
     for b in sorted(gpu.live):
         gpu.cold.release(b)
@@ -188,22 +233,29 @@ def small_workload(seed=21):
 @pytest.mark.parametrize("P", [1, 16])
 def test_multistep_small_all_rows(P):
     note(f"[gpu] multistep small P={P}")
-    run(small_workload(), P, lambda n, rng: list(range(n)))
+    run(small_workload(), P, lambda s, n, rng: None)
 
 
 @pytest.mark.parametrize("P", [1, 16])
 def test_multistep_small_fused_appends(P):
     # forks, releases and copy-on-write with the appends fused into the step
     note(f"[gpu] multistep small fused P={P}")
-    run(small_workload(), P, lambda n, rng: list(range(n)), fused=True)
+    run(small_workload(), P, lambda s, n, rng: None, fused=True)
 
 
-@pytest.mark.timeout(600)
+C4_FULL_STEPS = (0, 8, 9, 24, 25, 31)   # first step, the forks and the step after, the releases and after, last
+
+
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("P", [1, 16])
-def test_multistep_c4_sampled_rows(P):
-    # the full heterogeneous multi-agent run at page size 1 and 16 (copy-on-write after the forks)
+def test_multistep_c4(P):
+    # The full heterogeneous multi-agent run at page size 1 and 16 (copy-on-write
+    # after the forks): every row at the first step, around the forks and the
+    # releases and at the last step; two sampled rows at the other steps; the
+    # copy-on-write invariant on the device after every step from the forks on.
     wl = W.make_workload(W.CONFIGS["C4"], page_size=P)
     note(f"[gpu] multistep C4: B={wl.batch} groups={len(wl.group_prefix_len)} P={P}")
-    seen = run(wl, P, lambda n, rng: sorted(rng.choice(n, size=2, replace=False).tolist()))
+    seen = run(wl, P, lambda s, n, rng: None if s in C4_FULL_STEPS
+               else sorted(rng.choice(n, size=2, replace=False).tolist()))
     # per-group mode takes the cascade for the long shared prefixes
     assert any(all(c) for c in seen[A.SPKV_MODE_PER_GROUP])
