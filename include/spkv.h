@@ -351,6 +351,24 @@ spkv_status spkv_decode_step_append(const spkv_batch *batch, const spkv_kv *kv,
                                     const int32_t *host_slots, float *out, float *lse, void *ws,
                                     size_t ws_bytes, void *stream, int32_t *cascade_out);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * call as spkv_decode_step_append, with the same results, but without a
+ * workspace argument.  The partial states live in a static device array of
+ * SPKV_NOALLOC_SCRATCH_BYTES that the library holds on every device it runs
+ * on until the process ends (its address is looked up once per device with
+ * hipGetSymbolAddress).  The call allocates nothing.  Returns SPKV_E_INVAL,
+ * before any launch, when the step's plan needs more scratch than that
+ * (spkv_plan_query reports workspace_bytes).  Every call on one device uses
+ * the same array: calls that overlap on one device (other streams, other
+ * threads) race and must be serialised by the caller.  Nothing in the array
+ * has to start at zero. */
+#define SPKV_NOALLOC_SCRATCH_BYTES (32u << 20)
+spkv_status spkv_decode_step_append_noalloc(const spkv_batch *batch, const spkv_kv *kv,
+                                            const spkv_dispatch_params *params, const void *k_new,
+                                            const void *v_new, const int32_t *host_slots, float *out, float *lse,
+                                            void *stream, int32_t *cascade_out);
+
 /* ======================================================================
  * Plan inspection and kernel timing (measurement support).
  * ==================================================================== */

@@ -10,6 +10,7 @@ SPKV_OK, SPKV_E_INVAL, SPKV_E_NOMEM, SPKV_E_STATE, SPKV_E_HIP = 0, -1, -2, -3, -
 SPKV_DTYPE_BF16, SPKV_DTYPE_F32 = 0, 1
 SPKV_MODE_PER_GROUP, SPKV_MODE_BATCH_GLOBAL, SPKV_MODE_FORCE_CASCADE, SPKV_MODE_FORCE_DENSE = 0, 1, 2, 3
 SPKV_KERNEL_PREFIX, SPKV_KERNEL_FLAT, SPKV_KERNEL_MERGE, SPKV_KERNEL_CACHE, SPKV_NUM_KERNELS = 0, 1, 2, 3, 4
+SPKV_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class spkv_hot_info(C.Structure):
@@ -90,6 +91,8 @@ SIGNATURES = {
     "spkv_decode_step": (c_i32, [P_batch, P_kv, P_params, c_vp, c_vp, c_vp, c_sz, c_vp, P_i32]),
     "spkv_decode_step_append": (c_i32, [P_batch, P_kv, P_params, c_vp, c_vp, P_i32, c_vp, c_vp, c_vp, c_sz, c_vp,
                                         P_i32]),
+    "spkv_decode_step_append_noalloc": (c_i32, [P_batch, P_kv, P_params, c_vp, c_vp, P_i32, c_vp, c_vp, c_vp,
+                                                P_i32]),
     "spkv_plan_query": (c_i32, [P_batch, P_i32, C.POINTER(spkv_plan_info)]),
     "spkv_plan_parts": (c_i32, [P_batch, P_i32, P_i32, P_i32]),
     "spkv_timing_enable": (c_i32, [c_i32]),

@@ -1796,6 +1796,45 @@ spkv_status run_decode(const spkv_batch *b, const spkv_kv *kv, const int32_t *ca
     return SPKV_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Static scratch for spkv_decode_step_append_noalloc: the partial states of the
+// split plan live in this file-scope device array instead of a caller
+// workspace.  Host code never passes the array's name to a kernel (on the host
+// it is only a stand-in symbol); it uses the device address that
+// hipGetSymbolAddress returns, looked up once per device with that device
+// current.  Every call on one device shares the array.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = SPKV_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) u32x4_t scratch[kScratchBytes / sizeof(u32x4_t)];
+
+constexpr int kMaxDevices = 64;
+struct ScratchTable {
+    std::mutex mu;
+    void *ptr[kMaxDevices] = {};
+};
+ScratchTable &scratch_table() {
+    static ScratchTable t;
+    return t;
+}
+
+spkv_status scratch_address(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(SPKV_E_HIP, std::string("noalloc: no current device: ") + hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(SPKV_E_HIP, "noalloc: device index beyond the scratch table");
+    ScratchTable &t = scratch_table();
+    std::lock_guard<std::mutex> g(t.mu);
+    if (!t.ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(SPKV_E_HIP, std::string("noalloc: scratch address lookup failed: ") + hipGetErrorString(e));
+        t.ptr[dev] = p;
+    }
+    *out = t.ptr[dev];
+    return SPKV_OK;
+}
+
 spkv_status check_kv_shape(int32_t hkv, int32_t d, int32_t dtype) {
     if (hkv < 1 || hkv > spkv::kMaxKvHeads) return fail(SPKV_E_INVAL, "num_kv_heads must be 1..16");
     if (d != 64 && d != 128) return fail(SPKV_E_INVAL, "head_dim must be 64 or 128");
@@ -1963,6 +2002,29 @@ spkv_status spkv_decode_step_append(const spkv_batch *batch, const spkv_kv *kv, 
         for (int g = 0; g < batch->num_groups; ++g) cascade_out[g] = choice[(size_t)g];
     const AppendIn app{k_new, v_new, host_slots};
     return run_decode(batch, kv, choice.data(), out, lse, ws, ws_bytes, stream, &app);
+}
+
+spkv_status spkv_decode_step_append_noalloc(const spkv_batch *batch, const spkv_kv *kv,
+                                            const spkv_dispatch_params *params, const void *k_new,
+                                            const void *v_new, const int32_t *host_slots, float *out, float *lse,
+                                            void *stream, int32_t *cascade_out) {
+    spkv_status st = spkv::validate_batch(batch, kv);
+    if (st != SPKV_OK) return st;
+    std::vector<int32_t> choice((size_t)std::max(1, batch->num_groups), 0);
+    st = spkv_dispatch(batch, params, choice.data());
+    if (st != SPKV_OK) return st;
+    Plan p;
+    st = spkv::make_plan(batch, choice.data(), spkv::kPlanCUs, &p);
+    if (st != SPKV_OK) return st;
+    if ((size_t)p.ws_bytes > kScratchBytes)
+        return fail(SPKV_E_INVAL, "decode_step_append_noalloc: the plan needs " + std::to_string(p.ws_bytes) +
+                                      " bytes of scratch, more than the static " +
+                                      std::to_string(kScratchBytes) + " (use spkv_decode_step_append)");
+    void *ws = nullptr;
+    st = scratch_address(&ws);
+    if (st != SPKV_OK) return st;
+    return spkv_decode_step_append(batch, kv, params, k_new, v_new, host_slots, out, lse, ws, kScratchBytes, stream,
+                                   cascade_out);
 }
 
 spkv_status spkv_merge_states(const float *o_a, const float *lse_a, const float *o_b, const float *lse_b, float *o,

@@ -388,6 +388,19 @@ def decode_step_append(batch: DecodeBatch, kv: KVPools, params: A.spkv_dispatch_
     return out, lse, choice[:batch.num_groups]
 
 
+def decode_step_append_noalloc(batch: DecodeBatch, kv: KVPools, params: A.spkv_dispatch_params, k_new, v_new,
+                               slots: np.ndarray, out=None, lse=None, stream=None):
+    """spkv_decode_step_append_noalloc: decode_step_append without a workspace
+    (the library's static per-device scratch holds the partial states)."""
+    out, lse = _outputs(batch, out, lse)
+    choice = np.zeros(max(batch.num_groups, 1), np.int32)
+    slots = np.ascontiguousarray(slots, dtype=np.int32)
+    check(lib.spkv_decode_step_append_noalloc(C.byref(batch.struct), C.byref(kv.struct), C.byref(params),
+                                              _dp(k_new), _dp(v_new), _ptr(slots, C.c_int32), _dp(out), _dp(lse),
+                                              stream_handle(stream), _ptr(choice, C.c_int32)))
+    return out, lse, choice[:batch.num_groups]
+
+
 def merge_states(o_a, lse_a, o_b, lse_b, out=None, lse=None, stream=None):
     torch = _torch()
     rows, d = o_a.shape

@@ -142,3 +142,20 @@ def test_group_membership_is_group_of_alone():
     fp, pp = batch.plan_parts()
     assert list(pp > 0) == [True, True, True]
 
+
+def test_noalloc_rejects_plans_beyond_its_scratch_before_launching():
+    # The entry point without a workspace refuses, on the host, a step whose
+    # plan needs more than its static scratch (2048 requests x 32 heads).
+    import torch
+    from shared_prefix_paged_amd import runtime as R
+    B = 2048
+    q = torch.zeros((B, 32, 128), dtype=torch.bfloat16)
+    batch = R.DecodeBatch(q, [0] * B, [0], [4096], np.zeros((B, 64), np.int32), [60] * B, 1, 8)
+    assert batch.plan().workspace_bytes > A.SPKV_NOALLOC_SCRATCH_BYTES
+    fake = C.c_void_p(16)
+    kv = A.spkv_kv(16, 16, 4096, 16, 16, 1 << 20)
+    slots = np.arange(B, dtype=np.int32)
+    st = spkv.spkv_decode_step_append_noalloc(C.byref(batch.struct), C.byref(kv),
+                                              C.byref(R.default_params()), fake, fake,
+                                              slots.ctypes.data_as(C.POINTER(C.c_int32)), fake, fake, None, None)
+    assert st == A.SPKV_E_INVAL and "static" in spkv.lib.spkv_last_error().decode()
