@@ -53,16 +53,20 @@ def parse():
     ap.add_argument("--flush-mib", type=int, default=1024, help="bytes written before each cold-cache run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
-                    help="measured HBM traffic per launch (written by shared_prefix_paged_amd/profile_step.py)")
+                    help="measured HBM traffic per launch (written by profile_step.py)")
     ap.add_argument("--sweep-lp", default=None, metavar="L1,L2,...",
                     help="time cascade and dense attention at each prefix length (C3 crossover sweep) and exit")
     ap.add_argument("--sweep-batch", default=None, metavar="B1,B2,...",
                     help="time cascade and dense attention at each number of requests sharing the prefix "
                          "(at the configuration's or --lp's prefix length) and exit")
+    ap.add_argument("--graph-steps", type=int, default=20,
+                    help="after the timed steps, this many steps through the HIP-graph entry point "
+                         "(spkv_graph_decode_step_append), timed the same way (0: skip)")
     ap.add_argument("--separate-append", action="store_true",
                     help="append the step's K/V with its own launch (spkv_append_tokens) before the decode step")
     ap.add_argument("--layers", type=int, default=1,
-                    help="with L > 1: a decode step over L layers (per-layer pools, shared slots); own JSON line")
+                    help="with L > 1: a decode step over L layers (one layer-strided HOT and COLD allocation, "
+                         "shared slots); own JSON line")
     ap.add_argument("--admission-sweep", default=None, metavar="F1,F2,...",
                     help="time the multi-agent batch with the HOT pool at each fraction of the total prefix "
                          "length (groups that do not fit fall back to COLD) and exit")
@@ -71,6 +75,9 @@ def parse():
     ap.add_argument("--layout-batch", type=int, default=256, help="requests sharing the prefix in --layout-study")
     ap.add_argument("--layout-variant", default=None, choices=["hot_cascade", "hot_flat", "private_flat"],
                     help="only this variant of --layout-study (one per counter run)")
+    ap.add_argument("--multistep", action="store_true",
+                    help="the multi-agent run (C4 recipe): 32 decode steps with forks at step 8 and releases at "
+                         "step 24, per-group vs batch-global dispatch, COLD page size 1 and 16; one JSON line")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-MiB device buffer 5 times (counter calibration) and exit")
     return ap.parse_args()
@@ -265,12 +272,15 @@ def layout_study(args) -> int:
 
 
 def multi_layer(args) -> int:
-    """A decode step over L layers of one model: per-layer HOT slabs and COLD
-    pools (the same slots in every layer), one host append per step, then per
-    layer the K/V write and the attention call.  The step touches L times one
-    layer's K/V, far more than the caches hold, so nothing is reused from the
-    previous step.  One JSON line: KV tokens attended per second over all
-    layers, and per-layer times."""
+    """A decode step over L layers of one model, the layers sharing one HOT
+    and one COLD allocation with the GraniKV paper's layer stride (Section
+    3.2: head h of layer l of a slab at row base*Hkv*L + l*Lp*Hkv + h*Lp; COLD
+    layer-major with the same slots in every layer): one host append per step,
+    one copy-on-write launch for all layers, then per layer the K/V write and
+    the attention call.  The step touches L times one layer's K/V, far more
+    than the caches hold, so nothing is reused from the previous step.  One
+    JSON line: KV tokens attended per second over all layers, and per-layer
+    times."""
     import numpy as np
     import torch
     import workloads as W
@@ -286,18 +296,14 @@ def multi_layer(args) -> int:
                          extra_steps=max(32, total_steps + 1))
     cfg = wl.cfg
     B, Hq, Hkv, d, P = wl.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.page_size
-    st = setup_single_step(wl, device=dev, max_blocks=(int(wl.suffix_len.max()) + total_steps + P - 1) // P + 1)
-    batch, cold = st.batch, st.cold
-    layers = [st.pools]
-    for _ in range(1, L):                        # the same contents at other addresses
-        p0 = st.pools
-        pl = R.KVPools.allocate(p0.hot_capacity, p0.cold_slots, Hkv, d, p0.k_cold.dtype, dev)
-        for dst, src in ((pl.k_hot, p0.k_hot), (pl.v_hot, p0.v_hot), (pl.k_cold, p0.k_cold), (pl.v_cold, p0.v_cold)):
-            dst.copy_(src)
-        layers.append(pl)
+    st = setup_single_step(wl, device=dev, max_blocks=(int(wl.suffix_len.max()) + total_steps + P - 1) // P + 1,
+                           num_layers=L)
+    batch, cold, pools = st.batch, st.cold, st.pools
+    per_layer = [pools.at_layer(li) for li in range(L)]
+    cold_views = [pools.cold_layer(li) for li in range(L)]
     gen = torch.Generator(device=dev)
     gen.manual_seed(106)
-    qs = [torch.randn((B, Hq, d), generator=gen, device=dev).to(layers[0].k_cold.dtype) for _ in range(L)]
+    qs = [torch.randn((B, Hq, d), generator=gen, device=dev).to(pools.k_cold.dtype) for _ in range(L)]
     kv_new = []
     for s_ in range(total_steps):
         dr = W.step_draws(cfg, s_, B)
@@ -315,18 +321,19 @@ def multi_layer(args) -> int:
         i = state["i"]
         slots, cows = cold.append_batch(seqs)
         k, v = kv_new[i]
-        for li, pl in enumerate(layers):
-            if cows:
-                R.copy_blocks(torch.tensor(cows, dtype=torch.int32, device=dev), pl.k_cold, pl.v_cold,
-                              cold.num_pages, P, Hkv, d)
+        if cows:                                   # one launch copies the pages in every layer
+            R.copy_blocks(torch.tensor(cows, dtype=torch.int32, device=dev), pools.k_cold, pools.v_cold,
+                          cold.num_pages, P, Hkv, d, num_layers=L)
+        for li in range(L):
+            kc, vc = cold_views[li]
             # layer 0 also appends to the (shared) device block tables and lengths
-            R.append_tokens(k, v, slots, pl.k_cold, pl.v_cold, pl.cold_slots, P, Hkv, d,
+            R.append_tokens(k, v, slots, kc, vc, pools.cold_slots, P, Hkv, d,
                             tables=batch.tables if li == 0 else None, max_blocks=mb if li == 0 else 0,
                             lens=batch.lens if li == 0 else None)
         batch.lens_h += 1
-        for li, pl in enumerate(layers):
+        for li in range(L):
             batch.struct.q = qs[li].data_ptr()
-            R.decode_step(batch, pl, params, ws, out, lse)
+            R.decode_step(batch, per_layer[li], params, ws, out, lse)
         state["i"] = i + 1
         return L * int(np.sum(lp_of + batch.lens_h))
 
@@ -357,11 +364,128 @@ def multi_layer(args) -> int:
         "ms_per_step": round(1e3 * wall / args.steps, 4), "gpu_ms_per_step": round(gpu_ms / args.steps, 4),
         "us_per_layer": round(1e3 * gpu_ms / args.steps / L, 2), "higher_is_better": True, "dtype": cfg.dtype,
         "data": "synthetic",
-        "config": {"workload": f"{cfg.name} layer shape x {L} layers (per-layer HOT slab and COLD pool, shared slots)",
+        "config": {"workload": f"{cfg.name} layer shape x {L} layers (one HOT and one COLD allocation, "
+                               "layer-strided slabs, shared slots)",
                    "layers": L, "batch": B, "prefix_len": [int(x) for x in wl.group_prefix_len], "page_size": P},
         "kernels_avg_us": {k: round(1e3 * v[0] / v[1], 2) for k, v in per.items() if v[1]},
-        "hbm_bytes_held": int(sum(t.numel() * t.element_size() for pl in layers
-                                  for t in (pl.k_hot, pl.v_hot, pl.k_cold, pl.v_cold)))}), flush=True)
+        "hbm_bytes_held": int(sum(t.numel() * t.element_size()
+                                  for t in (pools.k_hot, pools.v_hot, pools.k_cold, pools.v_cold)))}), flush=True)
+    return 0
+
+
+def multistep(args) -> int:
+    """The heterogeneous multi-agent run as the GraniKV paper measures it
+    (Section 4.5 Table 4, Appendix B.8b Table 21: several prefix groups,
+    per-group dispatch against one batch-global decision): the C4 recipe (8
+    groups x 16 requests, Lp_g ~ U[2048, 16384], Ls ~ U[128, 4096], Llama-3.1-8B
+    layer), 32 decode steps; before the appends of step 8 the first request of
+    every group forks (COLD fork + HOT reference), at step 24 those parents are
+    released; every step appends one token per live request (host allocator,
+    copy-on-write copies, the new K/V fused into the step).  The schedule runs
+    once per (page size, dispatch mode) from the same initial state, so both
+    modes see identical pools.  Per run: attention time per step (sum of the
+    attention kernels' event durations) and KV tokens attended; one JSON line.
+    Timing only (the same schedule is parity-checked against the oracle by the
+    GPU tests)."""
+    import numpy as np
+    import torch
+    import workloads as W
+    from shared_prefix_paged_amd import runtime as R
+    from shared_prefix_paged_amd import _abi as A
+    from hip_setup import setup_single_step, to_device
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    steps, fork_step, release_step = 32, 8, 24
+    attn_ids = (A.SPKV_KERNEL_PREFIX, A.SPKV_KERNEL_FLAT, A.SPKV_KERNEL_MERGE)
+    runs = {}
+    for P in (1, 16):
+        wl = W.make_workload(W.CONFIGS["C4"], page_size=P, extra_steps=40)
+        cfg = wl.cfg
+        B, Hq, Hkv, d = wl.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim
+        mb = (int(wl.suffix_len.max()) + steps + P - 1) // P + 2
+        draws = []
+        n_live = B
+        for s_ in range(steps):
+            n_live += 8 if s_ == fork_step else (-8 if s_ == release_step else 0)
+            dr = W.step_draws(cfg, s_, n_live)
+            draws.append((to_device(dr.k_new, cfg.dtype, dev), to_device(dr.v_new, cfg.dtype, dev),
+                          to_device(dr.q, cfg.dtype, dev)))
+        for mode_name, mode in (("per_group", A.SPKV_MODE_PER_GROUP), ("batch_global", A.SPKV_MODE_BATCH_GLOBAL)):
+            st = setup_single_step(wl, device=dev, max_blocks=mb)
+            hot, cold, pools = st.hot, st.cold, st.pools
+            group_of = {b: int(wl.group_of[b]) for b in range(B)}
+            live = list(range(B))
+            parents = []
+            params = R.default_params(mode)
+            out = torch.empty((B + 8, Hq, d), dtype=torch.float32, device=dev)
+            lse = torch.empty((B + 8, Hq), dtype=torch.float32, device=dev)
+            ws = None
+            batch = None
+            recs = []
+            quiet_gc()
+            for s_ in range(steps):
+                if s_ == fork_step:
+                    firsts = {}
+                    for b in sorted(live):
+                        firsts.setdefault(group_of[b], b)
+                    for g in sorted(firsts):
+                        c = cold.fork(firsts[g])
+                        hot.incref(st.bases[g])
+                        group_of[c] = g
+                        live.append(c)
+                        parents.append(firsts[g])
+                if s_ == release_step:
+                    for p in parents:
+                        cold.release(p)
+                        hot.decref(st.bases[group_of[p]])
+                        live.remove(p)
+                live.sort()
+                if batch is None or s_ in (fork_step, release_step):
+                    tables, lens = cold.block_tables(live, mb)
+                    batch = R.DecodeBatch(draws[s_][2], [group_of[b] for b in live], st.bases, wl.group_prefix_len,
+                                          tables, lens, P, Hkv)
+                    ws = torch.empty(batch.workspace_size(), dtype=torch.uint8, device=dev)
+                k_new, v_new, q = draws[s_]
+                slots, cows = cold.append_batch(live)
+                if cows:
+                    R.copy_blocks(torch.tensor(cows, dtype=torch.int32, device=dev), pools.k_cold, pools.v_cold,
+                                  cold.num_pages, P, Hkv, d)
+                batch.lens_h += 1
+                batch.struct.q = q.data_ptr()
+                n = len(live)
+                with R.KernelTimer() as kt:
+                    _, _, choice = R.decode_step_append(batch, pools, params, ws, k_new, v_new, slots, out[:n],
+                                                        lse[:n])
+                    torch.cuda.synchronize()
+                    us = 1e3 * sum(kt.read(k)[0] for k in attn_ids)
+                tokens = int(sum(int(wl.group_prefix_len[group_of[b]]) if group_of[b] >= 0 else 0 for b in live)
+                             + int(batch.lens_h.sum()))
+                recs.append({"step": s_, "live": n, "cow_pairs": len(cows), "groups_cascade": int(np.sum(choice)),
+                             "attention_us": round(us, 2), "kv_tokens": tokens})
+            assert torch.isfinite(out).all()
+            t = np.array([r["attention_us"] for r in recs])
+            tok = np.array([r["kv_tokens"] for r in recs])
+            runs[f"P{P}/{mode_name}"] = {
+                "mean_attention_us": round(float(t.mean()), 2),
+                "kv_tokens_per_s": round(float(tok.sum() / (t.sum() * 1e-6)), 1),
+                "steps_0_7_us": round(float(t[:fork_step].mean()), 2),
+                "steps_8_23_us": round(float(t[fork_step:release_step].mean()), 2),
+                "steps_24_31_us": round(float(t[release_step:].mean()), 2),
+                "cow_pairs": int(sum(r["cow_pairs"] for r in recs)),
+                "groups_cascade_per_step": sorted({r["groups_cascade"] for r in recs}),
+                "per_step": recs}
+            print(f"[multistep] P={P} {mode_name}: {runs[f'P{P}/{mode_name}']['mean_attention_us']} us/step "
+                  f"{runs[f'P{P}/{mode_name}']['kv_tokens_per_s']:.3g} KV-tok/s", file=sys.stderr, flush=True)
+            del st, batch, ws, out, lse
+            torch.cuda.empty_cache()
+    ratio = {f"P{P}": round(runs[f"P{P}/batch_global"]["mean_attention_us"] / runs[f"P{P}/per_group"]["mean_attention_us"], 3)
+             for P in (1, 16)}
+    print(json.dumps({"metric": "multi-agent decode: attention time per step, per-group vs batch-global dispatch",
+                      "unit": "us", "config": {"workload": "C4 recipe: 8 groups x 16 requests, Lp_g~U[2048, 16384], "
+                                                           "Ls~U[128, 4096], Hq=32, Hkv=8, d=128, bf16, shuffled slots; "
+                                                           "32 steps, forks at 8, releases at 24"},
+                      "speedup_per_group_over_batch_global": ratio, "runs": runs}), flush=True)
     return 0
 
 
@@ -490,6 +614,8 @@ def main():
         return layout_study(args)
     if args.layers > 1:
         return multi_layer(args)
+    if args.multistep:
+        return multistep(args)
     if args.admission_sweep:
         return admission_sweep(args)
     if args.gpus != 1:
@@ -511,7 +637,9 @@ def main():
     dev = torch.device("cuda:0")
     cfg = W.CONFIGS[args.config]
     cold_warm = 10 if args.cold_runs > 0 else 0
-    total_steps = args.warmup + 2 * args.steps + 1 + cold_warm + max(0, args.cold_runs)
+    graph_steps = max(0, args.graph_steps)
+    total_steps = args.warmup + 2 * args.steps + 1 + cold_warm + max(0, args.cold_runs) + \
+        (graph_steps + 3 if graph_steps else 0)
     wl = W.make_workload(cfg, prefix_len=args.lp, page_size=args.page_size, extra_steps=max(32, total_steps + 1))
     if args.contiguous:
         wl.free_order = None
@@ -544,9 +672,13 @@ def main():
     state = {"i": 0, "choice": None}
     separate = args.separate_append or cfg.dtype != "bf16"     # the fused step is bf16 only
 
-    def one_step(flush=None):
+    host = {"append_s": 0.0, "call_s": 0.0, "n": 0}
+
+    def one_step(flush=None, graph=None):
         i = state["i"]
+        h0 = time.perf_counter()
         slots, cows = cold.append_batch(seqs)                       # host allocator
+        host["append_s"] += time.perf_counter() - h0
         if cows:
             R.copy_blocks(torch.tensor(cows, dtype=torch.int32, device=dev), pools.k_cold, pools.v_cold,
                           cold.num_pages, P, Hkv, d)
@@ -558,10 +690,17 @@ def main():
         batch.struct.q = q_steps[i].data_ptr()
         if flush is not None:
             flush()                                                  # outside the event window
-        if separate:
+        h1 = time.perf_counter()
+        if graph is not None:
+            _, _, choice, inst = graph.decode_step_append(batch, pools, params, ws, k_steps[i], v_steps[i], slots,
+                                                          out, lse)
+            state["instantiations"] = state.get("instantiations", 0) + int(inst)
+        elif separate:
             _, _, choice = R.decode_step(batch, pools, params, ws, out, lse)
         else:
             _, _, choice = R.decode_step_append(batch, pools, params, ws, k_steps[i], v_steps[i], slots, out, lse)
+        host["call_s"] += time.perf_counter() - h1                  # dispatch + plan + launches (asynchronous)
+        host["n"] += 1
         state["choice"] = choice
         state["i"] = i + 1
         return int(np.sum(lp_of + batch.lens_h))                     # logical KV tokens attended
@@ -570,6 +709,7 @@ def main():
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
+    host.update(append_s=0.0, call_s=0.0, n=0)
 
     # ---- timed region: exactly `steps` steps --------------------------------
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -585,6 +725,29 @@ def main():
     gpu_ms = ev0.elapsed_time(ev1)
     ms_per_step = 1e3 * wall / args.steps
     value = tokens / wall
+    host_step = {"append_batch_us": round(1e6 * host["append_s"] / host["n"], 2),
+                 "decode_call_us": round(1e6 * host["call_s"] / host["n"], 2)}
+    # The dispatcher and the plan alone (host only, pure): the per-step
+    # decision of the GraniKV paper's Section 3.6 and the split plan.
+    reps = 2000
+    hd0 = time.perf_counter()
+    for _ in range(reps):
+        R.dispatch(batch, params)
+    hd1 = time.perf_counter()
+    for _ in range(reps):
+        batch.plan()
+    hd2 = time.perf_counter()
+    from shared_prefix_paged_amd import lib as _lib
+    for _ in range(reps):
+        _lib.spkv_version()
+    hd3 = time.perf_counter()
+    host_step["dispatch_us"] = round(1e6 * (hd1 - hd0) / reps, 3)
+    host_step["plan_us"] = round(1e6 * (hd2 - hd1) / reps, 3)
+    host_step["empty_ctypes_call_us"] = round(1e6 * (hd3 - hd2) / reps, 3)
+    host_step["note"] = ("decode_call_us: host time of the spkv call that dispatches, plans and enqueues the step's "
+                         "kernels (they run asynchronously); dispatch_us / plan_us: spkv_dispatch and "
+                         "spkv_plan_query alone, each from Python through ctypes (call overhead included; "
+                         "empty_ctypes_call_us is a call that does nothing, for comparison)")
 
     # ---- per-kernel durations from HIP events on the launch stream ----------
     # (the plan's per-request partial-state counts are recorded at every step
@@ -596,10 +759,39 @@ def main():
             choice = state["choice"]
             casc = list(map(int, choice)) if len(choice) else None
             fp, pp = batch.plan_parts(casc)
-            per_step.append((batch.lens_h.copy(), fp, pp, bool(len(choice) and choice[0])))
+            per_step.append((batch.lens_h.copy(), fp, pp, [int(c) for c in choice]))
         torch.cuda.synchronize()
     kt_ms = {k: kt.read(k) for k in (A.SPKV_KERNEL_PREFIX, A.SPKV_KERNEL_FLAT, A.SPKV_KERNEL_MERGE,
                                      A.SPKV_KERNEL_CACHE)}
+
+    # ---- the same steps through the HIP-graph entry point: host time of the
+    # call (record, update the graph's kernel nodes in place, launch) and GPU
+    # time per step, next to the direct call's figures above.
+    graph_res = None
+    if graph_steps and not separate:
+        g = R.StepGraph()
+        for _ in range(3):
+            one_step(graph=g)
+        torch.cuda.synchronize()
+        host.update(append_s=0.0, call_s=0.0, n=0)
+        state["instantiations"] = 0
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        tg = time.perf_counter()
+        g0.record()
+        for _ in range(graph_steps):
+            one_step(graph=g)
+        g1.record()
+        torch.cuda.synchronize()
+        gwall = time.perf_counter() - tg
+        graph_res = {"steps": graph_steps, "ms_per_step": round(1e3 * gwall / graph_steps, 4),
+                     "gpu_ms_per_step": round(g0.elapsed_time(g1) / graph_steps, 4),
+                     "graph_call_us": round(1e6 * host["call_s"] / host["n"], 2),
+                     "direct_call_us": host_step["decode_call_us"],
+                     "instantiations": int(state["instantiations"]),
+                     "note": "graph_call_us: host time of spkv_graph_decode_step_append (record the step, update the "
+                             "instantiated graph's kernel nodes, launch); instantiations: steps whose launches "
+                             "differed from the graph's (re-instantiated instead of updated)"}
+        g.close()
 
     # ---- cold-cache protocol: the last-level cache (256 MB) and the L2s are
     # flushed by a large write (then a read of another buffer, so the flush's
@@ -646,9 +838,11 @@ def main():
                 "window": "sum of the attention kernels' event durations, after a write of flush_bytes "
                           "and a read of as many other bytes have completed",
                 "warm_attention_us": None}
-    choice = state["choice"]
-    cascade = bool(len(choice) and choice[0])
-    plan = batch.plan(list(map(int, choice)) if len(choice) else None)
+    choice = [int(c) for c in state["choice"]]
+    n_casc = sum(choice)
+    backend = "cascade" if choice and n_casc == len(choice) else ("dense" if n_casc == 0 else
+                                                                  f"mixed: {n_casc} of {len(choice)} groups cascade")
+    plan = batch.plan(choice if choice else None)
 
     # Algorithmic bytes / FLOPs of one launch, averaged over the profiled steps
     # (the lengths grow by one token per step).  Paged pass: K and V rows of
@@ -658,15 +852,17 @@ def main():
     # every partial state, then O and LSE.
     rows = B * Hq
     flat_b, prefix_b, prefix_f, merge_b = [], [], [], []
-    for L, fp, pp, casc in per_step:
-        Lf = L + (np.zeros(B, np.int64) if casc else lp_of)
+    for L, fp, pp, ch in per_step:
+        # the per-group choice: members of a group that takes the flat pass read its prefix there
+        flat_member = np.array([g >= 0 and not ch[g] for g in wl.group_of], dtype=bool)
+        Lf = L + np.where(flat_member, lp_of, 0)
         part_bytes = Hq * int(fp.sum()) * (d + 1) * 4
         flat_b.append(int(Lf.sum()) * kvb + 4 * int(np.sum(-(-L // P))) + Hq * int(fp.sum()) * d * esz + part_bytes)
         pb = pf = ppart = 0.0
-        if casc:
+        if any(ch):
             for g, lp in enumerate(wl.group_prefix_len):
                 members = np.flatnonzero(wl.group_of == g)
-                if lp <= 0 or len(members) == 0:
+                if lp <= 0 or len(members) == 0 or not ch[g]:
                     continue
                 npf = int(pp[members[0]])
                 pb += int(lp) * kvb + len(members) * Hq * d * esz + len(members) * Hq * npf * (d + 1) * 4
@@ -702,7 +898,15 @@ def main():
         roofline = {"bound": "hbm", "achieved": dk["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(dk["gbps"] / HBM_PEAK_GBPS, 4), "traffic": None}
     roofline["kernel"] = dom
-    roofline["traffic"] = measured_traffic(args.traffic, args.config, args.mode, dom)
+    roofline["traffic"] = measured_traffic(args.traffic, args.config if args.lp is None else f"{args.config}@{args.lp}",
+                                           args.mode, dom)
+    if roofline["traffic"]:
+        # HBM bytes the counters saw (L2 <-> fabric) over the same duration:
+        # for the flat pass over a shared slab the algorithmic bytes count every
+        # request's re-read of the prefix, most of which the caches serve.
+        tg = roofline["traffic"] / dk["avg_us"] / 1e3
+        roofline["traffic_gbps"] = round(tg, 1)
+        roofline["traffic_frac"] = round(tg / HBM_PEAK_GBPS, 4)
     attn_us = sum(k["avg_us"] for k in kernels.values())
     if cold_res is not None:
         cold_res["warm_attention_us"] = round(attn_us, 2)
@@ -744,13 +948,15 @@ def main():
                         f"COLD page size {P}, {'contiguous' if args.contiguous else 'shuffled'} slots",
             "batch": B, "prefix_len": [int(x) for x in wl.group_prefix_len], "page_size": P,
             "slots": "contiguous" if args.contiguous else "shuffled",
-            "backend": ("cascade" if cascade else "dense"), "mode": args.mode,
+            "backend": backend, "mode": args.mode,
             "append": "separate launch" if separate else "fused into the step",
         },
         "gpu_ms_per_step": round(gpu_ms / args.steps, 4),
         "attention_us_per_step": round(attn_us, 2),
         "kv_tokens_per_s_attention": round(tokens / args.steps / (attn_us * 1e-6), 1),
         "kernels": kernels,
+        "host": host_step,
+        "graph": graph_res,
         "plan": {f: int(getattr(plan, f)) for f, _ in plan._fields_},
         "roofline": roofline,
         "step_roofline": step_roofline,
@@ -763,11 +969,15 @@ def main():
 
 
 def cpu_baseline(wl, budget_s: float, threads=None):
-    """The oracle, untuned, on the host cores: fp64 attention per request,
-    cycling over the workload's requests, until the budget is spent.
-    threads=1 limits the BLAS pools to one thread."""
+    """The oracle, untuned, on the host cores: fp64 attention per request
+    (decode_request over the logical concatenation of prefix and suffix),
+    cycling over the workload's requests until the budget is spent.  Each
+    group's prefix is widened to float64 once, before the clock starts (it is
+    shared by the group's requests); a request's own suffix and queries are
+    widened inside the timed loop.  threads=1 limits the BLAS pools to one
+    thread."""
     import contextlib
-    from oracle.attention import decode_reference
+    from oracle.attention import decode_request, widen
     limit = contextlib.nullcontext()
     try:
         from threadpoolctl import threadpool_info, threadpool_limits
@@ -777,18 +987,27 @@ def cpu_baseline(wl, budget_s: float, threads=None):
     except Exception:
         pool = os.cpu_count() or 1
     cores = 1 if threads == 1 else min(pool, len(os.sched_getaffinity(0)))
-    done, tokens, t0 = 0, 0, time.perf_counter()
+    cfg = wl.cfg
+    scale = 1.0 / float(cfg.head_dim) ** 0.5
+    pk = [widen(k, cfg.dtype) for k in wl.prefix_k]
+    pv = [widen(v, cfg.dtype) for v in wl.prefix_v]
+    done, tokens = 0, 0
     order = list(range(wl.batch))
     with limit:
+        t0 = time.perf_counter()
         while done == 0 or time.perf_counter() - t0 < budget_s:
             b = order[done % len(order)]
-            decode_reference(wl, rows=[b])
+            g = int(wl.group_of[b])
+            sk, sv = wl.suffix_kv(b)
+            decode_request(widen(wl.q[b], cfg.dtype), pk[g] if g >= 0 else None, pv[g] if g >= 0 else None,
+                           widen(sk, cfg.dtype), widen(sv, cfg.dtype), scale, cfg.group_size)
             tokens += wl.prefix_len_of(b) + int(wl.suffix_len[b])
             done += 1
-    el = time.perf_counter() - t0
+        el = time.perf_counter() - t0
     return {"value": round(tokens / el, 1), "unit": "KV-tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{done} requests ({done / wl.batch:.2f} passes over the {wl.batch} requests of the same "
-                      f"workload, all query heads, prefix + suffix), fp64 numpy, {el:.1f} s"}
+                      f"workload, all query heads, prefix + suffix; each group's prefix widened to fp64 once "
+                      f"beforehand), fp64 numpy, {el:.1f} s"}
 
 
 if __name__ == "__main__":

@@ -27,13 +27,17 @@
  *     allocate device memory: scratch space is the caller's workspace.
  *   - Layouts (row-major, element type per `dtype`):
  *       Q        [B, Hq, d]
- *       HOT      per pool: [capacity_tokens * Hkv * d]; a prefix of length Lp
- *                admitted at token slot `base` keeps head h's rows as one
- *                dense [Lp, d] matrix starting at row base*Hkv + h*Lp
- *                ([GKV] Section 3.2 stride, one layer).
- *       COLD     per pool: [num_pages * page_size, Hkv, d]; token t of a
- *                sequence lives at slot table[t / P] * P + t % P
- *                ([PKV] How it works).
+ *       HOT      per pool of L layers: [capacity_tokens * L * Hkv * d]; a
+ *                prefix of length Lp admitted at token slot `base` keeps
+ *                head h of layer l as one dense [Lp, d] matrix starting at
+ *                row base*Hkv*L + l*Lp*Hkv + h*Lp ([GKV] Section 3.2 stride:
+ *                the slab holds all L layers of the prefix, layer-major).
+ *       COLD     per pool of L layers: [L, num_pages * page_size, Hkv, d]
+ *                (layer-major; every layer uses the same slots and block
+ *                tables); token t of a sequence lives at slot
+ *                table[t / P] * P + t % P ([PKV] How it works).
+ *                One layer's COLD pool starts at element
+ *                layer * num_pages * page_size * Hkv * d.
  *       out      [B, Hq, d] float32 (normalised attention output)
  *       lse      [B, Hq] float32, natural-log log-sum-exp of the scaled scores
  *   - GQA: query head j reads KV head j / (Hq / Hkv).
@@ -167,28 +171,34 @@ spkv_status spkv_cold_seq_info(const spkv_cold *cold, int32_t seq, int32_t *len_
  * Cache writes (device, stream-ordered).
  * ==================================================================== */
 
-/* Store a prefix's K and V, each [lp, Hkv, d] token-major, into its HOT slab
- * at `base`: element (t, h, c) goes to ((base*Hkv + h*lp) + t)*d + c
- * ([GKV] Section 3.2).  SPKV_E_INVAL unless 0 <= base and base+lp <= capacity. */
+/* Store layer `layer` of a prefix's K and V, each [lp, Hkv, d] token-major,
+ * into its HOT slab at `base` in a pool of num_layers layers: element
+ * (t, h, c) goes to ((base*Hkv*L + layer*lp*Hkv + h*lp) + t)*d + c ([GKV]
+ * Section 3.2).  SPKV_E_INVAL unless 0 <= base, base+lp <= capacity and
+ * 0 <= layer < num_layers. */
 spkv_status spkv_hot_write(const void *k_src, const void *v_src, int64_t base, int64_t lp,
-                           void *k_hot, void *v_hot, int64_t hot_capacity,
+                           void *k_hot, void *v_hot, int64_t hot_capacity, int32_t num_layers, int32_t layer,
                            int32_t num_kv_heads, int32_t head_dim, int32_t dtype, void *stream);
 
 /* Write token i's K and V rows ([n, Hkv, d] each) at COLD slot
  * slot_mapping[i] ([PKV] How it works, step 1: reshape_and_cache).
- * slot_mapping is device memory.  Slots outside [0, cold_slots) (e.g. -1
- * padding) are skipped. */
+ * k_cold / v_cold are one layer's pool (for layer l of a multi-layer pool,
+ * the pool pointer plus l * cold_slots * Hkv * d elements).  slot_mapping is
+ * device memory.  Slots outside [0, cold_slots) (e.g. -1 padding) are
+ * skipped. */
 spkv_status spkv_reshape_and_cache(const void *k_new, const void *v_new, const int32_t *slot_mapping,
                                    int32_t n, void *k_cold, void *v_cold, int64_t cold_slots,
                                    int32_t num_kv_heads, int32_t head_dim, int32_t dtype, void *stream);
 
 /* Copy-on-write page copies ([PKV] How it works, step 2): for each of the n
  * (src, dst) pairs in device memory `pairs` ([n, 2] int32), copy all
- * page_size slots of page src to page dst, K and V.  Pairs with a page
- * outside [0, num_pages) are skipped.  Destination pages must be distinct and
- * must not be the source of another pair (true of pairs from append). */
+ * page_size slots of page src to page dst, K and V, in every one of the
+ * num_layers layers of the pool (a page is shared or copied for all layers
+ * at once).  Pairs with a page outside [0, num_pages) are skipped.
+ * Destination pages must be distinct and must not be the source of another
+ * pair (true of pairs from append). */
 spkv_status spkv_copy_blocks(const int32_t *pairs, int32_t n, void *k_cold, void *v_cold,
-                             int32_t num_pages, int32_t page_size,
+                             int32_t num_pages, int32_t page_size, int32_t num_layers,
                              int32_t num_kv_heads, int32_t head_dim, int32_t dtype, void *stream);
 
 /* One decode step's appends in one launch ([PKV] How it works, steps 1-3):
@@ -260,14 +270,18 @@ typedef struct spkv_batch {
     const int32_t *host_cold_lens; /* host copy of cold_lens */
 } spkv_batch;
 
-/* The pools attention reads (device memory, caller-owned). */
+/* The pools attention reads (device memory, caller-owned), and the layer
+ * this call attends: both pools hold num_layers layers in the layouts above,
+ * with one HOT allocation and one COLD allocation for all of them. */
 typedef struct spkv_kv {
     const void *k_hot;
     const void *v_hot;
     int64_t hot_capacity;          /* tokens */
     const void *k_cold;
     const void *v_cold;
-    int64_t cold_slots;            /* num_pages * page_size */
+    int64_t cold_slots;            /* num_pages * page_size (per layer) */
+    int32_t num_layers;            /* L >= 1 */
+    int32_t layer;                 /* 0 <= layer < L */
 } spkv_kv;
 
 /* Workspace bytes the decode calls below need for this batch in any mode
@@ -368,6 +382,30 @@ spkv_status spkv_decode_step_append_noalloc(const spkv_batch *batch, const spkv_
                                             const spkv_dispatch_params *params, const void *k_new,
                                             const void *v_new, const int32_t *host_slots, float *out, float *lse,
                                             void *stream, int32_t *cascade_out);
+
+/* ======================================================================
+ * The decode step as a HIP graph ([GKV] Appendix B.2b: per-backend graph
+ * buffers in the serving engine).  The step's kernel arguments change every
+ * step (lengths grow, slots move), so the graph is not replayed as recorded:
+ * each call records the step on a private stream (recording enqueues no GPU
+ * work), updates the instantiated graph's kernel nodes with this step's
+ * arguments in place (hipGraphExecUpdate) when the step has the same launches
+ * as the graph, re-instantiates it otherwise, and launches the graph on
+ * `stream`.  The graph uses no memset nodes.
+ * ==================================================================== */
+typedef struct spkv_graph spkv_graph;
+
+spkv_status spkv_graph_create(spkv_graph **out);
+void        spkv_graph_destroy(spkv_graph *graph);
+/* The same arguments, results and errors as spkv_decode_step_append, run as
+ * the handle's graph; *instantiated_out (nullable) is 1 when the graph had to
+ * be (re)instantiated instead of updated.  A handle is single-owner and not
+ * thread-safe; the workspace must stay valid until the launch has run. */
+spkv_status spkv_graph_decode_step_append(spkv_graph *graph, const spkv_batch *batch, const spkv_kv *kv,
+                                          const spkv_dispatch_params *params, const void *k_new,
+                                          const void *v_new, const int32_t *host_slots, float *out, float *lse,
+                                          void *ws, size_t ws_bytes, void *stream, int32_t *cascade_out,
+                                          int32_t *instantiated_out);
 
 /* ======================================================================
  * Plan inspection and kernel timing (measurement support).

@@ -1,6 +1,6 @@
 """Profiles the decode step of bench.py with rocprofv3 (on a machine with the GPU).
 
-    python shared_prefix_paged_amd/profile_step.py [--config C1] [--mode step] [--out DIR]
+    python profile_step.py [--config C1] [--lp N] [--mode step|cascade|dense] [--out DIR]
 
 Runs, each as its own rocprofv3 process (program directly after ``--``, from
 /tmp with TMPDIR=/tmp, under a hard time limit):
@@ -36,7 +36,7 @@ import os
 import subprocess
 import sys
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ROOT = os.path.dirname(os.path.abspath(__file__))
 KERNELS = {"flat_kernel": "flat_paged", "prefix_mfma_kernel": "prefix_mfma", "merge_kernel": "merge"}
 COPY_MIB = 256
 NUM_CUS, SIMDS_PER_CU, NUM_XCC = 256, 4, 8
@@ -132,6 +132,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--config", default="C1")
     ap.add_argument("--mode", default="step")
+    ap.add_argument("--lp", type=int, default=None, help="override the prefix length (C3 sweep points)")
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "profile"), help="raw rocprofv3 output")
@@ -146,6 +147,11 @@ def main():
     bench = os.path.join(ROOT, "bench.py")
     run = [bench, "--config", a.config, "--mode", a.mode, "--no-cpu-baseline", "--cold-runs", "0"]
     name = f"{a.config.lower()}_{a.mode}"
+    cfg_key = a.config
+    if a.lp is not None:
+        run += ["--lp", str(a.lp)]
+        name = f"{a.config.lower()}_lp{a.lp}_{a.mode}"
+        cfg_key = f"{a.config}@{a.lp}"
 
     # 1. kernel trace + stats of the bench command
     cmd, files = rocprof(["--kernel-trace", "--stats"], a.out, "stats",
@@ -200,7 +206,7 @@ def main():
         t = {}
     if t.get("sources") != bm.source_digest():
         t = {"sources": bm.source_digest(), "runs": {}}
-    t["runs"][f"{a.config}/{a.mode}"] = runs
+    t["runs"][f"{cfg_key}/{a.mode}"] = runs
     t["factors"] = factors
     json.dump(t, open(tpath, "w"), indent=1, sort_keys=True)
     md = [f"# HBM traffic per launch: {a.config}, mode {a.mode}", "",

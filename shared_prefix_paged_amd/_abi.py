@@ -34,7 +34,8 @@ class spkv_batch(C.Structure):
 
 class spkv_kv(C.Structure):
     _fields_ = [("k_hot", c_vp), ("v_hot", c_vp), ("hot_capacity", c_i64),
-                ("k_cold", c_vp), ("v_cold", c_vp), ("cold_slots", c_i64)]
+                ("k_cold", c_vp), ("v_cold", c_vp), ("cold_slots", c_i64),
+                ("num_layers", c_i32), ("layer", c_i32)]
 
 
 class spkv_dispatch_params(C.Structure):
@@ -76,9 +77,10 @@ SIGNATURES = {
     "spkv_cold_refcounts": (c_i32, [c_vp, P_i32]),
     "spkv_cold_free_stack": (c_i32, [c_vp, P_i32]),
     "spkv_cold_seq_info": (c_i32, [c_vp, c_i32, P_i32, P_i32, P_i32]),
-    "spkv_hot_write": (c_i32, [c_vp, c_vp, c_i64, c_i64, c_vp, c_vp, c_i64, c_i32, c_i32, c_i32, c_vp]),
+    "spkv_hot_write": (c_i32, [c_vp, c_vp, c_i64, c_i64, c_vp, c_vp, c_i64, c_i32, c_i32, c_i32, c_i32, c_i32,
+                               c_vp]),
     "spkv_reshape_and_cache": (c_i32, [c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i64, c_i32, c_i32, c_i32, c_vp]),
-    "spkv_copy_blocks": (c_i32, [c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp]),
+    "spkv_copy_blocks": (c_i32, [c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp]),
     "spkv_block_table_append": (c_i32, [c_vp, c_i32, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_vp]),
     "spkv_append_tokens": (c_i32, [c_vp, c_vp, P_i32, P_i32, c_i32, c_vp, c_vp, c_i64, c_vp, c_i32, c_vp, c_i32,
                                    c_i32, c_i32, c_i32, c_i32, c_vp]),
@@ -93,6 +95,10 @@ SIGNATURES = {
                                         P_i32]),
     "spkv_decode_step_append_noalloc": (c_i32, [P_batch, P_kv, P_params, c_vp, c_vp, P_i32, c_vp, c_vp, c_vp,
                                                 P_i32]),
+    "spkv_graph_create": (c_i32, [C.POINTER(c_vp)]),
+    "spkv_graph_destroy": (None, [c_vp]),
+    "spkv_graph_decode_step_append": (c_i32, [c_vp, P_batch, P_kv, P_params, c_vp, c_vp, P_i32, c_vp, c_vp, c_vp,
+                                              c_sz, c_vp, P_i32, P_i32]),
     "spkv_plan_query": (c_i32, [P_batch, P_i32, C.POINTER(spkv_plan_info)]),
     "spkv_plan_parts": (c_i32, [P_batch, P_i32, P_i32, P_i32]),
     "spkv_timing_enable": (c_i32, [c_i32]),

@@ -76,6 +76,11 @@ struct Args {
     const void *k_new;
     const void *v_new;
     int32_t append;
+    // Layer of this call in pools of num_layers layers: the HOT slab of a
+    // prefix at token slot base holds layer l's head h at row
+    // base*Hkv*L + l*Lp*Hkv + h*Lp ([GKV] Section 3.2); k_cold / v_cold already
+    // point at this layer's COLD pool.
+    int32_t num_layers, layer;
     // Set when no request's paged-pass tokens include HOT slab rows: every
     // K/V row the bf16 paged pass reads is then a private COLD row, read once
     // per step, and is loaded with the non-temporal hint.
@@ -83,6 +88,12 @@ struct Args {
 };
 
 __device__ __forceinline__ bool mask_get(const GroupMask &m, int g) { return (m.bits[g >> 5] >> (g & 31)) & 1u; }
+
+// First row of head h of this call's layer in a HOT slab at token slot base
+// holding a prefix of lp tokens (rows of the pool's K or V buffer).
+__device__ __forceinline__ int64_t slab_row(const Args &a, int64_t base, int lp, int h) {
+    return base * a.Hkv * a.num_layers + (int64_t)a.layer * lp * a.Hkv + (int64_t)h * lp;
+}
 
 // Geometry of one request, clamped so that no index can leave its buffer.
 struct Req {
@@ -312,7 +323,7 @@ __device__ __forceinline__ void attend_range(const Args &a, const Req &r, int b,
     const char *vcold = (const char *)a.v_cold;
     const int32_t *table = a.tables + (int64_t)b * a.max_blocks;
     const int64_t num_pages = a.cold_slots / a.page_size;
-    const uint32_t hot_row0 = (uint32_t)(r.base * a.Hkv + (int64_t)h * r.lp);
+    const uint32_t hot_row0 = (uint32_t)slab_row(a, r.base, r.lp, h);
     const int32_t *tab_lds = (const int32_t *)(ring + S * FG::STAGEB);
     const uint32_t tab_off = ring_off + S * FG::STAGEB;
 
@@ -584,7 +595,7 @@ __device__ __forceinline__ void attend_range_mfma(const Args &a, const Req &r, i
     const char *vcold = (const char *)a.v_cold;
     const int32_t *table = a.tables + (int64_t)b * a.max_blocks;
     const int64_t num_pages = a.cold_slots / a.page_size;
-    const uint32_t hot_row0 = (uint32_t)(r.base * a.Hkv + (int64_t)h * r.lp);
+    const uint32_t hot_row0 = (uint32_t)slab_row(a, r.base, r.lp, h);
     const int32_t *tab_lds = (const int32_t *)(ring + S * F::STAGEB);
     const uint32_t tab_off = ring_off + S * F::STAGEB;
 
@@ -955,8 +966,8 @@ __global__ __launch_bounds__(64 * W * KH) void prefix_mfma_kernel(Args a) {
     const int half = lane >> 5;
     const int col = lane & 31;
 
-    const char *kh = (const char *)a.k_hot + ((int64_t)base * a.Hkv + (int64_t)h * lp) * ROWB;
-    const char *vh = (const char *)a.v_hot + ((int64_t)base * a.Hkv + (int64_t)h * lp) * ROWB;
+    const char *kh = (const char *)a.k_hot + slab_row(a, base, lp, h) * ROWB;
+    const char *vh = (const char *)a.v_hot + slab_row(a, base, lp, h) * ROWB;
     // kh / vh are wave-uniform (kernel arguments and block indices only), so
     // they live in SGPRs as the DMA's "s" operand requires.  (The readfirstlane
     // builtin is 32-bit and must not be applied to these 64-bit pointers.)
@@ -1421,7 +1432,8 @@ __global__ __launch_bounds__(256) void merge2_kernel(const float *oa, const floa
 // Cache writes: 16-byte copies.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void hot_write_kernel(const u32x4_t *ksrc, const u32x4_t *vsrc, u32x4_t *khot,
-                                                        u32x4_t *vhot, int64_t base, int64_t lp, int hkv, int pieces_per_row) {
+                                                        u32x4_t *vhot, int64_t base, int64_t lp, int num_layers, int layer,
+                                                        int hkv, int pieces_per_row) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t total = lp * hkv * pieces_per_row;
     if (i >= total) return;
@@ -1429,7 +1441,7 @@ __global__ __launch_bounds__(256) void hot_write_kernel(const u32x4_t *ksrc, con
     const int64_t th = i / pieces_per_row;      // token-major source row: t * hkv + h
     const int64_t t = th / hkv;
     const int64_t h = th % hkv;
-    const int64_t dst = ((base * hkv + h * lp) + t) * pieces_per_row + piece;
+    const int64_t dst = ((base * hkv * num_layers + (int64_t)layer * lp * hkv + h * lp) + t) * pieces_per_row + piece;
     khot[dst] = ksrc[i];
     vhot[dst] = vsrc[i];
 }
@@ -1452,6 +1464,9 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(const int32_t *pairs, 
     const int p = blockIdx.y;
     const int64_t src = pairs[2 * p], dst = pairs[2 * p + 1];
     if (src < 0 || src >= num_pages || dst < 0 || dst >= num_pages) return;
+    const int64_t layer_off = (int64_t)blockIdx.z * num_pages * pieces_per_page;   // layer of the pool
+    kcold += layer_off;
+    vcold += layer_off;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < pieces_per_page; i += (int64_t)gridDim.x * blockDim.x) {
         kcold[dst * pieces_per_page + i] = kcold[src * pieces_per_page + i];
         vcold[dst * pieces_per_page + i] = vcold[src * pieces_per_page + i];
@@ -1547,6 +1562,8 @@ struct TimedLaunch {
         Timing &t = timing();
         std::lock_guard<std::mutex> g(t.mu);
         if (!t.on) return;
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(s, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone) return;   // a graph node: no events
         a = take_event(t);
         b = take_event(t);
     }
@@ -1699,8 +1716,12 @@ Args make_args(const spkv_batch *b, const spkv_kv *kv, const Plan &p, void *ws) 
     a.k_hot = kv->k_hot;
     a.v_hot = kv->v_hot;
     a.hot_capacity = kv->hot_capacity;
-    a.k_cold = kv->k_cold;
-    a.v_cold = kv->v_cold;
+    a.num_layers = kv->num_layers;
+    a.layer = kv->layer;
+    const int64_t cold_layer = (int64_t)kv->layer * kv->cold_slots * b->num_kv_heads * b->head_dim *
+                               (b->dtype == SPKV_DTYPE_BF16 ? 2 : 4);
+    a.k_cold = kv->k_cold ? (const char *)kv->k_cold + cold_layer : nullptr;
+    a.v_cold = kv->v_cold ? (const char *)kv->v_cold + cold_layer : nullptr;
     a.cold_slots = kv->cold_slots;
     const int64_t rows = (int64_t)b->batch * b->num_q_heads;
     a.o_part = (float *)ws;
@@ -1847,10 +1868,12 @@ spkv_status check_kv_shape(int32_t hkv, int32_t d, int32_t dtype) {
 extern "C" {
 
 spkv_status spkv_hot_write(const void *k_src, const void *v_src, int64_t base, int64_t lp, void *k_hot, void *v_hot,
-                           int64_t hot_capacity, int32_t hkv, int32_t d, int32_t dtype, void *stream) {
+                           int64_t hot_capacity, int32_t num_layers, int32_t layer, int32_t hkv, int32_t d,
+                           int32_t dtype, void *stream) {
     spkv_status st = check_kv_shape(hkv, d, dtype);
     if (st != SPKV_OK) return st;
     if (base < 0 || lp < 0 || base + lp > hot_capacity) return fail(SPKV_E_INVAL, "hot_write: slab outside the pool");
+    if (num_layers < 1 || layer < 0 || layer >= num_layers) return fail(SPKV_E_INVAL, "hot_write: layer outside the pool");
     if (lp == 0) return SPKV_OK;
     if (!k_src || !v_src || !k_hot || !v_hot) return fail(SPKV_E_INVAL, "hot_write: null pointer");
     const int esz = dtype == SPKV_DTYPE_BF16 ? 2 : 4;
@@ -1858,7 +1881,7 @@ spkv_status spkv_hot_write(const void *k_src, const void *v_src, int64_t base, i
     const int64_t total = lp * hkv * ppr;
     TimedLaunch tl(SPKV_KERNEL_CACHE, (hipStream_t)stream);
     tl.launch(hot_write_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, (const u32x4_t *)k_src,
-              (const u32x4_t *)v_src, (u32x4_t *)k_hot, (u32x4_t *)v_hot, base, lp, hkv, ppr);
+              (const u32x4_t *)v_src, (u32x4_t *)k_hot, (u32x4_t *)v_hot, base, lp, num_layers, layer, hkv, ppr);
     return check_launch("hot_write_kernel");
 }
 
@@ -1921,10 +1944,12 @@ spkv_status spkv_append_tokens(const void *k_new, const void *v_new, const int32
 }
 
 spkv_status spkv_copy_blocks(const int32_t *pairs, int32_t n, void *k_cold, void *v_cold, int32_t num_pages,
-                             int32_t page_size, int32_t hkv, int32_t d, int32_t dtype, void *stream) {
+                             int32_t page_size, int32_t num_layers, int32_t hkv, int32_t d, int32_t dtype,
+                             void *stream) {
     spkv_status st = check_kv_shape(hkv, d, dtype);
     if (st != SPKV_OK) return st;
     if (n < 0 || num_pages < 0 || page_size < 1) return fail(SPKV_E_INVAL, "copy_blocks: bad size");
+    if (num_layers < 1 || num_layers > 65535) return fail(SPKV_E_INVAL, "copy_blocks: num_layers must be 1..65535");
     if (n == 0) return SPKV_OK;
     if (n > 65535) return fail(SPKV_E_INVAL, "copy_blocks: at most 65535 pairs per call");
     if (!pairs || !k_cold || !v_cold) return fail(SPKV_E_INVAL, "copy_blocks: null pointer");
@@ -1932,8 +1957,8 @@ spkv_status spkv_copy_blocks(const int32_t *pairs, int32_t n, void *k_cold, void
     const int64_t ppp = (int64_t)page_size * hkv * d * esz / 16;
     const unsigned gx = (unsigned)std::min<int64_t>(64, (ppp + 255) / 256);
     TimedLaunch tl(SPKV_KERNEL_CACHE, (hipStream_t)stream);
-    tl.launch(copy_blocks_kernel, dim3(gx, (unsigned)n), dim3(256), 0, pairs, (u32x4_t *)k_cold, (u32x4_t *)v_cold,
-              num_pages, ppp);
+    tl.launch(copy_blocks_kernel, dim3(gx, (unsigned)n, (unsigned)num_layers), dim3(256), 0, pairs, (u32x4_t *)k_cold,
+              (u32x4_t *)v_cold, num_pages, ppp);
     return check_launch("copy_blocks_kernel");
 }
 
@@ -2025,6 +2050,90 @@ spkv_status spkv_decode_step_append_noalloc(const spkv_batch *batch, const spkv_
     if (st != SPKV_OK) return st;
     return spkv_decode_step_append(batch, kv, params, k_new, v_new, host_slots, out, lse, ws, kScratchBytes, stream,
                                    cascade_out);
+}
+
+}  // extern "C"
+
+// A decode step recorded as a HIP graph and replayed with each step's kernel
+// arguments: the step is captured on a private stream (capture enqueues no GPU
+// work), the instantiated graph's nodes take the new arguments through
+// hipGraphExecUpdate when the launches are the same as last time (same kernels
+// and node count; grids may change), and the graph is re-instantiated
+// otherwise.
+struct spkv_graph {
+    hipStream_t capture = nullptr;
+    hipGraphExec_t exec = nullptr;
+    int64_t instantiations = 0;
+    int64_t updates = 0;
+};
+
+extern "C" {
+
+spkv_status spkv_graph_create(spkv_graph **out) {
+    if (!out) return fail(SPKV_E_INVAL, "graph_create: null out");
+    auto *g = new spkv_graph();
+    hipError_t e = hipStreamCreateWithFlags(&g->capture, hipStreamNonBlocking);
+    if (e != hipSuccess) {
+        delete g;
+        return fail(SPKV_E_HIP, std::string("graph_create: stream: ") + hipGetErrorString(e));
+    }
+    *out = g;
+    return SPKV_OK;
+}
+
+void spkv_graph_destroy(spkv_graph *g) {
+    if (!g) return;
+    if (g->exec) (void)hipGraphExecDestroy(g->exec);
+    if (g->capture) (void)hipStreamDestroy(g->capture);
+    delete g;
+}
+
+spkv_status spkv_graph_decode_step_append(spkv_graph *g, const spkv_batch *batch, const spkv_kv *kv,
+                                          const spkv_dispatch_params *params, const void *k_new, const void *v_new,
+                                          const int32_t *host_slots, float *out, float *lse, void *ws,
+                                          size_t ws_bytes, void *stream, int32_t *cascade_out,
+                                          int32_t *instantiated_out) {
+    if (!g) return fail(SPKV_E_INVAL, "graph_decode_step_append: null graph");
+    if (instantiated_out) *instantiated_out = 0;
+    // Argument errors come out of the capture as they would from the call itself.
+    hipError_t e = hipStreamBeginCapture(g->capture, hipStreamCaptureModeRelaxed);
+    if (e != hipSuccess) return fail(SPKV_E_HIP, std::string("graph: begin capture: ") + hipGetErrorString(e));
+    spkv_status st = spkv_decode_step_append(batch, kv, params, k_new, v_new, host_slots, out, lse, ws, ws_bytes,
+                                             g->capture, cascade_out);
+    hipGraph_t graph = nullptr;
+    e = hipStreamEndCapture(g->capture, &graph);
+    if (st != SPKV_OK) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return st;
+    }
+    if (e != hipSuccess || !graph) return fail(SPKV_E_HIP, std::string("graph: end capture: ") + hipGetErrorString(e));
+    bool updated = false;
+    if (g->exec) {
+        hipGraphExecUpdateResult res = hipGraphExecUpdateError;
+        hipGraphNode_t bad = nullptr;
+        updated = hipGraphExecUpdate(g->exec, graph, &bad, &res) == hipSuccess && res == hipGraphExecUpdateSuccess;
+        (void)hipGetLastError();
+        if (!updated) {
+            (void)hipGraphExecDestroy(g->exec);
+            g->exec = nullptr;
+        }
+    }
+    if (!updated) {
+        e = hipGraphInstantiate(&g->exec, graph, nullptr, nullptr, 0);
+        if (e != hipSuccess) {
+            (void)hipGraphDestroy(graph);
+            g->exec = nullptr;
+            return fail(SPKV_E_HIP, std::string("graph: instantiate: ") + hipGetErrorString(e));
+        }
+        g->instantiations += 1;
+        if (instantiated_out) *instantiated_out = 1;
+    } else {
+        g->updates += 1;
+    }
+    (void)hipGraphDestroy(graph);
+    e = hipGraphLaunch(g->exec, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(SPKV_E_HIP, std::string("graph: launch: ") + hipGetErrorString(e));
+    return SPKV_OK;
 }
 
 spkv_status spkv_merge_states(const float *o_a, const float *lse_a, const float *o_b, const float *lse_b, float *o,

@@ -71,8 +71,11 @@ spkv_status validate_batch(const spkv_batch *b, const spkv_kv *kv) {
     }
     if (kv) {
         if (kv->hot_capacity < 0 || kv->cold_slots < 0) return fail(SPKV_E_INVAL, "negative pool size");
-        if (kv->hot_capacity * b->num_kv_heads >= (int64_t(1) << 31) || kv->cold_slots * b->num_kv_heads >= (int64_t(1) << 31))
-            return fail(SPKV_E_INVAL, "pools limited to 2^31 rows (slots x KV heads)");
+        if (kv->num_layers < 1 || kv->layer < 0 || kv->layer >= kv->num_layers)
+            return fail(SPKV_E_INVAL, "layer outside [0, num_layers) or num_layers < 1");
+        if (kv->hot_capacity * b->num_kv_heads * kv->num_layers >= (int64_t(1) << 31) ||
+            kv->cold_slots * b->num_kv_heads >= (int64_t(1) << 31))
+            return fail(SPKV_E_INVAL, "pools limited to 2^31 rows (HOT: slots x KV heads x layers; COLD: per layer)");
         if (B > 0 && kv->cold_slots > 0 && (!kv->k_cold || !kv->v_cold)) return fail(SPKV_E_INVAL, "null COLD pool");
         if (ng > 0 && kv->hot_capacity > 0 && (!kv->k_hot || !kv->v_hot)) return fail(SPKV_E_INVAL, "null HOT pool");
         if (kv->cold_slots % b->page_size) return fail(SPKV_E_INVAL, "cold_slots must be a multiple of page_size");

@@ -197,10 +197,10 @@ def _dp(t) -> Optional[int]:
 
 
 def hot_write(k_src, v_src, base: int, k_hot, v_hot, hot_capacity: int, num_kv_heads: int, head_dim: int,
-              stream=None):
+              stream=None, num_layers: int = 1, layer: int = 0):
     check(lib.spkv_hot_write(_dp(k_src), _dp(v_src), int(base), int(k_src.shape[0]), _dp(k_hot), _dp(v_hot),
-                             int(hot_capacity), int(num_kv_heads), int(head_dim), dtype_code(k_hot),
-                             stream_handle(stream)))
+                             int(hot_capacity), int(num_layers), int(layer), int(num_kv_heads), int(head_dim),
+                             dtype_code(k_hot), stream_handle(stream)))
 
 
 def reshape_and_cache(k_new, v_new, slot_mapping, k_cold, v_cold, cold_slots: int, num_kv_heads: int,
@@ -211,10 +211,10 @@ def reshape_and_cache(k_new, v_new, slot_mapping, k_cold, v_cold, cold_slots: in
 
 
 def copy_blocks(pairs, k_cold, v_cold, num_pages: int, page_size: int, num_kv_heads: int, head_dim: int,
-                stream=None):
+                stream=None, num_layers: int = 1):
     n = int(pairs.numel() // 2)
     check(lib.spkv_copy_blocks(_dp(pairs) if n else None, n, _dp(k_cold), _dp(v_cold), int(num_pages),
-                               int(page_size), int(num_kv_heads), int(head_dim), dtype_code(k_cold),
+                               int(page_size), int(num_layers), int(num_kv_heads), int(head_dim), dtype_code(k_cold),
                                stream_handle(stream)))
 
 
@@ -242,23 +242,37 @@ def append_tokens(k_new, v_new, slots: np.ndarray, k_cold, v_cold, cold_slots: i
 
 
 class KVPools:
-    """Caller-owned device pools; ``struct`` is the spkv_kv describing them."""
+    """Caller-owned device pools of num_layers layers; ``struct`` is the
+    spkv_kv describing them for the current ``layer`` (see ``at_layer``)."""
 
-    def __init__(self, k_hot, v_hot, hot_capacity: int, k_cold, v_cold, cold_slots: int):
+    def __init__(self, k_hot, v_hot, hot_capacity: int, k_cold, v_cold, cold_slots: int, num_layers: int = 1,
+                 layer: int = 0, row: int = 0):
         self.k_hot, self.v_hot, self.k_cold, self.v_cold = k_hot, v_hot, k_cold, v_cold
         self.hot_capacity, self.cold_slots = int(hot_capacity), int(cold_slots)
+        self.num_layers, self.layer, self.row = int(num_layers), int(layer), int(row)
         self.struct = A.spkv_kv(_dp(k_hot), _dp(v_hot), self.hot_capacity, _dp(k_cold), _dp(v_cold),
-                                self.cold_slots)
+                                self.cold_slots, self.num_layers, self.layer)
+
+    def at_layer(self, layer: int) -> "KVPools":
+        """The same pools, attended at another layer."""
+        return KVPools(self.k_hot, self.v_hot, self.hot_capacity, self.k_cold, self.v_cold, self.cold_slots,
+                       self.num_layers, layer, self.row)
+
+    def cold_layer(self, layer: int):
+        """Views of one layer's COLD K / V pool (for reshape_and_cache and append_tokens)."""
+        n = self.cold_slots * self.row
+        return self.k_cold[layer * n:(layer + 1) * n], self.v_cold[layer * n:(layer + 1) * n]
 
     @classmethod
-    def allocate(cls, hot_capacity: int, cold_slots: int, num_kv_heads: int, head_dim: int, dtype, device="cuda"):
+    def allocate(cls, hot_capacity: int, cold_slots: int, num_kv_heads: int, head_dim: int, dtype, device="cuda",
+                 num_layers: int = 1):
         torch = _torch()
         row = num_kv_heads * head_dim
-        hot = max(hot_capacity, 1) * row
-        cold = max(cold_slots, 1) * row
+        hot = max(hot_capacity, 1) * row * num_layers
+        cold = max(cold_slots, 1) * row * num_layers
         return cls(torch.zeros(hot, dtype=dtype, device=device), torch.zeros(hot, dtype=dtype, device=device),
                    hot_capacity, torch.zeros(cold, dtype=dtype, device=device),
-                   torch.zeros(cold, dtype=dtype, device=device), cold_slots)
+                   torch.zeros(cold, dtype=dtype, device=device), cold_slots, num_layers, 0, row)
 
 
 class DecodeBatch:
@@ -399,6 +413,40 @@ def decode_step_append_noalloc(batch: DecodeBatch, kv: KVPools, params: A.spkv_d
                                               _dp(k_new), _dp(v_new), _ptr(slots, C.c_int32), _dp(out), _dp(lse),
                                               stream_handle(stream), _ptr(choice, C.c_int32)))
     return out, lse, choice[:batch.num_groups]
+
+
+class StepGraph:
+    """spkv_graph_*: the fused decode step run as a HIP graph whose kernel
+    nodes take each step's arguments (see spkv_graph_decode_step_append)."""
+
+    def __init__(self):
+        h = C.c_void_p()
+        check(lib.spkv_graph_create(C.byref(h)))
+        self._h = h
+
+    def close(self):
+        if self._h:
+            lib.spkv_graph_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def decode_step_append(self, batch: DecodeBatch, kv: KVPools, params: A.spkv_dispatch_params, ws, k_new, v_new,
+                           slots: np.ndarray, out=None, lse=None, stream=None):
+        """Returns (out, lse, per-group choice, instantiated)."""
+        out, lse = _outputs(batch, out, lse)
+        choice = np.zeros(max(batch.num_groups, 1), np.int32)
+        inst = C.c_int32()
+        slots = np.ascontiguousarray(slots, dtype=np.int32)
+        check(lib.spkv_graph_decode_step_append(self._h, C.byref(batch.struct), C.byref(kv.struct), C.byref(params),
+                                                _dp(k_new), _dp(v_new), _ptr(slots, C.c_int32), _dp(out), _dp(lse),
+                                                _dp(ws), ws.numel(), stream_handle(stream),
+                                                _ptr(choice, C.c_int32), C.byref(inst)))
+        return out, lse, choice[:batch.num_groups], bool(inst.value)
 
 
 def merge_states(o_a, lse_a, o_b, lse_b, out=None, lse=None, stream=None):

@@ -53,7 +53,10 @@ def members_per_group(wl) -> np.ndarray:
 
 
 def setup_single_step(wl, page_size: Optional[int] = None, free_order=None, device="cuda",
-                      max_blocks: Optional[int] = None) -> GpuStep:
+                      max_blocks: Optional[int] = None, num_layers: int = 1) -> GpuStep:
+    """num_layers > 1: pools of that many layers (one HOT and one COLD
+    allocation), every layer holding the workload's K/V; attention reads the
+    layer set in the returned pools (pools.at_layer(l) for another)."""
     cfg = wl.cfg
     P = cfg.page_size if page_size is None else page_size
     hkv, d = cfg.num_kv_heads, cfg.head_dim
@@ -73,26 +76,30 @@ def setup_single_step(wl, page_size: Optional[int] = None, free_order=None, devi
     setup_slots, _ = cold.append_batch(setup_ids) if setup_ids else (np.zeros(0, np.int32), [])
     step_slots, step_cows = cold.append_batch(seqs) if B else (np.zeros(0, np.int32), [])
 
-    pools = R.KVPools.allocate(wl.hot_capacity, wl.num_cold_pages * P, hkv, d, torch_dtype(cfg.dtype), device)
-    for g, base in enumerate(bases):
-        R.hot_write(to_device(wl.prefix_k[g], cfg.dtype, device), to_device(wl.prefix_v[g], cfg.dtype, device),
-                    base, pools.k_hot, pools.v_hot, wl.hot_capacity, hkv, d)
+    pools = R.KVPools.allocate(wl.hot_capacity, wl.num_cold_pages * P, hkv, d, torch_dtype(cfg.dtype), device,
+                               num_layers=num_layers)
+    for layer in range(num_layers):
+        for g, base in enumerate(bases):
+            R.hot_write(to_device(wl.prefix_k[g], cfg.dtype, device), to_device(wl.prefix_v[g], cfg.dtype, device),
+                        base, pools.k_hot, pools.v_hot, wl.hot_capacity, hkv, d, num_layers=num_layers, layer=layer)
     off = wl.suffix_offsets
     if len(setup_slots):
         rows = np.concatenate([np.arange(off[b], off[b + 1] - 1) for b in range(B)])
-        R.reshape_and_cache(to_device(wl.suffix_k[rows], cfg.dtype, device),
-                            to_device(wl.suffix_v[rows], cfg.dtype, device),
-                            torch.from_numpy(setup_slots).to(device), pools.k_cold, pools.v_cold,
-                            pools.cold_slots, hkv, d)
+        ks, vs = to_device(wl.suffix_k[rows], cfg.dtype, device), to_device(wl.suffix_v[rows], cfg.dtype, device)
+        sl = torch.from_numpy(setup_slots).to(device)
+        for layer in range(num_layers):
+            kc, vc = pools.cold_layer(layer)
+            R.reshape_and_cache(ks, vs, sl, kc, vc, pools.cold_slots, hkv, d)
     if step_cows:
         R.copy_blocks(torch.tensor(step_cows, dtype=torch.int32, device=device), pools.k_cold, pools.v_cold,
-                      wl.num_cold_pages, P, hkv, d)
+                      wl.num_cold_pages, P, hkv, d, num_layers=num_layers)
     if B:
         last = off[1:] - 1
-        R.reshape_and_cache(to_device(wl.suffix_k[last], cfg.dtype, device),
-                            to_device(wl.suffix_v[last], cfg.dtype, device),
-                            torch.from_numpy(np.asarray(step_slots, np.int32)).to(device), pools.k_cold,
-                            pools.v_cold, pools.cold_slots, hkv, d)
+        ks, vs = to_device(wl.suffix_k[last], cfg.dtype, device), to_device(wl.suffix_v[last], cfg.dtype, device)
+        sl = torch.from_numpy(np.asarray(step_slots, np.int32)).to(device)
+        for layer in range(num_layers):
+            kc, vc = pools.cold_layer(layer)
+            R.reshape_and_cache(ks, vs, sl, kc, vc, pools.cold_slots, hkv, d)
     lens_now = [cold.seq_info(s)[0] for s in seqs]
     need = max([(l + P - 1) // P for l in lens_now] + [1])
     mb = need if max_blocks is None else max(max_blocks, need)

@@ -89,10 +89,12 @@ def test_block_tables_padding_and_bounds():
 def test_device_ops_validate_before_touching_the_gpu():
     # Shape and range checks fail before any HIP call is made.
     null = None
-    assert spkv.spkv_hot_write(null, null, 0, 4, null, null, 2, 1, 128, 0, null) == A.SPKV_E_INVAL
-    assert spkv.spkv_hot_write(null, null, 0, 4, null, null, 8, 1, 96, 0, null) == A.SPKV_E_INVAL
+    assert spkv.spkv_hot_write(null, null, 0, 4, null, null, 2, 1, 0, 1, 128, 0, null) == A.SPKV_E_INVAL
+    assert spkv.spkv_hot_write(null, null, 0, 4, null, null, 8, 1, 0, 1, 96, 0, null) == A.SPKV_E_INVAL
+    assert spkv.spkv_hot_write(null, null, 0, 4, null, null, 8, 2, 2, 1, 128, 0, null) == A.SPKV_E_INVAL  # layer 2 of 2
     assert spkv.spkv_reshape_and_cache(null, null, null, -1, null, null, 4, 1, 64, 0, null) == A.SPKV_E_INVAL
-    assert spkv.spkv_copy_blocks(null, 1, null, null, 4, 0, 1, 64, 0, null) == A.SPKV_E_INVAL
+    assert spkv.spkv_copy_blocks(null, 1, null, null, 4, 0, 1, 1, 64, 0, null) == A.SPKV_E_INVAL
+    assert spkv.spkv_copy_blocks(null, 1, null, null, 4, 1, 0, 1, 64, 0, null) == A.SPKV_E_INVAL  # no layers
     assert spkv.spkv_merge_states(null, null, null, null, null, null, 4, 100, null) == A.SPKV_E_INVAL
     # zero-sized work is a successful no-op
     assert spkv.spkv_reshape_and_cache(null, null, null, 0, null, null, 4, 1, 64, 0, null) == A.SPKV_OK
@@ -153,7 +155,7 @@ def test_noalloc_rejects_plans_beyond_its_scratch_before_launching():
     batch = R.DecodeBatch(q, [0] * B, [0], [4096], np.zeros((B, 64), np.int32), [60] * B, 1, 8)
     assert batch.plan().workspace_bytes > A.SPKV_NOALLOC_SCRATCH_BYTES
     fake = C.c_void_p(16)
-    kv = A.spkv_kv(16, 16, 4096, 16, 16, 1 << 20)
+    kv = A.spkv_kv(16, 16, 4096, 16, 16, 1 << 20, 1, 0)
     slots = np.arange(B, dtype=np.int32)
     st = spkv.spkv_decode_step_append_noalloc(C.byref(batch.struct), C.byref(kv),
                                               C.byref(R.default_params()), fake, fake,

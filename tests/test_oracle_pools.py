@@ -212,3 +212,44 @@ def test_copy_on_write_check_fails_without_the_copy():
                         [shared_slot, shared_slot])
     ka, _ = m.gather_suffix(pool.block_table(a), 21, P)
     assert ka[20, 0, 0] == 101.0                         # the parent now reads the child's token
+
+
+def test_layer_stride_hand_values():
+    # GraniKV paper, Section 3.2: head h of layer l sits at base + l*Lp*Hkv + h*Lp
+    # (rows) inside the prefix's slab, which starts at row base*Hkv*L.  base 2,
+    # Lp 5, Hkv 3, L 4, layer 2, head 1, token 4, d 8:
+    # slab start 2*3*4 = 24, layer 2*5*3 = 30, head 1*5 = 5, token 4 -> row 63.
+    # Catches: a layer term of l*Lp (missing Hkv), a slab start without L, or
+    # layers interleaved per head (h*Lp*L + l*Lp).
+    assert hot_offset(2, 5, 3, 8, 4, 1, layer=2, num_layers=4) == 63 * 8
+    assert hot_offset(2, 5, 3, 8, 4, 1) == (2 * 3 + 5 + 4) * 8          # one layer: the single-layer formula
+    # Consecutive layers of one head are Lp*Hkv rows apart; the next slab
+    # (base + Lp) starts right after the last layer of this one.
+    assert hot_offset(0, 5, 3, 8, 0, 0, 1, 4) - hot_offset(0, 5, 3, 8, 0, 0, 0, 4) == 5 * 3 * 8
+    assert hot_offset(5, 7, 3, 8, 0, 0, 0, 4) == hot_offset(0, 5, 3, 8, 4, 2, 3, 4) + 8
+
+
+def test_multi_layer_pools_keep_layers_apart_and_copy_pages_in_every_layer():
+    # Two layers sharing slots: layer 1's writes never touch layer 0, a prefix
+    # written per layer reads back per layer, and a copy-on-write pair copies
+    # the page in both layers.  Catches: a COLD layer offset of 0, or
+    # copy_blocks copying only the first layer.
+    hkv, d, P, L = 2, 2, 2, 2
+    m = PoolMirror(hot_capacity=6, cold_slots=8, hkv=hkv, d=d, np_dtype=np.float32, num_layers=L)
+    pk = [np.arange(3 * hkv * d, dtype=np.float32).reshape(3, hkv, d) + 100 * (l + 1) for l in range(L)]
+    for l in range(L):
+        m.hot_write(pk[l], -pk[l], base=2, layer=l)
+    for l in range(L):
+        k, v = m.gather_prefix(2, 3, layer=l)
+        np.testing.assert_array_equal(k, pk[l])
+        np.testing.assert_array_equal(v, -pk[l])
+    rows = [token_rows(2, hkv, d, start=1 + 10 * l) for l in range(L)]
+    for l in range(L):
+        m.reshape_and_cache(rows[l], rows[l], [2, 3], layer=l)        # page 1 in both layers
+    m.copy_blocks([(1, 3)], page_size=P)
+    for l in range(L):
+        k, _ = m.gather_suffix([3], 2, P, layer=l)
+        np.testing.assert_array_equal(k, rows[l])
+        k, _ = m.gather_suffix([1], 2, P, layer=l)
+        np.testing.assert_array_equal(k, rows[l])
+    assert not m.k_cold[:P * hkv * d].any()                            # layer 0's page 0 untouched
