@@ -293,8 +293,10 @@ size_t spkv_workspace_size(const spkv_batch *batch);
  * (bf16 MFMA); per request, the COLD suffix is attended by a paged pass; the
  * two partial states are merged by log-sum-exp ([GKV] Eq. (1)).  Requests
  * without a group take the paged pass over their COLD tokens only.
- * For float32 pools the prefix part runs as a per-request pass over the slab
- * (no bf16 MFMA for float32 inputs).  `lse` may be NULL. */
+ * For float32 pools the prefix part is the same batched contraction (every
+ * member's query rows against the slab, read once per group) in float32 on
+ * the vector units; the per-group dispatcher only picks it when forced (its
+ * cost constants are fitted to the bf16 kernels).  `lse` may be NULL. */
 spkv_status spkv_cascade_decode(const spkv_batch *batch, const spkv_kv *kv, float *out, float *lse,
                                 void *ws, size_t ws_bytes, void *stream);
 

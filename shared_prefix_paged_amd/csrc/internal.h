@@ -95,7 +95,7 @@ struct Plan {
     int32_t flat_splits;      // partial slots per row reserved for the flat pass
     int32_t prefix_chunk;     // base tau for the prefix pass (multiple of kPrefixKeyTile)
     int32_t prefix_splits;    // grid x of the prefix kernel
-    int32_t prefix_waves;     // row waves per prefix block (32 rows each)
+    int32_t prefix_waves;     // row waves per prefix block (32 rows each; float32: 1, a 256-thread block)
     int32_t prefix_key_halves;  // 2: each block's key chunk is split over two wave sets
     int32_t prefix_mtiles;    // grid y of the prefix kernel
     int32_t splits_total;     // prefix_splits + flat_splits (partial stride per row)
@@ -103,11 +103,9 @@ struct Plan {
     int64_t prefix_items;
     int64_t ws_bytes;
     std::vector<FlatLaunch> flat;    // paged pass (suffix, or whole context for flat-mode groups)
-    std::vector<FlatLaunch> pflat;   // float32 cascade: the prefix part as a paged pass
     int32_t flat_head_groups;        // grid y of the paged pass
     bool run_prefix;          // some cascade group has Lp > 0 (bf16)
     bool prefix_split_p;      // some cascade group is short: carry P as bf16 hi + lo
-    bool prefix_as_flat;      // float32 pools: prefix part via a per-request pass
 };
 
 // LDS bytes of one wave of the bf16 paged pass: its ring (K and V rows of

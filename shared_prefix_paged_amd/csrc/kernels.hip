@@ -41,8 +41,6 @@ typedef float f32x4v_t __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kPartPrefix = 0;   // flat kernel covers the HOT prefix of cascade groups only
-constexpr int kPartRest = 1;     // flat kernel covers COLD tokens (plus HOT for flat-mode groups)
 constexpr int kFlatWavesMax = 4; // KV heads per flat block
 
 struct Args {
@@ -68,7 +66,7 @@ struct Args {
     int32_t prefix_splits;  // offset of the flat partials inside a row
     int32_t flat_splits;    // flat partial slots per row
     int32_t flat_tau, prefix_tau, prefix_granule;
-    int32_t prefix_mode;    // 0: no prefix partials; 1: MFMA split rule; 2: paged prefix pass
+    int32_t prefix_mode;    // 0: no prefix partials; 1: the prefix contraction's split rule
     GroupMask cascade;
     // Append mode (the step's new tokens not yet in the pools): every request
     // has one COLD token more than cold_lens counts, the last one, whose K/V
@@ -135,15 +133,12 @@ __device__ __forceinline__ Req req_geo(const Args &a, int b) {
     return r;
 }
 
-// Tokens of request b covered by one flat launch: [lo, hi) of [HOT prefix ; COLD suffix].
-__device__ __forceinline__ void flat_range(const Req &r, int part, int &lo, int &hi) {
-    if (part == kPartPrefix) {
-        lo = 0;
-        hi = (r.g >= 0 && r.casc) ? r.lp : 0;
-    } else {
-        lo = (r.g >= 0 && r.casc) ? r.lp : 0;
-        hi = r.lp + r.ls;
-    }
+// Tokens of request b the paged pass attends: [lo, hi) of [HOT prefix ; COLD
+// suffix] - the COLD suffix, plus the HOT prefix when the request's group
+// takes the flat pass instead of the prefix contraction.
+__device__ __forceinline__ void flat_range(const Req &r, int &lo, int &hi) {
+    lo = (r.g >= 0 && r.casc) ? r.lp : 0;
+    hi = r.lp + r.ls;
 }
 
 template <int N>
@@ -821,7 +816,7 @@ struct MergeRows {
 // bf16: the LDS ring (4 x 8 KB per wave for d = 128) admits one or two
 // blocks per CU, so registers are not the limit.
 template <bool BF16, int D, int G, bool APP = false, bool NT = false>
-__global__ __launch_bounds__(256, (BF16 ? 2 : (G <= 6 ? 4 : 3))) void flat_kernel(Args a, int part, FlatLaunch fl) {
+__global__ __launch_bounds__(256, (BF16 ? 2 : (G <= 6 ? 4 : 3))) void flat_kernel(Args a, FlatLaunch fl) {
     extern __shared__ __attribute__((aligned(1024))) char flat_smem[];
     const int k = blockIdx.x;
     const int wave = threadIdx.x >> 6;
@@ -845,7 +840,7 @@ __global__ __launch_bounds__(256, (BF16 ? 2 : (G <= 6 ? 4 : 3))) void flat_kerne
     int i = 0;
 #pragma unroll
     for (int j = 0; j < NQW; ++j) i += __popcll(__ballot(lane + 64 * j < fl.nreq && ends[j] <= s0));
-    const int slot0 = part == kPartRest ? a.prefix_splits : 0;
+    const int slot0 = a.prefix_splits;     // the paged pass's partial slots follow the prefix contraction's
     for (; i < fl.nreq; ++i) {
         const int64_t o0 = (int64_t)fl.offs[i] + fl.head, o1 = fl.offs[i + 1];
         if (o0 >= s1) break;
@@ -856,7 +851,7 @@ __global__ __launch_bounds__(256, (BF16 ? 2 : (G <= 6 ? 4 : 3))) void flat_kerne
         const int b = fl.b0 + i;
         const Req r = req_geo(a, b);
         int lo, hi;
-        flat_range(r, part, lo, hi);
+        flat_range(r, lo, hi);
         const int t0 = lo + (int)(lo_s - o0);
         const int t1 = min(hi, lo + (int)(hi_s - o0));   // device data shorter than the plan: clamp
         if (t1 <= t0) continue;
@@ -1259,6 +1254,174 @@ __global__ __launch_bounds__(64 * W * KH) void prefix_mfma_kernel(Args a) {
 }
 
 // ---------------------------------------------------------------------------
+// Prefix contraction for float32 pools ([GKV] Section 2.3: every member query
+// of a group against the group's one slab), on the VALU in float32: a block of
+// 256 threads takes 32 query rows of one group and KV head over one key chunk
+// (the split rule of the bf16 contraction), with K / V tiles of 32 keys
+// staged in LDS.  Eight consecutive lanes share a query row: each scores four
+// keys of the tile and keeps D / 8 output dimensions; the row's online
+// softmax state is reduced across those eight lanes.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void prefix_f32_kernel(Args a) {
+    constexpr int RT = 32;            // query rows per block
+    constexpr int KT = 32;            // keys per tile
+    constexpr int TPR = 8;            // lanes per row
+    constexpr int KPT = KT / TPR;     // keys scored per lane per tile
+    constexpr int DPT = D / TPR;      // output dims per lane
+    constexpr int PAD = D + 4;        // LDS row stride in floats (rows start on distinct banks)
+    constexpr int kWin = RT + 8;      // >= 32 rows / G + 1 members
+    static_assert(spkv::kPrefixKeyTile == KT, "the split rule's granule is one tile");
+    __shared__ float qs[RT][PAD];
+    __shared__ float ks[KT][PAD];
+    __shared__ float vs[KT][PAD];
+    __shared__ float ps[RT][KT + 1];
+    __shared__ int32_t win[kWin];
+    __shared__ int32_t members_s;
+
+    const int g = blockIdx.z / a.Hkv, h = blockIdx.z % a.Hkv;
+    if (g >= a.ng || !mask_get(a.cascade, g)) return;
+    const int64_t base = a.hot_base[g];
+    const int lp = a.hot_len[g];
+    if (lp <= 0 || base < 0 || base + lp > a.hot_capacity) return;
+    const int mt = blockIdx.y;
+    const int chunk = spkv::chunk_for(lp, a.prefix_tau, spkv::kPrefixSplitCap, KT);
+    const int s = blockIdx.x;
+    if (s >= spkv::splits_for(lp, chunk)) return;
+    const int kc0 = s * chunk, kc1 = min(lp, kc0 + chunk);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int r = tid / TPR, kg = tid % TPR;
+
+    // Members of group g (ascending request id, [GKV] Section 3.4): wave 0
+    // scans group_of, counts them and writes the ids the block's rows need.
+    const int kw0 = (mt * RT) / a.G;
+    if (tid < 64) {
+        int count = 0;
+        for (int c0 = 0; c0 < a.B; c0 += 64) {
+            const int i = c0 + lane;
+            const bool mine = i < a.B && a.group_of[i] == g;
+            const uint64_t m = __ballot(mine);
+            const int rank = count + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            if (mine && rank >= kw0 && rank < kw0 + kWin) win[rank - kw0] = i;
+            count += __popcll(m);
+        }
+        if (lane == 0) members_s = count;
+    }
+    __syncthreads();
+    const int M = members_s * a.G;
+    if (mt * RT >= M) return;                       // block-uniform
+
+    const float *khot = (const float *)a.k_hot + slab_row(a, base, lp, h) * D;
+    const float *vhot = (const float *)a.v_hot + slab_row(a, base, lp, h) * D;
+    const int row = mt * RT + r;
+    const bool row_ok = row < M;
+    int qb = 0, qj = 0;
+    if (row_ok) {
+        qb = max(0, min(win[row / a.G - kw0], a.B - 1));
+        qj = h * a.G + row % a.G;
+    }
+    // this row's query, D / 8 floats per lane, into LDS (zeros past the last row)
+    {
+        const float *qp = (const float *)a.q + ((int64_t)qb * a.Hq + qj) * D;
+#pragma unroll
+        for (int c = 0; c < DPT; c += 4) {
+            const int col = kg * DPT + c;
+            const float4 v = row_ok ? *(const float4 *)(qp + col) : make_float4(0.f, 0.f, 0.f, 0.f);
+            *(float4 *)&qs[r][col] = v;
+        }
+    }
+    float o[DPT];
+#pragma unroll
+    for (int c = 0; c < DPT; ++c) o[c] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+    const float c2 = a.scale_log2;
+    // The next tile's K / V pieces are loaded into registers while the
+    // current tile is computed (one memory round trip per tile is hidden).
+    constexpr int F4 = KT * D / 4;                  // float4 pieces of one tile
+    constexpr int NPT = F4 / 256;                   // pieces per thread
+    static_assert(F4 % 256 == 0, "a tile splits evenly over the block");
+    float4 kpre[NPT], vpre[NPT];
+    auto fetch = [&](int kt) {
+#pragma unroll
+        for (int u = 0; u < NPT; ++u) {
+            const int i = tid + 256 * u, key = i / (D / 4), c = (i % (D / 4)) * 4;
+            const int64_t src = (int64_t)min(kt + key, kc1 - 1) * D + c;   // past the chunk: the last key (masked)
+            kpre[u] = *(const float4 *)(khot + src);
+            vpre[u] = *(const float4 *)(vhot + src);
+        }
+    };
+    fetch(kc0);
+    for (int kt = kc0; kt < kc1; kt += KT) {
+        __syncthreads();                            // every lane is done with the previous tile
+#pragma unroll
+        for (int u = 0; u < NPT; ++u) {
+            const int i = tid + 256 * u, key = i / (D / 4), c = (i % (D / 4)) * 4;
+            *(float4 *)&ks[key][c] = kpre[u];
+            *(float4 *)&vs[key][c] = vpre[u];
+        }
+        __syncthreads();
+        if (kt + KT < kc1) fetch(kt + KT);
+        float sc[KPT];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            const int key = kg + TPR * j;
+            float acc = 0.f;
+#pragma unroll 8
+            for (int c = 0; c < D; c += 4) {
+                const float4 q4 = *(const float4 *)&qs[r][c];
+                const float4 k4 = *(const float4 *)&ks[key][c];
+                acc = fmaf(q4.x, k4.x, fmaf(q4.y, k4.y, fmaf(q4.z, k4.z, fmaf(q4.w, k4.w, acc))));
+            }
+            sc[j] = kt + key < kc1 ? acc * c2 : -INFINITY;
+            mx = fmaxf(mx, sc[j]);
+        }
+        // the row's eight lanes are consecutive: reduce over aligned groups of 8
+        mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 4, 64));
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        float ls = 0.f;
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            const float pj = sc[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[j] - m_new);
+            ps[r][kg + TPR * j] = pj;
+            ls += pj;
+        }
+        ls += __shfl_xor(ls, 1, 64);
+        ls += __shfl_xor(ls, 2, 64);
+        ls += __shfl_xor(ls, 4, 64);
+        l_run = l_run * alpha + ls;
+        m_run = m_new;
+#pragma unroll
+        for (int c = 0; c < DPT; ++c) o[c] *= alpha;
+        __builtin_amdgcn_wave_barrier();             // the row's weights (its own eight lanes) before they are read
+        asm volatile("" ::: "memory");
+        for (int key = 0; key < KT; ++key) {
+            const float pk = ps[r][key];
+#pragma unroll
+            for (int c = 0; c < DPT; c += 4) {
+                const float4 v4 = *(const float4 *)&vs[key][kg * DPT + c];
+                o[c] = fmaf(pk, v4.x, o[c]);
+                o[c + 1] = fmaf(pk, v4.y, o[c + 1]);
+                o[c + 2] = fmaf(pk, v4.z, o[c + 2]);
+                o[c + 3] = fmaf(pk, v4.w, o[c + 3]);
+            }
+        }
+    }
+    if (!row_ok) return;
+    const int64_t prow = ((int64_t)qb * a.Hq + qj) * a.splits_total + s;
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    float *dst = a.o_part + prow * D + kg * DPT;
+#pragma unroll
+    for (int c = 0; c < DPT; c += 4)
+        *(float4 *)(dst + c) = make_float4(o[c] * inv, o[c + 1] * inv, o[c + 2] * inv, o[c + 3] * inv);
+    if (kg == 0) a.lse_part[prow] = l_run > 0.f ? m_run + __log2f(l_run) : -INFINITY;
+}
+
+// ---------------------------------------------------------------------------
 // Merge of a row's partial states (Eq. (1) applied across all partials).
 // One wave per (request, query head) row; four rows per block.  Lane k first
 // holds partial k's weight exp2(lse_k - max); then each wave-wide load brings
@@ -1271,7 +1434,7 @@ __global__ __launch_bounds__(64 * W * KH) void prefix_mfma_kernel(Args a) {
 // as spkv_append_tokens does.
 template <int D, bool APPEND = false>
 __global__ __launch_bounds__(256) void merge_kernel(Args a, float *out, float *lse_out, FlatLaunch fr,
-                                                    FlatLaunch fp, MergeRows ap) {
+                                                    MergeRows ap) {
     constexpr int LPP = D / 4;      // lanes per partial row (float4 each)
     constexpr int PPW = 64 / LPP;   // partial rows per wave-wide load
     constexpr int BATCH = 40 / PPW; // wave-wide loads in flight (40 partials)
@@ -1311,12 +1474,8 @@ __global__ __launch_bounds__(256) void merge_kernel(Args a, float *out, float *l
     if (row >= (int64_t)(fr.b0 + fr.nreq) * a.Hq) return;
     const int b = (int)(row / a.Hq);
     const int i = b - fr.b0;
-    int np = 0, first;
-    if (a.prefix_mode == 1) {
-        np = ap.prefix_np[i];
-    } else if (a.prefix_mode == 2) {
-        np = flat_parts(fp, i, &first);
-    }
+    int first;
+    int np = a.prefix_mode == 1 ? ap.prefix_np[i] : 0;
     int nf = flat_parts(fr, i, &first);
     np = max(0, min(np, a.prefix_splits));   // never read past this row's partial slots
     nf = max(0, min(nf, a.flat_splits));
@@ -1596,60 +1755,67 @@ spkv_status check_launch(const char *what) {
 
 // Dynamic LDS above 64 KB is granted per kernel once its limit is raised.
 template <bool BF16, int D, int G, bool APP, bool NT>
-spkv_status launch_flat_k(const Args &a, int part, const FlatLaunch &f, dim3 grid, dim3 block, size_t lds,
+spkv_status launch_flat_k(const Args &a, const FlatLaunch &f, dim3 grid, dim3 block, size_t lds,
                           TimedLaunch &tl) {
     static const hipError_t attr = hipFuncSetAttribute((const void *)flat_kernel<BF16, D, G, APP, NT>,
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, spkv::kLdsPerCU);
     if (attr != hipSuccess) return fail(SPKV_E_HIP, std::string("flat_kernel LDS limit: ") + hipGetErrorString(attr));
-    tl.launch(flat_kernel<BF16, D, G, APP, NT>, grid, block, lds, a, part, f);
+    tl.launch(flat_kernel<BF16, D, G, APP, NT>, grid, block, lds, a, f);
     return check_launch("flat_kernel");
 }
 
 // bf16: append mode (the step's new tokens come from k_new / v_new) and the
 // streaming hint select the instantiation.
 template <bool BF16, int D, int G>
-spkv_status launch_flat_g(const Args &a, int part, const FlatLaunch &f, dim3 grid, dim3 block, size_t lds,
+spkv_status launch_flat_g(const Args &a, const FlatLaunch &f, dim3 grid, dim3 block, size_t lds,
                           const int32_t *append_slots, TimedLaunch &tl) {
     if constexpr (BF16) {
         if (append_slots)
-            return a.cold_nt ? launch_flat_k<BF16, D, G, true, true>(a, part, f, grid, block, lds, tl)
-                             : launch_flat_k<BF16, D, G, true, false>(a, part, f, grid, block, lds, tl);
-        if (a.cold_nt) return launch_flat_k<BF16, D, G, false, true>(a, part, f, grid, block, lds, tl);
+            return a.cold_nt ? launch_flat_k<BF16, D, G, true, true>(a, f, grid, block, lds, tl)
+                             : launch_flat_k<BF16, D, G, true, false>(a, f, grid, block, lds, tl);
+        if (a.cold_nt) return launch_flat_k<BF16, D, G, false, true>(a, f, grid, block, lds, tl);
     }
-    return launch_flat_k<BF16, D, G, false, false>(a, part, f, grid, block, lds, tl);
+    return launch_flat_k<BF16, D, G, false, false>(a, f, grid, block, lds, tl);
 }
 
 template <bool BF16, int D>
-spkv_status launch_flat_d(const Args &a, int part, const FlatLaunch &f, int head_groups,
+spkv_status launch_flat_d(const Args &a, const FlatLaunch &f, int head_groups,
                           const int32_t *append_slots, hipStream_t st) {
     const int waves = a.Hkv < kFlatWavesMax ? a.Hkv : kFlatWavesMax;
     dim3 grid(f.blocks, head_groups), block(64 * waves);
     const size_t lds = (size_t)waves * (BF16 ? FlatMfmaGeom<D>::WAVEB : FlatGeom<BF16, D>::WAVEB);
     TimedLaunch tl(SPKV_KERNEL_FLAT, st);
     switch (a.G) {
-    case 1: return launch_flat_g<BF16, D, 1>(a, part, f, grid, block, lds, append_slots, tl);
-    case 2: return launch_flat_g<BF16, D, 2>(a, part, f, grid, block, lds, append_slots, tl);
-    case 3: return launch_flat_g<BF16, D, 3>(a, part, f, grid, block, lds, append_slots, tl);
-    case 4: return launch_flat_g<BF16, D, 4>(a, part, f, grid, block, lds, append_slots, tl);
-    case 5: return launch_flat_g<BF16, D, 5>(a, part, f, grid, block, lds, append_slots, tl);
-    case 6: return launch_flat_g<BF16, D, 6>(a, part, f, grid, block, lds, append_slots, tl);
-    case 7: return launch_flat_g<BF16, D, 7>(a, part, f, grid, block, lds, append_slots, tl);
-    case 8: return launch_flat_g<BF16, D, 8>(a, part, f, grid, block, lds, append_slots, tl);
+    case 1: return launch_flat_g<BF16, D, 1>(a, f, grid, block, lds, append_slots, tl);
+    case 2: return launch_flat_g<BF16, D, 2>(a, f, grid, block, lds, append_slots, tl);
+    case 3: return launch_flat_g<BF16, D, 3>(a, f, grid, block, lds, append_slots, tl);
+    case 4: return launch_flat_g<BF16, D, 4>(a, f, grid, block, lds, append_slots, tl);
+    case 5: return launch_flat_g<BF16, D, 5>(a, f, grid, block, lds, append_slots, tl);
+    case 6: return launch_flat_g<BF16, D, 6>(a, f, grid, block, lds, append_slots, tl);
+    case 7: return launch_flat_g<BF16, D, 7>(a, f, grid, block, lds, append_slots, tl);
+    case 8: return launch_flat_g<BF16, D, 8>(a, f, grid, block, lds, append_slots, tl);
     default: return fail(SPKV_E_INVAL, "unsupported GQA group size");
     }
 }
 
-spkv_status launch_flat(const Args &a, bool bf16, int d, int part, const FlatLaunch &f, int head_groups,
+spkv_status launch_flat(const Args &a, bool bf16, int d, const FlatLaunch &f, int head_groups,
                         const int32_t *append_slots, hipStream_t st) {
     if (f.blocks <= 0 || a.B == 0) return SPKV_OK;
-    if (bf16) return d == 128 ? launch_flat_d<true, 128>(a, part, f, head_groups, append_slots, st)
-                              : launch_flat_d<true, 64>(a, part, f, head_groups, append_slots, st);
-    return d == 128 ? launch_flat_d<false, 128>(a, part, f, head_groups, nullptr, st)
-                    : launch_flat_d<false, 64>(a, part, f, head_groups, nullptr, st);
+    if (bf16) return d == 128 ? launch_flat_d<true, 128>(a, f, head_groups, append_slots, st)
+                              : launch_flat_d<true, 64>(a, f, head_groups, append_slots, st);
+    return d == 128 ? launch_flat_d<false, 128>(a, f, head_groups, nullptr, st)
+                    : launch_flat_d<false, 64>(a, f, head_groups, nullptr, st);
 }
 
-spkv_status launch_prefix(const Args &a, const Plan &p, int d, hipStream_t st) {
+spkv_status launch_prefix(const Args &a, const Plan &p, int d, bool bf16, hipStream_t st) {
     if (p.prefix_splits <= 0 || p.prefix_mtiles <= 0) return SPKV_OK;
+    if (!bf16) {
+        dim3 grid(p.prefix_splits, p.prefix_mtiles, a.ng * a.Hkv), block(256);
+        TimedLaunch tl(SPKV_KERNEL_PREFIX, st);
+        if (d == 128) tl.launch(prefix_f32_kernel<128>, grid, block, 0, a);
+        else tl.launch(prefix_f32_kernel<64>, grid, block, 0, a);
+        return check_launch("prefix_f32_kernel");
+    }
     dim3 grid(p.prefix_splits, p.prefix_mtiles, a.ng * a.Hkv), block(64 * p.prefix_waves * p.prefix_key_halves);
     TimedLaunch tl(SPKV_KERNEL_PREFIX, st);
     const int key = p.prefix_waves * 1000 + d + (p.prefix_split_p ? 10000 : 0) + (p.prefix_key_halves == 2 ? 100000 : 0);
@@ -1675,7 +1841,7 @@ spkv_status launch_prefix(const Args &a, const Plan &p, int d, hipStream_t st) {
     return check_launch("prefix_mfma_kernel");
 }
 
-spkv_status launch_merge(const Args &a, int d, float *out, float *lse, const FlatLaunch &fr, const FlatLaunch &fp,
+spkv_status launch_merge(const Args &a, int d, float *out, float *lse, const FlatLaunch &fr,
                          const int32_t *append_slots, const uint8_t *prefix_np, hipStream_t st) {
     const int64_t rows = (int64_t)fr.nreq * a.Hq;
     if (rows == 0) return SPKV_OK;
@@ -1687,11 +1853,11 @@ spkv_status launch_merge(const Args &a, int d, float *out, float *lse, const Fla
     if (append_slots) {
         for (int i = 0; i < fr.nreq; ++i) ap.slots[i] = append_slots[fr.b0 + i];
         grid.x += (unsigned)((fr.nreq + 3) / 4);   // the new-token waves
-        if (d == 128) tl.launch(merge_kernel<128, true>, grid, block, 0, a, out, lse, fr, fp, ap);
-        else tl.launch(merge_kernel<64, true>, grid, block, 0, a, out, lse, fr, fp, ap);
+        if (d == 128) tl.launch(merge_kernel<128, true>, grid, block, 0, a, out, lse, fr, ap);
+        else tl.launch(merge_kernel<64, true>, grid, block, 0, a, out, lse, fr, ap);
     } else {
-        if (d == 128) tl.launch(merge_kernel<128>, grid, block, 0, a, out, lse, fr, fp, ap);
-        else tl.launch(merge_kernel<64>, grid, block, 0, a, out, lse, fr, fp, ap);
+        if (d == 128) tl.launch(merge_kernel<128>, grid, block, 0, a, out, lse, fr, ap);
+        else tl.launch(merge_kernel<64>, grid, block, 0, a, out, lse, fr, ap);
     }
     return check_launch("merge_kernel");
 }
@@ -1732,7 +1898,7 @@ Args make_args(const spkv_batch *b, const spkv_kv *kv, const Plan &p, void *ws) 
     a.flat_tau = p.flat_chunk;
     a.prefix_tau = p.prefix_chunk > 0 ? p.prefix_chunk : 1;
     a.prefix_granule = spkv::kPrefixKeyTile;
-    a.prefix_mode = !p.run_prefix ? 0 : (p.prefix_as_flat ? 2 : 1);
+    a.prefix_mode = p.run_prefix ? 1 : 0;
     a.cascade = p.cascade;
     return a;
 }
@@ -1782,19 +1948,14 @@ spkv_status run_decode(const spkv_batch *b, const spkv_kv *kv, const int32_t *ca
     // not compete with the paged pass's reads.  Sub-batch i is entry i of
     // both paged passes.
     for (size_t i = 0; i < p.flat.size(); ++i) {
-        if (p.run_prefix && !bf16) {
-            st = launch_flat(a, false, b->head_dim, kPartPrefix, p.pflat[i], p.flat_head_groups, nullptr, hs);
-            if (st != SPKV_OK) return st;
-        }
-        st = launch_flat(a, bf16, b->head_dim, kPartRest, p.flat[i], p.flat_head_groups, app ? app->slots : nullptr,
+        st = launch_flat(a, bf16, b->head_dim, p.flat[i], p.flat_head_groups, app ? app->slots : nullptr,
                          hs);
         if (st != SPKV_OK) return st;
     }
-    if (p.run_prefix && bf16) {
-        st = launch_prefix(a, p, b->head_dim, hs);
+    if (p.run_prefix) {
+        st = launch_prefix(a, p, b->head_dim, bf16, hs);
         if (st != SPKV_OK) return st;
     }
-    static const FlatLaunch kNone{};
     // Prefix partials per request (MFMA prefix pass): the split rule of the
     // prefix kernel applied to the host copies (validated by the plan).
     std::vector<uint8_t> prefix_np;
@@ -1810,8 +1971,8 @@ spkv_status run_decode(const spkv_batch *b, const spkv_kv *kv, const int32_t *ca
         }
     }
     for (size_t i = 0; i < p.flat.size(); ++i) {
-        st = launch_merge(a, b->head_dim, out, lse, p.flat[i], p.prefix_as_flat && p.run_prefix ? p.pflat[i] : kNone,
-                          app ? app->slots : nullptr, prefix_np.empty() ? nullptr : prefix_np.data(), hs);
+        st = launch_merge(a, b->head_dim, out, lse, p.flat[i], app ? app->slots : nullptr,
+                          prefix_np.empty() ? nullptr : prefix_np.data(), hs);
         if (st != SPKV_OK) return st;
     }
     return SPKV_OK;

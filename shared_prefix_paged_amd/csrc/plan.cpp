@@ -178,11 +178,13 @@ spkv_status make_plan(const spkv_batch *b, const int32_t *cascade, int32_t num_c
         if (f.blocks > 0) p->flat_chunk = std::max<int32_t>(p->flat_chunk, (int32_t)(f.total / f.blocks));
     }
     // ---- prefix pass ------------------------------------------------------
-    p->prefix_as_flat = !bf16;
+    // One batched contraction per cascade group and KV head in both dtypes:
+    // bf16 on MFMA in row tiles of 1, 2 or 4 waves of 32 rows; float32 on the
+    // VALU in row tiles of 32 rows.  Same key-split rule for both.
     p->run_prefix = max_lp_c > 0;
-    if (p->run_prefix && bf16) {
+    if (p->run_prefix) {
         int w = (int)std::min<int64_t>(4, (max_m + 31) / 32);
-        p->prefix_waves = w <= 1 ? 1 : (w == 2 ? 2 : 4);   // tile variants: 1, 2 or 4 waves of 32 rows
+        p->prefix_waves = !bf16 ? 1 : (w <= 1 ? 1 : (w == 2 ? 2 : 4));   // bf16 tile variants: 1, 2 or 4 waves
         // Tiles of 4 row waves take the two-key-half variant: one 8-wave block
         // (two 64 KB rings) per CU instead of two 4-wave blocks, and half as
         // many partial states per row.
@@ -202,7 +204,10 @@ spkv_status make_plan(const spkv_batch *b, const int32_t *cascade, int32_t num_c
         // is one chunk).
         const int64_t target = std::max<int64_t>(1, (int64_t)num_cus * 2 / p->prefix_key_halves);
         int64_t pt = (prefix_work + target - 1) / target;
-        pt = std::max<int64_t>(pt, 256);
+        // A floor on the chunk keeps partial states (written, then merged) few
+        // per row; the float32 contraction works a tile at a time and takes a
+        // lower one so short prefixes still spread over several blocks.
+        pt = std::max<int64_t>(pt, bf16 ? 256 : 64);
         pt = (pt + kPrefixKeyTile - 1) / kPrefixKeyTile * kPrefixKeyTile;
         auto blocks_for = [&](int64_t chunk) {
             int64_t nb = 0;
@@ -218,26 +223,6 @@ spkv_status make_plan(const spkv_batch *b, const int32_t *cascade, int32_t num_c
         while (pt < max_lp_c && pt < (1 << 20) && blocks_for(pt) > target) pt += kPrefixKeyTile;
         p->prefix_chunk = (int32_t)std::min<int64_t>(pt, 1 << 20);
         p->prefix_splits = std::min<int32_t>(kPrefixSplitCap, splits_for(max_lp_c, p->prefix_chunk));
-    } else if (p->run_prefix) {
-        // float32: the prefix part of cascade groups runs as a paged pass over the slab.
-        std::vector<int64_t> L((size_t)B);
-        for (int i = 0; i < B; ++i) {
-            const int g = b->host_group_of[i];
-            L[(size_t)i] = (g >= 0 && mask_get(p->cascade, g)) ? b->host_hot_len[g] : 0;
-        }
-        p->pflat = plan_flat(L, p->flat_head_groups, flat_blocks_per_cu(false, D, hpb), num_cus);
-        for (const auto &f : p->pflat)
-            if (f.total >= (int64_t(1) << 31)) return fail(SPKV_E_INVAL, "a paged-pass sub-batch exceeds 2^31 tokens");
-        p->prefix_splits = 0;
-        p->prefix_chunk = 0;
-        for (const auto &f : p->pflat) {
-            p->prefix_splits = std::max(p->prefix_splits, f.max_parts);
-            if (f.blocks > 0) p->prefix_chunk = std::max<int32_t>(p->prefix_chunk, (int32_t)(f.total / f.blocks));
-        }
-        p->run_prefix = false;
-        for (const auto &f : p->pflat) p->run_prefix = p->run_prefix || f.blocks > 0;
-        p->prefix_waves = 0;
-        p->prefix_mtiles = 0;
     }
     p->splits_total = p->prefix_splits + p->flat_splits;
 
@@ -245,13 +230,12 @@ spkv_status make_plan(const spkv_batch *b, const int32_t *cascade, int32_t num_c
     p->flat_items = 0;
     p->prefix_items = 0;
     for (const auto &f : p->flat) p->flat_items += (int64_t)f.blocks * p->flat_head_groups;
-    for (const auto &f : p->pflat) p->prefix_items += (int64_t)f.blocks * p->flat_head_groups;
     for (int g = 0; g < ng; ++g) {
         const int64_t n = members[(size_t)g];
         const int64_t lp = b->host_hot_len[g];
         if (n == 0 || lp == 0) continue;
         if (mask_get(p->cascade, g)) {
-            if (bf16) {
+            {
                 const int64_t mt = 32 * p->prefix_waves;
                 p->prefix_items += Hkv * ((n * G + mt - 1) / mt) *
                                    splits_for(lp, chunk_for(lp, p->prefix_chunk, kPrefixSplitCap, kPrefixKeyTile));
@@ -328,10 +312,7 @@ spkv_status spkv_plan_parts(const spkv_batch *batch, const int32_t *cascade, int
     }
     if (prefix_parts_out) {
         for (int b = 0; b < B; ++b) prefix_parts_out[b] = 0;
-        if (p.prefix_as_flat) {
-            for (const auto &f : p.pflat)
-                for (int i = 0; i < f.nreq; ++i) prefix_parts_out[f.b0 + i] = flat_parts(f, i, &first);
-        } else if (p.run_prefix) {
+        if (p.run_prefix) {
             for (int b = 0; b < B; ++b) {
                 const int g = batch->host_group_of[b];
                 if (g < 0 || !((p.cascade.bits[g >> 5] >> (g & 31)) & 1u)) continue;

@@ -80,6 +80,12 @@ def small_cases():
             batch=300, num_q_heads=8, num_kv_heads=2, head_dim=128, dtype="bf16", group_prefix_len=[96, 31, 700],
             group_of=[int(g) for g in np.random.default_rng(24).integers(-1, 3, 300)],
             suffix_len=[int(x) for x in np.random.default_rng(25).integers(1, 90, 300)], seed=24),
+        # float32 prefix contraction: several 32-row tiles per group and
+        # head, several key splits, a ragged last tile, two groups
+        "f32_many_rows": lambda: W.make_custom(
+            batch=45, num_q_heads=8, num_kv_heads=2, head_dim=128, dtype="f32", group_prefix_len=[3001, 40],
+            group_of=[0] * 40 + [1, 1, 1, -1, 0], suffix_len=[int(x) for x in np.random.default_rng(28).integers(1, 90, 45)],
+            seed=26),
         "f32_two_sub_batches": lambda: W.make_custom(
             batch=260, num_q_heads=4, num_kv_heads=1, head_dim=64, dtype="f32", group_prefix_len=[50, 130],
             group_of=[int(g) for g in np.random.default_rng(26).integers(-1, 2, 260)],
