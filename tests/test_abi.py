@@ -139,6 +139,12 @@ def test_group_membership_is_group_of_alone():
         batch = R.DecodeBatch(q, bad, [0, 10], [10, 5], tables, [1, 1, 1], 1, 2)
         with pytest.raises(spkv.InvalidArgument):
             batch.plan()
+    # at most 512 groups per step (the per-group cascade mask's size): 513 is refused
+    many = R.DecodeBatch(q, [0, 1, 512], list(range(513)), [1] * 513, tables, [1, 1, 1], 1, 2)
+    with pytest.raises(spkv.InvalidArgument):
+        many.plan()
+    ok = R.DecodeBatch(q, [0, 1, 511], list(range(512)), [1] * 512, tables, [1, 1, 1], 1, 2)
+    ok.plan()
     # members counted from group_of: two groups of 2 and 1 requests, cascade planned for both
     batch = R.DecodeBatch(q, [1, 0, 1], [0, 300], [300, 300], tables, [1, 1, 1], 1, 2)
     fp, pp = batch.plan_parts()

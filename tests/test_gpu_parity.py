@@ -86,6 +86,15 @@ def small_cases():
             batch=45, num_q_heads=8, num_kv_heads=2, head_dim=128, dtype="f32", group_prefix_len=[3001, 40],
             group_of=[0] * 40 + [1, 1, 1, -1, 0], suffix_len=[int(x) for x in np.random.default_rng(28).integers(1, 90, 45)],
             seed=26),
+        # the most groups a step takes (512): most groups with one or two
+        # members, some with none, a few requests without a prefix; more
+        # requests than one paged-pass launch takes
+        "bf16_512_groups": lambda: W.make_custom(
+            batch=700, num_q_heads=4, num_kv_heads=2, head_dim=64, dtype="bf16",
+            group_prefix_len=[int(x) for x in np.random.default_rng(29).integers(1, 70, 512)],
+            group_of=[-1 if i % 97 == 0 else int(g)
+                      for i, g in enumerate(np.random.default_rng(30).integers(0, 512, 700))],
+            suffix_len=[int(x) for x in np.random.default_rng(31).integers(1, 20, 700)], seed=27),
         "f32_two_sub_batches": lambda: W.make_custom(
             batch=260, num_q_heads=4, num_kv_heads=1, head_dim=64, dtype="f32", group_prefix_len=[50, 130],
             group_of=[int(g) for g in np.random.default_rng(26).integers(-1, 2, 260)],
@@ -296,3 +305,44 @@ def test_full_size_every_row(name, lp):
         note(f"    {mode}: max_abs={e_o:.3e} lse={e_l:.3e} rel={rel:.3e} outside_hull={outside}")
         assert e_o <= TOL_O and e_l <= TOL_LSE and rel <= TOL_REL
         assert outside == 0
+
+
+@pytest.mark.parametrize("P", [1, 16])
+def test_cold_fallback_matches_admitted_prefix(P):
+    # [GKV] Appendix B.10: a prefix that finds no room in the HOT pool stays in
+    # COLD as each of its requests' own leading tokens (private copies), and
+    # those requests take the paged pass.  Their attention must be what the
+    # admitted prefix gives: group 1 below is not admitted, group 0 is.
+    note(f"[gpu] COLD fallback P={P}")
+    wl = W.make_custom(batch=10, num_q_heads=8, num_kv_heads=2, head_dim=128, dtype="bf16",
+                       group_prefix_len=[300, 45], group_of=[0, 0, 1, 0, 1, 1, 0, -1, 0, 1],
+                       suffix_len=[5, 17, 1, 40, 16, 33, 2, 9, 64, 3], page_size=P, seed=61)
+    ref_o, ref_l = decode_reference(wl)
+    moved = wl.group_of == 1
+    ks, vs, ls = [], [], []
+    for b in range(wl.batch):
+        sk, sv = wl.suffix_kv(b)
+        if moved[b]:
+            sk, sv = np.concatenate([wl.prefix_k[1], sk]), np.concatenate([wl.prefix_v[1], sv])
+        ks.append(sk)
+        vs.append(sv)
+        ls.append(len(sk))
+    ls = np.asarray(ls, np.int64)
+    pages = W.cold_pages_for(int(ls.sum()), wl.batch, P)
+    fb = dataclasses.replace(
+        wl, cfg=dataclasses.replace(wl.cfg, num_groups=1), group_prefix_len=wl.group_prefix_len[:1],
+        prefix_k=wl.prefix_k[:1], prefix_v=wl.prefix_v[:1], group_of=np.where(moved, -1, wl.group_of).astype(np.int32),
+        suffix_len=ls, suffix_k=np.concatenate(ks), suffix_v=np.concatenate(vs), suffix_offsets=None,
+        num_cold_pages=pages, free_order=np.random.default_rng(62).permutation(pages).astype(np.int32),
+        hot_capacity=int(wl.group_prefix_len[0]))
+    fb.__post_init__()
+    st = setup_single_step(fb)
+    ws = R.workspace(st.batch)
+    for mode, fn in (("cascade", lambda: R.cascade_decode(st.batch, st.pools, ws)),
+                     ("dense", lambda: R.dense_decode(st.batch, st.pools, ws)),
+                     ("per_group", lambda: R.decode_step(st.batch, st.pools, R.default_params(A.SPKV_MODE_PER_GROUP), ws)[:2])):
+        out, lse = fn()
+        torch.cuda.synchronize()
+        e_o, e_l, rel = errors(out, lse, ref_o, ref_l)
+        note(f"    {mode}: max_abs={e_o:.2e} lse={e_l:.2e} rel={rel:.2e}")
+        assert e_o <= TOL_O and e_l <= TOL_LSE and rel <= TOL_REL
