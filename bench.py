@@ -218,8 +218,9 @@ def layout_study(args) -> int:
     pick = [args.layout_variant] if args.layout_variant else list(variants)
     scratch = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device=dev)
     clean = torch.zeros(args.flush_mib << 20, dtype=torch.uint8, device=dev)
-    attn_ids = (A.SPKV_KERNEL_PREFIX, A.SPKV_KERNEL_FLAT, A.SPKV_KERNEL_MERGE)
-    kname = {A.SPKV_KERNEL_PREFIX: "prefix_mfma", A.SPKV_KERNEL_FLAT: "flat_paged", A.SPKV_KERNEL_MERGE: "merge"}
+    attn_ids = (A.SPKV_KERNEL_PREFIX, A.SPKV_KERNEL_FLAT, A.SPKV_KERNEL_MERGE, A.SPKV_KERNEL_PAGED_PREFIX)
+    kname = {A.SPKV_KERNEL_PREFIX: "prefix_mfma", A.SPKV_KERNEL_FLAT: "flat_paged", A.SPKV_KERNEL_MERGE: "merge",
+             A.SPKV_KERNEL_PAGED_PREFIX: "paged_prefix"}
     res = {}
     built = {}
     for name in pick:
@@ -356,6 +357,7 @@ def multi_layer(args) -> int:
             one_step()
         torch.cuda.synchronize()
         per = {name: kt.read(k) for name, k in (("prefix_mfma", A.SPKV_KERNEL_PREFIX), ("flat_paged", A.SPKV_KERNEL_FLAT),
+                                                ("paged_prefix", A.SPKV_KERNEL_PAGED_PREFIX),
                                                 ("merge", A.SPKV_KERNEL_MERGE), ("append", A.SPKV_KERNEL_CACHE))}
     assert torch.isfinite(out).all()
     print(json.dumps({
@@ -397,7 +399,7 @@ def multistep(args) -> int:
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
     steps, fork_step, release_step = 32, 8, 24
-    attn_ids = (A.SPKV_KERNEL_PREFIX, A.SPKV_KERNEL_FLAT, A.SPKV_KERNEL_MERGE)
+    attn_ids = (A.SPKV_KERNEL_PREFIX, A.SPKV_KERNEL_FLAT, A.SPKV_KERNEL_MERGE, A.SPKV_KERNEL_PAGED_PREFIX)
     runs = {}
     for P in (1, 16):
         wl = W.make_workload(W.CONFIGS["C4"], page_size=P, extra_steps=40)
@@ -638,7 +640,7 @@ def main():
     cfg = W.CONFIGS[args.config]
     cold_warm = 10 if args.cold_runs > 0 else 0
     graph_steps = max(0, args.graph_steps)
-    total_steps = args.warmup + 2 * args.steps + 1 + cold_warm + max(0, args.cold_runs) + \
+    total_steps = args.warmup + 4 * args.steps + 1 + cold_warm + max(0, args.cold_runs) + \
         (graph_steps + 3 if graph_steps else 0)
     wl = W.make_workload(cfg, prefix_len=args.lp, page_size=args.page_size, extra_steps=max(32, total_steps + 1))
     if args.contiguous:
@@ -762,7 +764,28 @@ def main():
             per_step.append((batch.lens_h.copy(), fp, pp, [int(c) for c in choice]))
         torch.cuda.synchronize()
     kt_ms = {k: kt.read(k) for k in (A.SPKV_KERNEL_PREFIX, A.SPKV_KERNEL_FLAT, A.SPKV_KERNEL_MERGE,
-                                     A.SPKV_KERNEL_CACHE)}
+                                     A.SPKV_KERNEL_CACHE, A.SPKV_KERNEL_PAGED_PREFIX)}
+    # The same steps again with the paged pass and the prefix contraction as
+    # two launches (params.single_launch = 0), when the step above ran them as
+    # one: each kernel's own duration and roofline, beside the single launch's.
+    # (GPU time per step without per-kernel events first, then the kernels.)
+    kt2_ms, gpu2_ms = None, None
+    if kt_ms[A.SPKV_KERNEL_PAGED_PREFIX][1] > 0:
+        params.single_launch = 0
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            one_step()
+        e1.record()
+        torch.cuda.synchronize()
+        gpu2_ms = e0.elapsed_time(e1) / args.steps
+        with R.KernelTimer() as kt2:
+            for _ in range(args.steps):
+                one_step()
+            torch.cuda.synchronize()
+        kt2_ms = {k: kt2.read(k) for k in (A.SPKV_KERNEL_PREFIX, A.SPKV_KERNEL_FLAT, A.SPKV_KERNEL_MERGE)}
+        params.single_launch = 1
 
     # ---- the same steps through the HIP-graph entry point: host time of the
     # call (record, update the graph's kernel nodes in place, launch) and GPU
@@ -817,7 +840,7 @@ def main():
             one_step(flush)
         torch.cuda.synchronize()
         times, toks = [], []
-        attn_ids = (A.SPKV_KERNEL_PREFIX, A.SPKV_KERNEL_FLAT, A.SPKV_KERNEL_MERGE)
+        attn_ids = (A.SPKV_KERNEL_PREFIX, A.SPKV_KERNEL_FLAT, A.SPKV_KERNEL_MERGE, A.SPKV_KERNEL_PAGED_PREFIX)
 
         def flush_and_wait():
             flush()
@@ -875,31 +898,51 @@ def main():
     flat_bytes, prefix_bytes = float(np.mean(flat_b)), float(np.mean(prefix_b))
     prefix_flops, merge_bytes = float(np.mean(prefix_f)), float(np.mean(merge_b))
 
-    kernels = {}
-    for name, kid, nbytes, flops in (("prefix_mfma", A.SPKV_KERNEL_PREFIX, prefix_bytes, prefix_flops),
-                                     ("flat_paged", A.SPKV_KERNEL_FLAT, flat_bytes, 0.0),
-                                     ("merge", A.SPKV_KERNEL_MERGE, merge_bytes, 0.0)):
-        ms, n = kt_ms[kid]
-        if n == 0:
-            continue
-        avg_us = 1e3 * ms / n
-        kernels[name] = {"avg_us": round(avg_us, 3), "launches": n,
-                         "alg_bytes": int(nbytes), "gbps": round(nbytes / avg_us / 1e3, 1)}
-        if flops:
-            kernels[name]["tflops"] = round(flops / avg_us / 1e6, 2)
-            kernels[name]["mfma_frac"] = round(flops / avg_us / 1e6 / BF16_PEAK_TFLOPS, 4)
+    # Launch classes: the paged pass and the prefix contraction as two
+    # launches, or as one paged_prefix launch (both roles' bytes and FLOPs).
+    classes = (("prefix_mfma", A.SPKV_KERNEL_PREFIX, prefix_bytes, prefix_flops),
+               ("flat_paged", A.SPKV_KERNEL_FLAT, flat_bytes, 0.0),
+               ("paged_prefix", A.SPKV_KERNEL_PAGED_PREFIX, flat_bytes + prefix_bytes, prefix_flops),
+               ("merge", A.SPKV_KERNEL_MERGE, merge_bytes, 0.0))
+
+    def kernel_table(ms_by_class):
+        table = {}
+        for name, kid, nbytes, flops in classes:
+            if kid not in ms_by_class:
+                continue
+            ms, n = ms_by_class[kid]
+            if n == 0:
+                continue
+            avg_us = 1e3 * ms / n
+            table[name] = {"avg_us": round(avg_us, 3), "launches": n,
+                           "alg_bytes": int(nbytes), "gbps": round(nbytes / avg_us / 1e3, 1),
+                           "hbm_frac": round(nbytes / avg_us / 1e3 / HBM_PEAK_GBPS, 4)}
+            if flops:
+                table[name]["tflops"] = round(flops / avg_us / 1e6, 2)
+                table[name]["mfma_frac"] = round(flops / avg_us / 1e6 / BF16_PEAK_TFLOPS, 4)
+            tr = measured_traffic(args.traffic, traffic_key, args.mode, name)
+            if tr:
+                table[name]["traffic_bytes"] = int(tr)
+                table[name]["traffic_frac"] = round(tr / avg_us / 1e3 / HBM_PEAK_GBPS, 4)
+        return table
+
+    traffic_key = args.config if args.lp is None else f"{args.config}@{args.lp}"
+    kernels = kernel_table(kt_ms)
     dom = max(kernels, key=lambda k: kernels[k]["avg_us"])
     dk = kernels[dom]
-    if dom == "prefix_mfma" and prefix_flops / (dk["avg_us"] * 1e6) / BF16_PEAK_TFLOPS > \
-            (prefix_bytes / dk["avg_us"] / 1e3) / HBM_PEAK_GBPS:
+    if dk.get("mfma_frac", 0.0) > dk["hbm_frac"]:
         roofline = {"bound": "mfma", "achieved": dk["tflops"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(dk["tflops"] / BF16_PEAK_TFLOPS, 4), "traffic": None}
     else:
         roofline = {"bound": "hbm", "achieved": dk["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(dk["gbps"] / HBM_PEAK_GBPS, 4), "traffic": None}
     roofline["kernel"] = dom
-    roofline["traffic"] = measured_traffic(args.traffic, args.config if args.lp is None else f"{args.config}@{args.lp}",
-                                           args.mode, dom)
+    two_launches = None
+    if kt2_ms is not None:
+        two_launches = {"kernels": kernel_table(kt2_ms), "gpu_ms_per_step": round(gpu2_ms, 4),
+                        "note": "the same steps with spkv_dispatch_params.single_launch = 0: the paged pass and "
+                                "the prefix contraction as separate launches (each kernel's own roofline)"}
+    roofline["traffic"] = measured_traffic(args.traffic, traffic_key, args.mode, dom)
     if roofline["traffic"]:
         # HBM bytes the counters saw (L2 <-> fabric) over the same duration:
         # for the flat pass over a shared slab the algorithmic bytes count every
@@ -911,10 +954,14 @@ def main():
     if cold_res is not None:
         cold_res["warm_attention_us"] = round(attn_us, 2)
     # Step roofline: T* = sum over kernels of max(bytes / HBM peak, flops / MFMA peak).
+    # Per role (the paged pass, the prefix contraction, the merge), whether
+    # the first two ran as one launch or two.
     t_star = 0.0
-    for name, nbytes, flops in (("prefix_mfma", prefix_bytes, prefix_flops), ("flat_paged", flat_bytes, 0.0),
-                                ("merge", merge_bytes, 0.0)):
-        if name in kernels:
+    ran = set(kernels)
+    for names, nbytes, flops in ((("prefix_mfma", "paged_prefix"), prefix_bytes, prefix_flops),
+                                 (("flat_paged", "paged_prefix"), flat_bytes, 0.0),
+                                 (("merge",), merge_bytes, 0.0)):
+        if ran.intersection(names):
             t_star += max(nbytes / (HBM_PEAK_GBPS * 1e3), flops / (BF16_PEAK_TFLOPS * 1e6))
     step_roofline = {"t_star_us": round(t_star, 2), "t_measured_us": round(attn_us, 2),
                      "frac": round(t_star / attn_us, 4) if attn_us > 0 else None,
@@ -956,6 +1003,7 @@ def main():
         "kv_tokens_per_s_attention": round(tokens / args.steps / (attn_us * 1e-6), 1),
         "kernels": kernels,
         "host": host_step,
+        "two_launches": two_launches,
         "graph": graph_res,
         "plan": {f: int(getattr(plan, f)) for f, _ in plan._fields_},
         "roofline": roofline,

@@ -334,6 +334,9 @@ typedef struct spkv_dispatch_params {
     double  prefix_tflops;         /* effective bf16 MFMA rate of the prefix contraction */
     double  row_cost_ns;           /* cascade cost per query row of a group that takes it
                                       (its prefix partial states: written, then merged) */
+    int32_t single_launch;         /* 1 (default): the paged pass and the prefix contraction run as one
+                                      launch where the plan allows it (spkv_plan_info.single_launch);
+                                      0: always two launches.  Results are the same either way. */
 } spkv_dispatch_params;
 
 /* Defaults fitted on MI355X (see the design notes for the fit). */
@@ -344,6 +347,10 @@ spkv_status spkv_dispatch(const spkv_batch *batch, const spkv_dispatch_params *p
 
 /* Dispatch, then run: groups chosen for cascade take the prefix contraction,
  * the others are folded into the flat pass; one merge finishes every row.
+ * Where the plan allows it and params->single_launch is set, the paged pass
+ * and the prefix contraction run as one launch (the prefix blocks fill the
+ * paged pass's tail); the results are bit-identical to two launches.
+ * spkv_cascade_decode uses the single launch wherever the plan allows it.
  * cascade_out (host [ng], nullable) reports the choice. */
 spkv_status spkv_decode_step(const spkv_batch *batch, const spkv_kv *kv, const spkv_dispatch_params *params,
                              float *out, float *lse, void *ws, size_t ws_bytes, void *stream,
@@ -430,6 +437,10 @@ typedef struct spkv_plan_info {
     int32_t prefix_granule;
     int32_t prefix_key_halves;     /* 2: each prefix work item's key chunk is split over two wave sets whose
                                       states merge in LDS (one partial per row per item either way) */
+    int32_t single_launch;         /* 1: the paged pass's ranges and the prefix blocks can run as one launch
+                                      (bf16, head_dim 128, Hkv >= 4, one paged sub-batch of <= 256 requests,
+                                      prefix tiles of 4 row waves with two key halves); the paged ranges come
+                                      first in the grid and the prefix blocks take CUs as ranges finish */
 } spkv_plan_info;
 
 spkv_status spkv_plan_query(const spkv_batch *batch, const int32_t *cascade, spkv_plan_info *out);
@@ -442,11 +453,12 @@ spkv_status spkv_plan_query(const spkv_batch *batch, const int32_t *cascade, spk
 spkv_status spkv_plan_parts(const spkv_batch *batch, const int32_t *cascade, int32_t *flat_parts,
                             int32_t *prefix_parts);
 
-#define SPKV_KERNEL_PREFIX  0   /* prefix contraction (bf16 MFMA) */
-#define SPKV_KERNEL_FLAT    1   /* paged pass: suffix part, or whole context when flat */
-#define SPKV_KERNEL_MERGE   2   /* log-sum-exp merge of partial states */
-#define SPKV_KERNEL_CACHE   3   /* hot_write / reshape_and_cache / copy_blocks */
-#define SPKV_NUM_KERNELS    4
+#define SPKV_KERNEL_PREFIX        0   /* prefix contraction (bf16 MFMA, or float32) */
+#define SPKV_KERNEL_FLAT          1   /* paged pass: suffix part, or whole context when flat */
+#define SPKV_KERNEL_MERGE         2   /* log-sum-exp merge of partial states */
+#define SPKV_KERNEL_CACHE         3   /* hot_write / reshape_and_cache / copy_blocks / append_tokens */
+#define SPKV_KERNEL_PAGED_PREFIX  4   /* paged pass and prefix contraction in one launch */
+#define SPKV_NUM_KERNELS          5
 
 /* When on, every launch is bracketed by HIP events on its stream. */
 spkv_status spkv_timing_enable(int32_t on);

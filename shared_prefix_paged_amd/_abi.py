@@ -9,7 +9,8 @@ P_i32, P_i64, P_f32, P_f64 = C.POINTER(c_i32), C.POINTER(c_i64), C.POINTER(c_f32
 SPKV_OK, SPKV_E_INVAL, SPKV_E_NOMEM, SPKV_E_STATE, SPKV_E_HIP = 0, -1, -2, -3, -4
 SPKV_DTYPE_BF16, SPKV_DTYPE_F32 = 0, 1
 SPKV_MODE_PER_GROUP, SPKV_MODE_BATCH_GLOBAL, SPKV_MODE_FORCE_CASCADE, SPKV_MODE_FORCE_DENSE = 0, 1, 2, 3
-SPKV_KERNEL_PREFIX, SPKV_KERNEL_FLAT, SPKV_KERNEL_MERGE, SPKV_KERNEL_CACHE, SPKV_NUM_KERNELS = 0, 1, 2, 3, 4
+SPKV_KERNEL_PREFIX, SPKV_KERNEL_FLAT, SPKV_KERNEL_MERGE, SPKV_KERNEL_CACHE = 0, 1, 2, 3
+SPKV_KERNEL_PAGED_PREFIX, SPKV_NUM_KERNELS = 4, 5
 SPKV_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
@@ -40,7 +41,8 @@ class spkv_kv(C.Structure):
 
 class spkv_dispatch_params(C.Structure):
     _fields_ = [("mode", c_i32), ("min_group_requests", c_i32), ("fixed_cost_us", c_f64),
-                ("flat_gbps", c_f64), ("prefix_gbps", c_f64), ("prefix_tflops", c_f64), ("row_cost_ns", c_f64)]
+                ("flat_gbps", c_f64), ("prefix_gbps", c_f64), ("prefix_tflops", c_f64), ("row_cost_ns", c_f64),
+                ("single_launch", c_i32)]
 
 
 class spkv_plan_info(C.Structure):
@@ -48,7 +50,7 @@ class spkv_plan_info(C.Structure):
                 ("prefix_waves", c_i32), ("prefix_mtiles", c_i32), ("flat_items", c_i64),
                 ("prefix_items", c_i64), ("workspace_bytes", c_i64), ("flat_split_cap", c_i32),
                 ("flat_head_tokens", c_i32), ("prefix_split_cap", c_i32), ("prefix_granule", c_i32),
-                ("prefix_key_halves", c_i32)]
+                ("prefix_key_halves", c_i32), ("single_launch", c_i32)]
 
 
 P_batch, P_kv, P_params = C.POINTER(spkv_batch), C.POINTER(spkv_kv), C.POINTER(spkv_dispatch_params)

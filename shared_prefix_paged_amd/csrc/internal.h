@@ -104,8 +104,9 @@ struct Plan {
     int64_t ws_bytes;
     std::vector<FlatLaunch> flat;    // paged pass (suffix, or whole context for flat-mode groups)
     int32_t flat_head_groups;        // grid y of the paged pass
-    bool run_prefix;          // some cascade group has Lp > 0 (bf16)
+    bool run_prefix;          // some cascade group has Lp > 0
     bool prefix_split_p;      // some cascade group is short: carry P as bf16 hi + lo
+    bool single_launch;       // the paged pass and the prefix contraction may share one launch
 };
 
 // LDS bytes of one wave of the bf16 paged pass: its ring (K and V rows of

@@ -815,16 +815,16 @@ struct MergeRows {
 // the LDS ring (4 x 8.25 KB per block of 4 waves) admits 4 blocks per CU.
 // bf16: the LDS ring (4 x 8 KB per wave for d = 128) admits one or two
 // blocks per CU, so registers are not the limit.
-template <bool BF16, int D, int G, bool APP = false, bool NT = false>
-__global__ __launch_bounds__(256, (BF16 ? 2 : (G <= 6 ? 4 : 3))) void flat_kernel(Args a, FlatLaunch fl) {
-    extern __shared__ __attribute__((aligned(1024))) char flat_smem[];
-    const int k = blockIdx.x;
-    const int wave = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63;
-    const int h = blockIdx.y * kFlatWavesMax + wave;
+// One block of the paged pass: range k of the stream-K split, head group hy;
+// wave `wave` (< kFlatWavesMax) of it takes KV head hy * kFlatWavesMax + wave
+// with its ring at smem + wave * WAVEB.
+template <bool BF16, int D, int G, bool APP, bool NT>
+__device__ __forceinline__ void flat_block(const Args &a, const FlatLaunch &fl, const int k, const int hy,
+                                           const int wave, const int lane, char *smem) {
+    const int h = hy * kFlatWavesMax + wave;
     if (h >= a.Hkv) return;
     constexpr int WAVEB = BF16 ? FlatMfmaGeom<D>::WAVEB : FlatGeom<BF16, D>::WAVEB;
-    char *ring = flat_smem + wave * WAVEB;
+    char *ring = smem + wave * WAVEB;
     const uint32_t ring_off = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_offset(ring));
     const int64_t T = fl.total;
     const int nb = fl.blocks;
@@ -858,6 +858,12 @@ __global__ __launch_bounds__(256, (BF16 ? 2 : (G <= 6 ? 4 : 3))) void flat_kerne
         if constexpr (BF16) attend_range_mfma<D, G, APP, NT>(a, r, b, h, t0, t1, slot0 + slot, lane, ring, ring_off);
         else attend_range<BF16, D, G>(a, r, b, h, t0, t1, slot0 + slot, lane, ring, ring_off);
     }
+}
+
+template <bool BF16, int D, int G, bool APP = false, bool NT = false>
+__global__ __launch_bounds__(256, (BF16 ? 2 : (G <= 6 ? 4 : 3))) void flat_kernel(Args a, FlatLaunch fl) {
+    extern __shared__ __attribute__((aligned(1024))) char flat_smem[];
+    flat_block<BF16, D, G, APP, NT>(a, fl, blockIdx.x, blockIdx.y, threadIdx.x >> 6, threadIdx.x & 63, flat_smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -915,10 +921,19 @@ __device__ __forceinline__ int vchunk_logical(int r, int p) {
 // over the same W x 32 query rows with a ring of its own; the halves merge
 // their states through LDS ([GKV] Eq. (1)) before one partial is written, so
 // a row gets half as many partial states at the same number of waves per CU.
-template <int D, int W, bool SPLIT_P, int KH = 1>
-__global__ __launch_bounds__(64 * W * KH) void prefix_mfma_kernel(Args a) {
+constexpr int kPrefixStages = 4;
+constexpr int kMemberWin = 40;                 // >= 32 rows / G + 1 members
+template <int D, int KH>
+constexpr int prefix_ring_bytes() { return KH * kPrefixStages * 2 * spkv::kPrefixKeyTile * D * 2; }
+
+// One block of the prefix contraction: key split s, row tile mt, (group, KV
+// head) gz.  smem: prefix_ring_bytes<D, KH>() bytes of LDS (1 KB aligned);
+// member_win: W * KH windows of kMemberWin entries in LDS.
+template <int D, int W, bool SPLIT_P, int KH>
+__device__ __forceinline__ void prefix_block(const Args &a, const int s, const int mt, const int gz, char *smem,
+                                             int32_t (*member_win)[kMemberWin]) {
     constexpr int NT = spkv::kPrefixKeyTile;   // 32 keys per tile
-    constexpr int STAGES = 4;
+    constexpr int STAGES = kPrefixStages;
     constexpr int KS = D / 16;                 // MFMA k-steps for Q.K
     constexpr int NDB = D / 32;                // 32-column blocks of the output
     constexpr int ROWB = D * 2;                // bytes per K/V row
@@ -929,19 +944,16 @@ __global__ __launch_bounds__(64 * W * KH) void prefix_mfma_kernel(Args a) {
     static_assert(IPW >= 1 && (NT / RPI) % W == 0, "tile must split evenly over the waves");
     constexpr int AHEAD = (STAGES - 2) * 2 * IPW;   // DMAs issued after a tile's own
     static_assert(KH == 1 || KH == 2, "one or two key halves");
-    __shared__ __attribute__((aligned(1024))) char smem[KH * STAGES * 2 * TILEB];
+    static_assert(prefix_ring_bytes<D, KH>() == KH * STAGES * 2 * TILEB, "ring size");
 
-    const int gz = blockIdx.z;
     const int g = gz / a.Hkv;
     const int h = gz % a.Hkv;
     if (g >= a.ng || !mask_get(a.cascade, g)) return;
     const int64_t base = a.hot_base[g];
     const int lp = a.hot_len[g];
     if (lp <= 0 || base < 0 || base + lp > a.hot_capacity) return;
-    const int mt = blockIdx.y;
     const int chunk = spkv::chunk_for(lp, a.prefix_tau, spkv::kPrefixSplitCap, NT);
     const int nsplit = spkv::splits_for(lp, chunk);
-    const int s = blockIdx.x;
     if (s >= nsplit) return;
     const int tid = threadIdx.x;
     const int wave_id = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -1024,8 +1036,7 @@ __global__ __launch_bounds__(64 * W * KH) void prefix_mfma_kernel(Args a) {
     // One scan of group_of (64 requests per wave-wide load, several loads in
     // flight) counts the members and writes the ids this wave's 32 rows need,
     // member ranks [kw0, kw0 + kWin), to its LDS window.
-    constexpr int kWin = 40;                   // >= 32 rows / G + 1 members
-    __shared__ int32_t member_win[W * KH][kWin];
+    constexpr int kWin = kMemberWin;
     int32_t *win = member_win[wave_id];
     const int kw0 = (mt * 32 * W + wave * 32) / a.G;
     int count = 0;                             // wave-uniform
@@ -1251,6 +1262,39 @@ __global__ __launch_bounds__(64 * W * KH) void prefix_mfma_kernel(Args a) {
                                                oacc[db][j + 3] * inv);
         }
     if (half == 0) a.lse_part[prow] = l_tot > 0.f ? m_run + __log2f(l_tot) : -INFINITY;
+}
+
+template <int D, int W, bool SPLIT_P, int KH = 1>
+__global__ __launch_bounds__(64 * W * KH) void prefix_mfma_kernel(Args a) {
+    __shared__ __attribute__((aligned(1024))) char smem[prefix_ring_bytes<D, KH>()];
+    __shared__ int32_t member_win[W * KH][kMemberWin];
+    prefix_block<D, W, SPLIT_P, KH>(a, blockIdx.x, blockIdx.y, blockIdx.z, smem, member_win);
+}
+
+// The paged pass and the prefix contraction in one launch (bf16, d = 128,
+// prefix tiles of 4 row waves and two key halves): blocks [0, paged_blocks)
+// are the paged pass's ranges (waves 0..3 of a block; the other four leave at
+// once), the rest are prefix blocks (all 8 waves).  Either role fills a CU's
+// LDS, so one block runs per CU; blocks are handed out in index order, so
+// every paged range starts at once (the split plan is one resident round)
+// and prefix blocks take CUs as paged ranges finish: the prefix work fills
+// the paged pass's tail and its own start-up overlaps the paged pass, with
+// the same arithmetic and partial-state slots as the two separate launches.
+template <int D, int G, bool APP, bool NT>
+__global__ __launch_bounds__(512) void paged_prefix_kernel(Args a, FlatLaunch fl, int paged_blocks, int psplits,
+                                                           int pmtiles) {
+    extern __shared__ __attribute__((aligned(1024))) char pp_smem[];
+    const int bid = blockIdx.x;
+    if (bid < paged_blocks) {
+        const int wave = threadIdx.x >> 6;
+        if (wave >= kFlatWavesMax) return;
+        flat_block<true, D, G, APP, NT>(a, fl, bid % fl.blocks, bid / fl.blocks, wave, threadIdx.x & 63, pp_smem);
+        return;
+    }
+    const int r = bid - paged_blocks;
+    const int s = r % psplits, mt = (r / psplits) % pmtiles, gz = r / (psplits * pmtiles);
+    prefix_block<D, 4, false, 2>(a, s, mt, gz, pp_smem,
+                                 (int32_t(*)[kMemberWin])(pp_smem + prefix_ring_bytes<D, 2>()));
 }
 
 // ---------------------------------------------------------------------------
@@ -1841,6 +1885,53 @@ spkv_status launch_prefix(const Args &a, const Plan &p, int d, bool bf16, hipStr
     return check_launch("prefix_mfma_kernel");
 }
 
+// LDS of one paged_prefix_kernel block: the larger of the paged pass's four
+// rings and the prefix block's two rings plus its member windows.
+constexpr size_t paged_prefix_lds() {
+    constexpr size_t paged = (size_t)kFlatWavesMax * FlatMfmaGeom<128>::WAVEB;
+    constexpr size_t prefix = (size_t)prefix_ring_bytes<128, 2>() + 8 * kMemberWin * sizeof(int32_t);
+    return paged > prefix ? paged : prefix;
+}
+static_assert(paged_prefix_lds() <= (size_t)spkv::kLdsPerCU, "one paged_prefix_kernel block per CU");
+static_assert(2 * paged_prefix_lds() > (size_t)spkv::kLdsPerCU, "the paged plan assumes one block per CU");
+
+template <int G, bool APP, bool NT>
+spkv_status launch_paged_prefix_k(const Args &a, const Plan &p, TimedLaunch &tl) {
+    constexpr int D = 128;
+    static const hipError_t attr = hipFuncSetAttribute((const void *)paged_prefix_kernel<D, G, APP, NT>,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, spkv::kLdsPerCU);
+    if (attr != hipSuccess) return fail(SPKV_E_HIP, std::string("paged_prefix_kernel LDS limit: ") + hipGetErrorString(attr));
+    const FlatLaunch &f = p.flat[0];
+    const int64_t paged = (int64_t)f.blocks * p.flat_head_groups;
+    const int64_t prefix = (int64_t)p.prefix_splits * p.prefix_mtiles * a.ng * a.Hkv;
+    if (paged + prefix >= ((int64_t)1 << 31)) return fail(SPKV_E_INVAL, "paged_prefix_kernel: grid too large");
+    dim3 grid((unsigned)(paged + prefix)), block(512);
+    tl.launch(paged_prefix_kernel<D, G, APP, NT>, grid, block, paged_prefix_lds(), a, f, (int)paged,
+              p.prefix_splits, p.prefix_mtiles);
+    return check_launch("paged_prefix_kernel");
+}
+
+template <int G>
+spkv_status launch_paged_prefix_g(const Args &a, const Plan &p, bool app, TimedLaunch &tl) {
+    if (app) return a.cold_nt ? launch_paged_prefix_k<G, true, true>(a, p, tl) : launch_paged_prefix_k<G, true, false>(a, p, tl);
+    return a.cold_nt ? launch_paged_prefix_k<G, false, true>(a, p, tl) : launch_paged_prefix_k<G, false, false>(a, p, tl);
+}
+
+spkv_status launch_paged_prefix(const Args &a, const Plan &p, bool app, hipStream_t st) {
+    TimedLaunch tl(SPKV_KERNEL_PAGED_PREFIX, st);
+    switch (a.G) {
+    case 1: return launch_paged_prefix_g<1>(a, p, app, tl);
+    case 2: return launch_paged_prefix_g<2>(a, p, app, tl);
+    case 3: return launch_paged_prefix_g<3>(a, p, app, tl);
+    case 4: return launch_paged_prefix_g<4>(a, p, app, tl);
+    case 5: return launch_paged_prefix_g<5>(a, p, app, tl);
+    case 6: return launch_paged_prefix_g<6>(a, p, app, tl);
+    case 7: return launch_paged_prefix_g<7>(a, p, app, tl);
+    case 8: return launch_paged_prefix_g<8>(a, p, app, tl);
+    default: return fail(SPKV_E_INVAL, "unsupported GQA group size");
+    }
+}
+
 spkv_status launch_merge(const Args &a, int d, float *out, float *lse, const FlatLaunch &fr,
                          const int32_t *append_slots, const uint8_t *prefix_np, hipStream_t st) {
     const int64_t rows = (int64_t)fr.nreq * a.Hq;
@@ -1910,8 +2001,11 @@ struct AppendIn {
     const int32_t *slots;   // host [B]
 };
 
+// single_launch: run the paged pass and the prefix contraction as one
+// paged_prefix_kernel launch when the plan allows it (same results).
 spkv_status run_decode(const spkv_batch *b, const spkv_kv *kv, const int32_t *cascade, float *out, float *lse,
-                       void *ws, size_t ws_bytes, void *stream, const AppendIn *app = nullptr) {
+                       void *ws, size_t ws_bytes, void *stream, const AppendIn *app = nullptr,
+                       bool single_launch = true) {
     spkv_status st = spkv::validate_batch(b, kv);
     if (st != SPKV_OK) return st;
     if (!kv) return fail(SPKV_E_INVAL, "null kv");
@@ -1947,14 +2041,19 @@ spkv_status run_decode(const spkv_batch *b, const spkv_kv *kv, const int32_t *ca
     // last-level cache when the merge reads them, and their write-back does
     // not compete with the paged pass's reads.  Sub-batch i is entry i of
     // both paged passes.
-    for (size_t i = 0; i < p.flat.size(); ++i) {
-        st = launch_flat(a, bf16, b->head_dim, p.flat[i], p.flat_head_groups, app ? app->slots : nullptr,
-                         hs);
+    if (p.single_launch && single_launch) {
+        st = launch_paged_prefix(a, p, app != nullptr, hs);
         if (st != SPKV_OK) return st;
-    }
-    if (p.run_prefix) {
-        st = launch_prefix(a, p, b->head_dim, bf16, hs);
-        if (st != SPKV_OK) return st;
+    } else {
+        for (size_t i = 0; i < p.flat.size(); ++i) {
+            st = launch_flat(a, bf16, b->head_dim, p.flat[i], p.flat_head_groups, app ? app->slots : nullptr,
+                             hs);
+            if (st != SPKV_OK) return st;
+        }
+        if (p.run_prefix) {
+            st = launch_prefix(a, p, b->head_dim, bf16, hs);
+            if (st != SPKV_OK) return st;
+        }
     }
     // Prefix partials per request (MFMA prefix pass): the split rule of the
     // prefix kernel applied to the host copies (validated by the plan).
@@ -2157,7 +2256,8 @@ spkv_status spkv_decode_step(const spkv_batch *batch, const spkv_kv *kv, const s
     if (st != SPKV_OK) return st;
     if (cascade_out)
         for (int g = 0; g < batch->num_groups; ++g) cascade_out[g] = choice[(size_t)g];
-    return run_decode(batch, kv, choice.data(), out, lse, ws, ws_bytes, stream);
+    return run_decode(batch, kv, choice.data(), out, lse, ws, ws_bytes, stream, nullptr,
+                      !params || params->single_launch != 0);
 }
 
 spkv_status spkv_decode_step_append(const spkv_batch *batch, const spkv_kv *kv, const spkv_dispatch_params *params,
@@ -2187,7 +2287,8 @@ spkv_status spkv_decode_step_append(const spkv_batch *batch, const spkv_kv *kv, 
     if (cascade_out)
         for (int g = 0; g < batch->num_groups; ++g) cascade_out[g] = choice[(size_t)g];
     const AppendIn app{k_new, v_new, host_slots};
-    return run_decode(batch, kv, choice.data(), out, lse, ws, ws_bytes, stream, &app);
+    return run_decode(batch, kv, choice.data(), out, lse, ws, ws_bytes, stream, &app,
+                      !params || params->single_launch != 0);
 }
 
 spkv_status spkv_decode_step_append_noalloc(const spkv_batch *batch, const spkv_kv *kv,

@@ -225,6 +225,12 @@ spkv_status make_plan(const spkv_batch *b, const int32_t *cascade, int32_t num_c
         p->prefix_splits = std::min<int32_t>(kPrefixSplitCap, splits_for(max_lp_c, p->prefix_chunk));
     }
     p->splits_total = p->prefix_splits + p->flat_splits;
+    // One launch for both passes (paged_prefix_kernel) where its blocks keep
+    // the shapes the two plans assume: one paged sub-batch whose blocks of 4
+    // KV-head waves fill a CU's LDS at d = 128 (one per CU, as the paged plan
+    // counts them), and prefix tiles of 4 row waves with two key halves.
+    p->single_launch = bf16 && D == 128 && p->flat.size() == 1 && p->flat[0].blocks > 0 && Hkv >= kFlatWaves &&
+                       p->run_prefix && p->prefix_waves == 4 && p->prefix_key_halves == 2 && !p->prefix_split_p;
 
     // Item counts (informational).
     p->flat_items = 0;
@@ -293,6 +299,7 @@ spkv_status spkv_plan_query(const spkv_batch *batch, const int32_t *cascade, spk
     out->prefix_split_cap = kPrefixSplitCap;
     out->prefix_granule = kPrefixKeyTile;
     out->prefix_key_halves = p.prefix_key_halves;
+    out->single_launch = p.single_launch ? 1 : 0;
     return SPKV_OK;
 }
 
@@ -344,6 +351,7 @@ void spkv_dispatch_params_default(spkv_dispatch_params *p) {
     p->prefix_gbps = 4000.0;
     p->prefix_tflops = 420.0;
     p->row_cost_ns = 3.9;
+    p->single_launch = 1;
 }
 
 spkv_status spkv_dispatch(const spkv_batch *b, const spkv_dispatch_params *prm, int32_t *cascade_out) {

@@ -346,3 +346,59 @@ def test_cold_fallback_matches_admitted_prefix(P):
         e_o, e_l, rel = errors(out, lse, ref_o, ref_l)
         note(f"    {mode}: max_abs={e_o:.2e} lse={e_l:.2e} rel={rel:.2e}")
         assert e_o <= TOL_O and e_l <= TOL_LSE and rel <= TOL_REL
+
+
+def _single_launch_cases():
+    rng = np.random.default_rng(64)
+    return {
+        "one_group_8_heads": lambda: CASES["bf16_many_tiles"](),
+        "two_groups_4_heads": lambda: W.make_custom(
+            batch=70, num_q_heads=16, num_kv_heads=4, head_dim=128, dtype="bf16", group_prefix_len=[700, 2000],
+            group_of=[0] * 30 + [1] * 36 + [-1] * 4, suffix_len=[int(x) for x in rng.integers(1, 300, 70)],
+            seed=63),
+    }
+
+
+SINGLE = _single_launch_cases()
+
+
+@pytest.mark.parametrize("name", sorted(SINGLE))
+def test_single_launch_matches_two_launches(name):
+    # paged_prefix_kernel runs the paged pass's ranges and the prefix blocks
+    # of the same plan in one launch: outputs bit-identical to the two
+    # launches, for the decode step and for the step with fused appends (pools,
+    # block tables and lengths too), and both within the bound of the oracle.
+    note(f"[gpu] single launch {name}")
+    wl = SINGLE[name]()
+    ref_o, ref_l = decode_reference(wl)
+    states = [setup_single_step(wl, max_blocks=int(wl.suffix_len.max()) + 4) for _ in range(2)]
+    assert int(states[0].batch.plan().single_launch) == 1
+    res = []
+    for one, st in zip((1, 0), states):
+        params = R.default_params(A.SPKV_MODE_FORCE_CASCADE)
+        params.single_launch = one
+        ws = R.workspace(st.batch)
+        with R.KernelTimer() as kt:
+            out, lse, _ = R.decode_step(st.batch, st.pools, params, ws)
+            torch.cuda.synchronize()
+            n_single, n_paged = kt.read(A.SPKV_KERNEL_PAGED_PREFIX)[1], kt.read(A.SPKV_KERNEL_FLAT)[1]
+        assert (n_single, n_paged) == ((1, 0) if one else (0, 1))
+        e_o, e_l, rel = errors(out, lse, ref_o, ref_l)
+        note(f"    single_launch={one}: max_abs={e_o:.2e} lse={e_l:.2e} rel={rel:.2e}")
+        assert e_o <= TOL_O and e_l <= TOL_LSE and rel <= TOL_REL
+        # one more step with the appends fused in, from identical states
+        dr = W.step_draws(wl.cfg, 1, wl.batch)
+        k, v, q = (to_device(x, wl.cfg.dtype, "cuda") for x in (dr.k_new, dr.v_new, dr.q))
+        slots, cows = st.cold.append_batch(np.asarray(st.seqs, np.int32))
+        assert not cows
+        st.batch.lens_h += 1
+        st.batch.struct.q = q.data_ptr()
+        out2, lse2, _ = R.decode_step_append(st.batch, st.pools, params, R.workspace(st.batch), k, v, slots)
+        torch.cuda.synchronize()
+        res.append((out, lse, out2, lse2))
+    for x, y in zip(*res):
+        assert torch.equal(x, y)
+    a, b = states
+    for t0, t1 in ((a.pools.k_cold, b.pools.k_cold), (a.pools.v_cold, b.pools.v_cold)):
+        np.testing.assert_array_equal(pool_bytes(t0), pool_bytes(t1))
+    assert torch.equal(a.batch.tables, b.batch.tables) and torch.equal(a.batch.lens, b.batch.lens)

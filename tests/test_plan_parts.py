@@ -125,3 +125,30 @@ def test_prefix_blocks_fit_one_resident_round(shape):
     # and the chunk does not grow past what one round needs
     units = sum(hkv * -(-(groups.count(g) * (hq // hkv)) // (32 * info.prefix_waves)) for g in range(ng))
     assert info.prefix_items >= min(resident, units) // 2
+
+
+def test_single_launch_only_where_both_plans_keep_their_shapes():
+    # The paged pass and the prefix contraction share one launch only where a
+    # paged block (4 KV-head waves, d = 128) and a prefix block (4 row waves,
+    # two key halves) each fill a CU: one paged sub-batch, bf16, Hkv >= 4, a
+    # group with more than 64 query rows and a prefix of at least 256 keys.
+    def single(lens, groups, group_len, cascade=None, **kw):
+        return int(batch_of(lens, groups, group_len, **kw).plan(cascade).single_launch)
+
+    lens = [300] * 64
+    assert single(lens, [0] * 64, [16384]) == 1                       # 8B shape, Lp 16K
+    assert single(lens, [0] * 64, [16384], cascade=[0]) == 0          # no prefix contraction
+    assert single(lens, [0] * 64, [16384], hkv=2, hq=8) == 0          # 2 KV heads: blocks of 2 waves
+    assert single(lens, [0] * 64, [16384], d=64) == 0                 # d = 64: two paged blocks per CU
+    assert single(lens, [0] * 64, [200]) == 0                         # short prefix: P as hi + lo
+    assert single(lens[:16], [0] * 16, [16384]) == 0                  # 64 query rows: tiles of 2 waves
+    assert single(lens[:20], [0] * 20, [16384]) == 1                  # 80 query rows: tiles of 4 waves
+    assert single([30] * 300, [0] * 300, [16384]) == 0                # two paged sub-batches
+    q32 = torch.zeros((64, 32, 128), dtype=torch.float32)
+    tables = np.full((64, 300), -1, np.int32)
+    assert int(R.DecodeBatch(q32, [0] * 64, [0], [16384], tables, lens, 1, 8).plan().single_launch) == 0
+
+
+def test_two_launches_by_parameter():
+    p = R.default_params()
+    assert p.single_launch == 1
