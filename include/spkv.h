@@ -438,9 +438,10 @@ typedef struct spkv_plan_info {
     int32_t prefix_key_halves;     /* 2: each prefix work item's key chunk is split over two wave sets whose
                                       states merge in LDS (one partial per row per item either way) */
     int32_t single_launch;         /* 1: the paged pass's ranges and the prefix blocks can run as one launch
-                                      (bf16, head_dim 128, Hkv >= 4, one paged sub-batch of <= 256 requests,
-                                      prefix tiles of 4 row waves with two key halves); the paged ranges come
-                                      first in the grid and the prefix blocks take CUs as ranges finish */
+                                      (bf16, head_dim 128, Hkv of 1, 2 or >= 4, one paged sub-batch of
+                                      <= 256 requests, prefix tiles of 4 row waves with two key halves); the
+                                      paged ranges come first in the grid and the prefix blocks take CUs as
+                                      ranges finish */
 } spkv_plan_info;
 
 spkv_status spkv_plan_query(const spkv_batch *batch, const int32_t *cascade, spkv_plan_info *out);

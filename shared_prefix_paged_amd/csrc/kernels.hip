@@ -1280,6 +1280,9 @@ __global__ __launch_bounds__(64 * W * KH) void prefix_mfma_kernel(Args a) {
 // and prefix blocks take CUs as paged ranges finish: the prefix work fills
 // the paged pass's tail and its own start-up overlaps the paged pass, with
 // the same arithmetic and partial-state slots as the two separate launches.
+// With fewer than 4 KV heads a paged block has hpb = 1 or 2 waves, and waves
+// 0..3 of one launch block run 4 / hpb paged blocks side by side, each on its
+// own rings: as many per CU as the paged plan counts.
 template <int D, int G, bool APP, bool NT>
 __global__ __launch_bounds__(512) void paged_prefix_kernel(Args a, FlatLaunch fl, int paged_blocks, int psplits,
                                                            int pmtiles) {
@@ -1288,7 +1291,14 @@ __global__ __launch_bounds__(512) void paged_prefix_kernel(Args a, FlatLaunch fl
     if (bid < paged_blocks) {
         const int wave = threadIdx.x >> 6;
         if (wave >= kFlatWavesMax) return;
-        flat_block<true, D, G, APP, NT>(a, fl, bid % fl.blocks, bid / fl.blocks, wave, threadIdx.x & 63, pp_smem);
+        const int hpb = a.Hkv < kFlatWavesMax ? a.Hkv : kFlatWavesMax;   // 1, 2 or 4 (checked by the plan)
+        const int per = kFlatWavesMax / hpb;                           // paged blocks per launch block
+        const int pb = bid * per + wave / hpb;
+        const int head_groups = (a.Hkv + hpb - 1) / hpb;
+        if (pb >= fl.blocks * head_groups) return;
+        const int sub = wave / hpb;
+        flat_block<true, D, G, APP, NT>(a, fl, pb % fl.blocks, pb / fl.blocks, wave - sub * hpb, threadIdx.x & 63,
+                                        pp_smem + sub * hpb * FlatMfmaGeom<D>::WAVEB);
         return;
     }
     const int r = bid - paged_blocks;
@@ -1893,7 +1903,7 @@ constexpr size_t paged_prefix_lds() {
     return paged > prefix ? paged : prefix;
 }
 static_assert(paged_prefix_lds() <= (size_t)spkv::kLdsPerCU, "one paged_prefix_kernel block per CU");
-static_assert(2 * paged_prefix_lds() > (size_t)spkv::kLdsPerCU, "the paged plan assumes one block per CU");
+static_assert(2 * paged_prefix_lds() > (size_t)spkv::kLdsPerCU, "one launch block per CU, as the plan counts");
 
 template <int G, bool APP, bool NT>
 spkv_status launch_paged_prefix_k(const Args &a, const Plan &p, TimedLaunch &tl) {
@@ -1902,7 +1912,9 @@ spkv_status launch_paged_prefix_k(const Args &a, const Plan &p, TimedLaunch &tl)
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, spkv::kLdsPerCU);
     if (attr != hipSuccess) return fail(SPKV_E_HIP, std::string("paged_prefix_kernel LDS limit: ") + hipGetErrorString(attr));
     const FlatLaunch &f = p.flat[0];
-    const int64_t paged = (int64_t)f.blocks * p.flat_head_groups;
+    const int hpb = a.Hkv < kFlatWavesMax ? a.Hkv : kFlatWavesMax;
+    const int per = kFlatWavesMax / hpb;
+    const int64_t paged = ((int64_t)f.blocks * p.flat_head_groups + per - 1) / per;
     const int64_t prefix = (int64_t)p.prefix_splits * p.prefix_mtiles * a.ng * a.Hkv;
     if (paged + prefix >= ((int64_t)1 << 31)) return fail(SPKV_E_INVAL, "paged_prefix_kernel: grid too large");
     dim3 grid((unsigned)(paged + prefix)), block(512);

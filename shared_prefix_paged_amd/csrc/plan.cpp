@@ -226,11 +226,13 @@ spkv_status make_plan(const spkv_batch *b, const int32_t *cascade, int32_t num_c
     }
     p->splits_total = p->prefix_splits + p->flat_splits;
     // One launch for both passes (paged_prefix_kernel) where its blocks keep
-    // the shapes the two plans assume: one paged sub-batch whose blocks of 4
-    // KV-head waves fill a CU's LDS at d = 128 (one per CU, as the paged plan
-    // counts them), and prefix tiles of 4 row waves with two key halves.
-    p->single_launch = bf16 && D == 128 && p->flat.size() == 1 && p->flat[0].blocks > 0 && Hkv >= kFlatWaves &&
-                       p->run_prefix && p->prefix_waves == 4 && p->prefix_key_halves == 2 && !p->prefix_split_p;
+    // the shapes the two plans assume: one paged sub-batch at d = 128 whose
+    // blocks of hpb KV-head waves (hpb = 1, 2 or 4) fill a CU's LDS 4 / hpb
+    // at a time, as the paged plan counts them, and prefix tiles of 4 row
+    // waves with two key halves (one per CU).
+    p->single_launch = bf16 && D == 128 && p->flat.size() == 1 && p->flat[0].blocks > 0 && kFlatWaves % hpb == 0 &&
+                       flat_blocks_per_cu(bf16, D, hpb) == kFlatWaves / hpb && p->run_prefix &&
+                       p->prefix_waves == 4 && p->prefix_key_halves == 2 && !p->prefix_split_p;
 
     // Item counts (informational).
     p->flat_items = 0;

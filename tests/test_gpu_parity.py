@@ -356,6 +356,13 @@ def _single_launch_cases():
             batch=70, num_q_heads=16, num_kv_heads=4, head_dim=128, dtype="bf16", group_prefix_len=[700, 2000],
             group_of=[0] * 30 + [1] * 36 + [-1] * 4, suffix_len=[int(x) for x in rng.integers(1, 300, 70)],
             seed=63),
+        # fewer than 4 KV heads: 2 or 4 paged blocks side by side in one launch block
+        "one_group_2_heads": lambda: W.make_custom(
+            batch=61, num_q_heads=10, num_kv_heads=2, head_dim=128, dtype="bf16", group_prefix_len=[1500],
+            group_of=[0] * 60 + [-1], suffix_len=[int(x) for x in rng.integers(1, 400, 61)], seed=65),
+        "one_group_1_head": lambda: W.make_custom(
+            batch=41, num_q_heads=4, num_kv_heads=1, head_dim=128, dtype="bf16", group_prefix_len=[900],
+            group_of=[0] * 40 + [-1], suffix_len=[int(x) for x in rng.integers(1, 500, 41)], seed=66),
     }
 
 

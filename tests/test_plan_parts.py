@@ -130,15 +130,18 @@ def test_prefix_blocks_fit_one_resident_round(shape):
 def test_single_launch_only_where_both_plans_keep_their_shapes():
     # The paged pass and the prefix contraction share one launch only where a
     # paged block (4 KV-head waves, d = 128) and a prefix block (4 row waves,
-    # two key halves) each fill a CU: one paged sub-batch, bf16, Hkv >= 4, a
-    # group with more than 64 query rows and a prefix of at least 256 keys.
+    # two key halves) fill a CU as the two plans count them: one paged
+    # sub-batch, bf16, Hkv of 1, 2 or >= 4, a group with more than 64 query
+    # rows and a prefix of at least 256 keys.
     def single(lens, groups, group_len, cascade=None, **kw):
         return int(batch_of(lens, groups, group_len, **kw).plan(cascade).single_launch)
 
     lens = [300] * 64
     assert single(lens, [0] * 64, [16384]) == 1                       # 8B shape, Lp 16K
     assert single(lens, [0] * 64, [16384], cascade=[0]) == 0          # no prefix contraction
-    assert single(lens, [0] * 64, [16384], hkv=2, hq=8) == 0          # 2 KV heads: blocks of 2 waves
+    assert single(lens, [0] * 64, [16384], hkv=2, hq=8) == 1          # 2 KV heads: two paged blocks side by side
+    assert single(lens, [0] * 64, [16384], hkv=1, hq=4) == 1          # 1 KV head: four
+    assert single(lens, [0] * 64, [16384], hkv=3, hq=12) == 0         # 3 KV heads: blocks of 3 waves
     assert single(lens, [0] * 64, [16384], d=64) == 0                 # d = 64: two paged blocks per CU
     assert single(lens, [0] * 64, [200]) == 0                         # short prefix: P as hi + lo
     assert single(lens[:16], [0] * 16, [16384]) == 0                  # 64 query rows: tiles of 2 waves
