@@ -341,14 +341,16 @@ void spkv_dispatch_params_default(spkv_dispatch_params *p) {
     // Hkv 8) and 32B-shaped (Hq 10, Hkv 2) layers: prefix length 64 .. 32768
     // at 64 and 256 requests, and 1 .. 256 requests sharing a 4096- or
     // 16384-token prefix.  The flat pass re-reads a shared prefix at ~10 TB/s
-    // (the re-reads are mostly cache hits); the cascade path costs ~7.4 us per
-    // step (the prefix launch) plus ~3.9 ns per query row of the groups that
-    // take it (their partial states, written and merged).  The prefix
-    // contraction's own rates matter little near the crossover; they are
-    // those of the kernel at the 8B shape.
+    // (the re-reads are mostly cache hits); the cascade path costs ~3.2 us per
+    // step (the prefix blocks' start-up; they share the paged pass's launch
+    // where the plan allows it) plus ~3.9 ns per query row of the groups that
+    // take it (their partial states, written and merged).  Any fixed cost in
+    // [2.5, 4.0] us picks the faster backend at all 52 swept points.  The
+    // prefix contraction's own rates matter little near the crossover; they
+    // are those of the kernel at the 8B shape.
     p->mode = SPKV_MODE_PER_GROUP;
     p->min_group_requests = 2;
-    p->fixed_cost_us = 7.4;
+    p->fixed_cost_us = 3.2;
     p->flat_gbps = 10000.0;
     p->prefix_gbps = 4000.0;
     p->prefix_tflops = 420.0;
