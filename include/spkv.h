@@ -439,7 +439,8 @@ typedef struct spkv_plan_info {
                                       states merge in LDS (one partial per row per item either way) */
     int32_t single_launch;         /* 1: the paged pass's ranges and the prefix blocks can run as one launch
                                       (bf16, head_dim 128, Hkv of 1, 2 or >= 4, one paged sub-batch of
-                                      <= 256 requests, prefix tiles of 4 row waves with two key halves); the
+                                      <= 256 requests, prefix tiles of 2 or 4 row waves with two key halves
+                                      (groups of more than 32 query rows per KV head)); the
                                       paged ranges come first in the grid and the prefix blocks take CUs as
                                       ranges finish */
 } spkv_plan_info;

@@ -1272,9 +1272,9 @@ __global__ __launch_bounds__(64 * W * KH) void prefix_mfma_kernel(Args a) {
 }
 
 // The paged pass and the prefix contraction in one launch (bf16, d = 128,
-// prefix tiles of 4 row waves and two key halves): blocks [0, paged_blocks)
-// are the paged pass's ranges (waves 0..3 of a block; the other four leave at
-// once), the rest are prefix blocks (all 8 waves).  Either role fills a CU's
+// prefix tiles of 2 or 4 row waves and two key halves): blocks
+// [0, paged_blocks) are the paged pass's ranges (waves 0..3 of a block; the
+// other four leave at once), the rest are prefix blocks (2 * PW waves).  Either role fills a CU's
 // LDS, so one block runs per CU; blocks are handed out in index order, so
 // every paged range starts at once (the split plan is one resident round)
 // and prefix blocks take CUs as paged ranges finish: the prefix work fills
@@ -1283,7 +1283,9 @@ __global__ __launch_bounds__(64 * W * KH) void prefix_mfma_kernel(Args a) {
 // With fewer than 4 KV heads a paged block has hpb = 1 or 2 waves, and waves
 // 0..3 of one launch block run 4 / hpb paged blocks side by side, each on its
 // own rings: as many per CU as the paged plan counts.
-template <int D, int G, bool APP, bool NT>
+// PW: row waves of the prefix tiles (4: all 8 waves of the block; 2: waves
+// 0..3, the other four leave at once and are not waited for at barriers).
+template <int D, int G, bool APP, bool NT, int PW>
 __global__ __launch_bounds__(512) void paged_prefix_kernel(Args a, FlatLaunch fl, int paged_blocks, int psplits,
                                                            int pmtiles) {
     extern __shared__ __attribute__((aligned(1024))) char pp_smem[];
@@ -1301,10 +1303,11 @@ __global__ __launch_bounds__(512) void paged_prefix_kernel(Args a, FlatLaunch fl
                                         pp_smem + sub * hpb * FlatMfmaGeom<D>::WAVEB);
         return;
     }
+    if ((int)(threadIdx.x >> 6) >= 2 * PW) return;
     const int r = bid - paged_blocks;
     const int s = r % psplits, mt = (r / psplits) % pmtiles, gz = r / (psplits * pmtiles);
-    prefix_block<D, 4, false, 2>(a, s, mt, gz, pp_smem,
-                                 (int32_t(*)[kMemberWin])(pp_smem + prefix_ring_bytes<D, 2>()));
+    prefix_block<D, PW, false, 2>(a, s, mt, gz, pp_smem,
+                                  (int32_t(*)[kMemberWin])(pp_smem + prefix_ring_bytes<D, 2>()));
 }
 
 // ---------------------------------------------------------------------------
@@ -1875,6 +1878,10 @@ spkv_status launch_prefix(const Args &a, const Plan &p, int d, bool bf16, hipStr
     const int key = p.prefix_waves * 1000 + d + (p.prefix_split_p ? 10000 : 0) + (p.prefix_key_halves == 2 ? 100000 : 0);
     switch (key) {
     case 104128: tl.launch(prefix_mfma_kernel<128, 4, false, 2>, grid, block, 0, a); break;
+    case 102128: tl.launch(prefix_mfma_kernel<128, 2, false, 2>, grid, block, 0, a); break;
+    case 102064: tl.launch(prefix_mfma_kernel<64, 2, false, 2>, grid, block, 0, a); break;
+    case 112128: tl.launch(prefix_mfma_kernel<128, 2, true, 2>, grid, block, 0, a); break;
+    case 112064: tl.launch(prefix_mfma_kernel<64, 2, true, 2>, grid, block, 0, a); break;
     case 104064: tl.launch(prefix_mfma_kernel<64, 4, false, 2>, grid, block, 0, a); break;
     case 114128: tl.launch(prefix_mfma_kernel<128, 4, true, 2>, grid, block, 0, a); break;
     case 114064: tl.launch(prefix_mfma_kernel<64, 4, true, 2>, grid, block, 0, a); break;
@@ -1905,10 +1912,10 @@ constexpr size_t paged_prefix_lds() {
 static_assert(paged_prefix_lds() <= (size_t)spkv::kLdsPerCU, "one paged_prefix_kernel block per CU");
 static_assert(2 * paged_prefix_lds() > (size_t)spkv::kLdsPerCU, "one launch block per CU, as the plan counts");
 
-template <int G, bool APP, bool NT>
+template <int G, bool APP, bool NT, int PW>
 spkv_status launch_paged_prefix_k(const Args &a, const Plan &p, TimedLaunch &tl) {
     constexpr int D = 128;
-    static const hipError_t attr = hipFuncSetAttribute((const void *)paged_prefix_kernel<D, G, APP, NT>,
+    static const hipError_t attr = hipFuncSetAttribute((const void *)paged_prefix_kernel<D, G, APP, NT, PW>,
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, spkv::kLdsPerCU);
     if (attr != hipSuccess) return fail(SPKV_E_HIP, std::string("paged_prefix_kernel LDS limit: ") + hipGetErrorString(attr));
     const FlatLaunch &f = p.flat[0];
@@ -1918,15 +1925,22 @@ spkv_status launch_paged_prefix_k(const Args &a, const Plan &p, TimedLaunch &tl)
     const int64_t prefix = (int64_t)p.prefix_splits * p.prefix_mtiles * a.ng * a.Hkv;
     if (paged + prefix >= ((int64_t)1 << 31)) return fail(SPKV_E_INVAL, "paged_prefix_kernel: grid too large");
     dim3 grid((unsigned)(paged + prefix)), block(512);
-    tl.launch(paged_prefix_kernel<D, G, APP, NT>, grid, block, paged_prefix_lds(), a, f, (int)paged,
+    tl.launch(paged_prefix_kernel<D, G, APP, NT, PW>, grid, block, paged_prefix_lds(), a, f, (int)paged,
               p.prefix_splits, p.prefix_mtiles);
     return check_launch("paged_prefix_kernel");
 }
 
+template <int G, int PW>
+spkv_status launch_paged_prefix_w(const Args &a, const Plan &p, bool app, TimedLaunch &tl) {
+    if (app) return a.cold_nt ? launch_paged_prefix_k<G, true, true, PW>(a, p, tl)
+                              : launch_paged_prefix_k<G, true, false, PW>(a, p, tl);
+    return a.cold_nt ? launch_paged_prefix_k<G, false, true, PW>(a, p, tl)
+                     : launch_paged_prefix_k<G, false, false, PW>(a, p, tl);
+}
+
 template <int G>
 spkv_status launch_paged_prefix_g(const Args &a, const Plan &p, bool app, TimedLaunch &tl) {
-    if (app) return a.cold_nt ? launch_paged_prefix_k<G, true, true>(a, p, tl) : launch_paged_prefix_k<G, true, false>(a, p, tl);
-    return a.cold_nt ? launch_paged_prefix_k<G, false, true>(a, p, tl) : launch_paged_prefix_k<G, false, false>(a, p, tl);
+    return p.prefix_waves == 4 ? launch_paged_prefix_w<G, 4>(a, p, app, tl) : launch_paged_prefix_w<G, 2>(a, p, app, tl);
 }
 
 spkv_status launch_paged_prefix(const Args &a, const Plan &p, bool app, hipStream_t st) {

@@ -185,10 +185,10 @@ spkv_status make_plan(const spkv_batch *b, const int32_t *cascade, int32_t num_c
     if (p->run_prefix) {
         int w = (int)std::min<int64_t>(4, (max_m + 31) / 32);
         p->prefix_waves = !bf16 ? 1 : (w <= 1 ? 1 : (w == 2 ? 2 : 4));   // bf16 tile variants: 1, 2 or 4 waves
-        // Tiles of 4 row waves take the two-key-half variant: one 8-wave block
-        // (two 64 KB rings) per CU instead of two 4-wave blocks, and half as
-        // many partial states per row.
-        p->prefix_key_halves = p->prefix_waves == 4 ? 2 : 1;
+        // Tiles of 2 or 4 row waves take the two-key-half variant: one block
+        // (two 64 KB rings) per CU instead of two blocks of one half, and half
+        // as many partial states per row.
+        p->prefix_key_halves = p->prefix_waves >= 2 ? 2 : 1;
         const int64_t mt = 32 * p->prefix_waves;
         p->prefix_mtiles = (int32_t)((max_m + mt - 1) / mt);
         for (int g = 0; g < ng; ++g) {
@@ -228,11 +228,11 @@ spkv_status make_plan(const spkv_batch *b, const int32_t *cascade, int32_t num_c
     // One launch for both passes (paged_prefix_kernel) where its blocks keep
     // the shapes the two plans assume: one paged sub-batch at d = 128 whose
     // blocks of hpb KV-head waves (hpb = 1, 2 or 4) fill a CU's LDS 4 / hpb
-    // at a time, as the paged plan counts them, and prefix tiles of 4 row
-    // waves with two key halves (one per CU).
+    // at a time, as the paged plan counts them, and prefix tiles of 2 or 4
+    // row waves with two key halves (one per CU).
     p->single_launch = bf16 && D == 128 && p->flat.size() == 1 && p->flat[0].blocks > 0 && kFlatWaves % hpb == 0 &&
                        flat_blocks_per_cu(bf16, D, hpb) == kFlatWaves / hpb && p->run_prefix &&
-                       p->prefix_waves == 4 && p->prefix_key_halves == 2 && !p->prefix_split_p;
+                       p->prefix_waves >= 2 && p->prefix_key_halves == 2 && !p->prefix_split_p;
 
     // Item counts (informational).
     p->flat_items = 0;

@@ -356,6 +356,10 @@ def _single_launch_cases():
             batch=70, num_q_heads=16, num_kv_heads=4, head_dim=128, dtype="bf16", group_prefix_len=[700, 2000],
             group_of=[0] * 30 + [1] * 36 + [-1] * 4, suffix_len=[int(x) for x in rng.integers(1, 300, 70)],
             seed=63),
+        # groups of 33..64 query rows per KV head: prefix tiles of 2 row waves (4 of the 8 waves)
+        "two_groups_2_wave_tiles": lambda: W.make_custom(
+            batch=33, num_q_heads=32, num_kv_heads=8, head_dim=128, dtype="bf16", group_prefix_len=[3000, 5000],
+            group_of=[0] * 16 + [1] * 16 + [-1], suffix_len=[int(x) for x in rng.integers(1, 600, 33)], seed=67),
         # fewer than 4 KV heads: 2 or 4 paged blocks side by side in one launch block
         "one_group_2_heads": lambda: W.make_custom(
             batch=61, num_q_heads=10, num_kv_heads=2, head_dim=128, dtype="bf16", group_prefix_len=[1500],

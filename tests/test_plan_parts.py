@@ -131,7 +131,7 @@ def test_single_launch_only_where_both_plans_keep_their_shapes():
     # The paged pass and the prefix contraction share one launch only where a
     # paged block (4 KV-head waves, d = 128) and a prefix block (4 row waves,
     # two key halves) fill a CU as the two plans count them: one paged
-    # sub-batch, bf16, Hkv of 1, 2 or >= 4, a group with more than 64 query
+    # sub-batch, bf16, Hkv of 1, 2 or >= 4, a group with more than 32 query
     # rows and a prefix of at least 256 keys.
     def single(lens, groups, group_len, cascade=None, **kw):
         return int(batch_of(lens, groups, group_len, **kw).plan(cascade).single_launch)
@@ -144,7 +144,8 @@ def test_single_launch_only_where_both_plans_keep_their_shapes():
     assert single(lens, [0] * 64, [16384], hkv=3, hq=12) == 0         # 3 KV heads: blocks of 3 waves
     assert single(lens, [0] * 64, [16384], d=64) == 0                 # d = 64: two paged blocks per CU
     assert single(lens, [0] * 64, [200]) == 0                         # short prefix: P as hi + lo
-    assert single(lens[:16], [0] * 16, [16384]) == 0                  # 64 query rows: tiles of 2 waves
+    assert single(lens[:8], [0] * 8, [16384]) == 0                    # 32 query rows: tiles of 1 wave
+    assert single(lens[:16], [0] * 16, [16384]) == 1                  # 64 query rows: tiles of 2 waves
     assert single(lens[:20], [0] * 20, [16384]) == 1                  # 80 query rows: tiles of 4 waves
     assert single([30] * 300, [0] * 300, [16384]) == 0                # two paged sub-batches
     q32 = torch.zeros((64, 32, 128), dtype=torch.float32)
