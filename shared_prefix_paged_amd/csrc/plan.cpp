@@ -177,6 +177,13 @@ spkv_status make_plan(const spkv_batch *b, const int32_t *cascade, int32_t num_c
         p->flat_splits = std::max(p->flat_splits, f.max_parts);
         if (f.blocks > 0) p->flat_chunk = std::max<int32_t>(p->flat_chunk, (int32_t)(f.total / f.blocks));
     }
+    // Whether the paged pass's blocks fit one launch with prefix blocks
+    // (paged_prefix_kernel): one sub-batch at d = 128 whose blocks of hpb
+    // KV-head waves (hpb = 1, 2 or 4) fill a CU's LDS 4 / hpb at a time, as
+    // the paged plan counts them.
+    const bool paged_one_launch = bf16 && D == 128 && p->flat.size() == 1 && p->flat[0].blocks > 0 &&
+                                  kFlatWaves % hpb == 0 && flat_blocks_per_cu(bf16, D, hpb) == kFlatWaves / hpb;
+
     // ---- prefix pass ------------------------------------------------------
     // One batched contraction per cascade group and KV head in both dtypes:
     // bf16 on MFMA in row tiles of 1, 2 or 4 waves of 32 rows; float32 on the
@@ -185,10 +192,14 @@ spkv_status make_plan(const spkv_batch *b, const int32_t *cascade, int32_t num_c
     if (p->run_prefix) {
         int w = (int)std::min<int64_t>(4, (max_m + 31) / 32);
         p->prefix_waves = !bf16 ? 1 : (w <= 1 ? 1 : (w == 2 ? 2 : 4));   // bf16 tile variants: 1, 2 or 4 waves
-        // Tiles of 2 or 4 row waves take the two-key-half variant: one block
-        // (two 64 KB rings) per CU instead of two blocks of one half, and half
-        // as many partial states per row.
-        p->prefix_key_halves = p->prefix_waves >= 2 ? 2 : 1;
+        // Tiles of 4 row waves take the two-key-half variant: one 8-wave block
+        // (two 64 KB rings) per CU instead of two 4-wave blocks, and half as
+        // many partial states per row.  Tiles of 2 row waves take it only where
+        // the paged pass and the prefix contraction then share one launch: on
+        // its own that tile ran slower than two 2-wave blocks of one half
+        // (C4: 71.7 against 64 us), in the one launch the pair is faster.
+        p->prefix_key_halves =
+            p->prefix_waves == 4 || (p->prefix_waves == 2 && paged_one_launch && !p->prefix_split_p) ? 2 : 1;
         const int64_t mt = 32 * p->prefix_waves;
         p->prefix_mtiles = (int32_t)((max_m + mt - 1) / mt);
         for (int g = 0; g < ng; ++g) {
@@ -226,13 +237,10 @@ spkv_status make_plan(const spkv_batch *b, const int32_t *cascade, int32_t num_c
     }
     p->splits_total = p->prefix_splits + p->flat_splits;
     // One launch for both passes (paged_prefix_kernel) where its blocks keep
-    // the shapes the two plans assume: one paged sub-batch at d = 128 whose
-    // blocks of hpb KV-head waves (hpb = 1, 2 or 4) fill a CU's LDS 4 / hpb
-    // at a time, as the paged plan counts them, and prefix tiles of 2 or 4
-    // row waves with two key halves (one per CU).
-    p->single_launch = bf16 && D == 128 && p->flat.size() == 1 && p->flat[0].blocks > 0 && kFlatWaves % hpb == 0 &&
-                       flat_blocks_per_cu(bf16, D, hpb) == kFlatWaves / hpb && p->run_prefix &&
-                       p->prefix_waves >= 2 && p->prefix_key_halves == 2 && !p->prefix_split_p;
+    // the shapes the two plans assume: the paged blocks above, and prefix
+    // tiles of 2 or 4 row waves with two key halves (one block per CU).
+    p->single_launch = paged_one_launch && p->run_prefix && p->prefix_waves >= 2 && p->prefix_key_halves == 2 &&
+                       !p->prefix_split_p;
 
     // Item counts (informational).
     p->flat_items = 0;

@@ -85,7 +85,7 @@ def test_row_cost_counts_per_member_row():
 # the paged pass and the prefix contraction in one launch where the plan
 # allows it): which backend was faster at each swept point; the defaults must
 # pick it (they do at 51 of the 52 points of the six sweeps; the exception, 2
-# requests sharing a 16K-token prefix, is a 0.7 us tie and not listed).
+# requests sharing a 16K-token prefix, is a tie under 1 us and not listed).
 SWEPT = [
     # (Hq, Hkv, requests, Lp, cascade faster)
     (32, 8, 64, 256, 0), (32, 8, 64, 512, 1), (32, 8, 64, 1024, 1), (32, 8, 64, 16384, 1),

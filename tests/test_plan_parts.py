@@ -147,6 +147,10 @@ def test_single_launch_only_where_both_plans_keep_their_shapes():
     assert single(lens[:8], [0] * 8, [16384]) == 0                    # 32 query rows: tiles of 1 wave
     assert single(lens[:16], [0] * 16, [16384]) == 1                  # 64 query rows: tiles of 2 waves
     assert single(lens[:20], [0] * 20, [16384]) == 1                  # 80 query rows: tiles of 4 waves
+    # 2-wave tiles take two key halves only with the one launch (alone, one half per block was faster)
+    assert int(batch_of(lens[:16], [0] * 16, [16384]).plan().prefix_key_halves) == 2
+    assert int(batch_of(lens[:16], [0] * 16, [16384], d=64).plan().prefix_key_halves) == 1
+    assert int(batch_of(lens[:16], [0] * 16, [16384], hkv=3, hq=12).plan().prefix_key_halves) == 1
     assert single([30] * 300, [0] * 300, [16384]) == 0                # two paged sub-batches
     q32 = torch.zeros((64, 32, 128), dtype=torch.float32)
     tables = np.full((64, 300), -1, np.int32)
