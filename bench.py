@@ -15,8 +15,8 @@ Default workload: the Llama-3.1-8B-shaped layer (B = 64, Hq = 32, Hkv = 8,
 d = 128, bf16, Lp = 16384, Ls ~ U[256, 2048] growing by one token per step,
 COLD page size 1 with shuffled slots).
 
-Prints one JSON line.  ``--gpus N`` with N > 1 is refused: this build runs on
-one GPU.
+Prints one JSON line.  ``--gpus N`` with N > 1 is refused: the library runs the
+step on one GPU.
 """
 from __future__ import annotations
 
@@ -622,7 +622,7 @@ def main():
         return admission_sweep(args)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
-              "this build has no multi-GPU path.", file=sys.stderr)
+              "the library has no multi-GPU path.", file=sys.stderr)
         return 2
     if args.steps < 1 or args.warmup < 0:
         print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
