@@ -20,7 +20,7 @@ namespace spkv {
 spkv_status fail(spkv_status code, const std::string &msg);
 void clear_error();
 
-// Limits of this build.
+// Limits of the library.
 constexpr int kMaxGroups = 512;        // groups per step (cascade bitmask size)
 constexpr int kMaxGqa = 8;             // Hq / Hkv
 constexpr int kMaxKvHeads = 16;

@@ -353,7 +353,8 @@ void spkv_dispatch_params_default(spkv_dispatch_params *p) {
     // step (the prefix blocks' start-up; they share the paged pass's launch
     // where the plan allows it) plus ~3.9 ns per query row of the groups that
     // take it (their partial states, written and merged).  Any fixed cost in
-    // [2.5, 4.0] us picks the faster backend at all 52 swept points.  The
+    // [2.5, 4.0] us picks the faster backend at 51 of the 52 swept points (the
+    // other a tie under 1 us).  The
     // prefix contraction's own rates matter little near the crossover; they
     // are those of the kernel at the 8B shape.
     p->mode = SPKV_MODE_PER_GROUP;

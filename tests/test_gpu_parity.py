@@ -360,6 +360,13 @@ def _single_launch_cases():
         "two_groups_2_wave_tiles": lambda: W.make_custom(
             batch=33, num_q_heads=32, num_kv_heads=8, head_dim=128, dtype="bf16", group_prefix_len=[3000, 5000],
             group_of=[0] * 16 + [1] * 16 + [-1], suffix_len=[int(x) for x in rng.integers(1, 600, 33)], seed=67),
+        # KV heads beyond one group of 4: the last paged head group partly filled (6), and the most (16)
+        "one_group_6_heads": lambda: W.make_custom(
+            batch=41, num_q_heads=12, num_kv_heads=6, head_dim=128, dtype="bf16", group_prefix_len=[1200],
+            group_of=[0] * 40 + [-1], suffix_len=[int(x) for x in rng.integers(1, 300, 41)], seed=68),
+        "one_group_16_heads": lambda: W.make_custom(
+            batch=100, num_q_heads=16, num_kv_heads=16, head_dim=128, dtype="bf16", group_prefix_len=[700],
+            group_of=[0] * 100, suffix_len=[int(x) for x in rng.integers(1, 200, 100)], seed=69),
         # fewer than 4 KV heads: 2 or 4 paged blocks side by side in one launch block
         "one_group_2_heads": lambda: W.make_custom(
             batch=61, num_q_heads=10, num_kv_heads=2, head_dim=128, dtype="bf16", group_prefix_len=[1500],
