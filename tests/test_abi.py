@@ -167,3 +167,22 @@ def test_noalloc_rejects_plans_beyond_its_scratch_before_launching():
                                               C.byref(R.default_params()), fake, fake,
                                               slots.ctypes.data_as(C.POINTER(C.c_int32)), fake, fake, None, None)
     assert st == A.SPKV_E_INVAL and "static" in spkv.lib.spkv_last_error().decode()
+
+
+def test_empty_batch_is_a_no_op_without_touching_the_device():
+    # B = 0: every decode entry point validates and returns SPKV_OK before any
+    # device call (this runs on a machine without a GPU).
+    b = A.spkv_batch()
+    b.batch, b.num_q_heads, b.num_kv_heads, b.head_dim = 0, 8, 2, 128
+    b.dtype, b.scale, b.page_size, b.max_blocks = A.SPKV_DTYPE_BF16, 0.088, 1, 0
+    kv = A.spkv_kv()
+    kv.num_layers, kv.layer = 1, 0
+    from shared_prefix_paged_amd import runtime as R
+    params = R.default_params()
+    assert spkv.spkv_cascade_decode(C.byref(b), C.byref(kv), None, None, None, 0, None) == A.SPKV_OK
+    assert spkv.spkv_dense_decode(C.byref(b), C.byref(kv), None, None, None, 0, None) == A.SPKV_OK
+    assert spkv.spkv_decode_step(C.byref(b), C.byref(kv), C.byref(params), None, None, None, 0, None, None) == A.SPKV_OK
+    assert spkv.spkv_workspace_size(C.byref(b)) > 0
+    info = A.spkv_plan_info()
+    assert spkv.spkv_plan_query(C.byref(b), None, C.byref(info)) == A.SPKV_OK
+    assert info.single_launch == 0 and info.flat_items == 0 and info.prefix_items == 0

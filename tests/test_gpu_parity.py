@@ -420,3 +420,32 @@ def test_single_launch_matches_two_launches(name):
     for t0, t1 in ((a.pools.k_cold, b.pools.k_cold), (a.pools.v_cold, b.pools.v_cold)):
         np.testing.assert_array_equal(pool_bytes(t0), pool_bytes(t1))
     assert torch.equal(a.batch.tables, b.batch.tables) and torch.equal(a.batch.lens, b.batch.lens)
+
+
+def test_prefix_only_requests_and_a_64k_prefix():
+    # Degenerate lengths: requests whose whole context is their group's
+    # prefix (no COLD token: the suffix part is empty, weight 0 in Eq. (1)),
+    # a request with neither (zero output, log-sum-exp -inf), and one group
+    # with a 65536-token prefix (key chunks at the 64-split cap), in every mode.
+    note("[gpu] prefix-only requests, 64K prefix")
+    suffix = [0, 7, 0, 300, 1, 0, 45, 0]
+    wl = W.make_custom(batch=8, num_q_heads=8, num_kv_heads=2, head_dim=128, dtype="bf16",
+                       group_prefix_len=[65536, 700], group_of=[0, 0, 1, 1, 0, -1, 1, 0], suffix_len=suffix, seed=70)
+    ref_o, ref_l = decode_reference(wl)
+    st = setup_single_step(wl)            # appends at least one token per request ...
+    zero = np.asarray(suffix) == 0
+    st.batch.lens_h[zero] = 0             # ... so the empty suffixes are set afterwards, host and device
+    st.batch.lens.copy_(torch.from_numpy(st.batch.lens_h).to(st.batch.lens.device))
+    ws = R.workspace(st.batch)
+    for mode, fn in (("cascade", lambda: R.cascade_decode(st.batch, st.pools, ws)),
+                     ("dense", lambda: R.dense_decode(st.batch, st.pools, ws)),
+                     ("per_group", lambda: R.decode_step(st.batch, st.pools, R.default_params(A.SPKV_MODE_PER_GROUP), ws)[:2])):
+        out, lse = fn()
+        torch.cuda.synchronize()
+        o, l = out.cpu().double().numpy(), lse.cpu().double().numpy()
+        assert np.all(o[5] == 0) and np.all(np.isneginf(l[5])), f"{mode}: empty context"
+        keep = np.arange(8) != 5
+        e_o = np.abs(o[keep] - ref_o[keep]).max()
+        e_l = np.abs(l[keep] - ref_l[keep]).max()
+        note(f"    {mode}: max_abs={e_o:.2e} lse={e_l:.2e}")
+        assert e_o <= TOL_O and e_l <= TOL_LSE
