@@ -23,6 +23,7 @@ from __future__ import annotations
 import argparse
 import gc
 import json
+import subprocess
 import os
 import sys
 import time
@@ -80,7 +81,39 @@ def parse():
                          "step 24, per-group vs batch-global dispatch, COLD page size 1 and 16; one JSON line")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-MiB device buffer 5 times (counter calibration) and exit")
+    ap.add_argument("--other-configs", default="C2,C3@16384,C4", metavar="LIST",
+                    help="configurations also measured (in child processes, short runs) by the default C1 step "
+                         "run and reported under 'other_configs'; 'none' for none")
     return ap.parse_args()
+
+
+def other_configs(args) -> dict:
+    """Short step-mode runs of further configurations, each in a child process
+    (its own pools and GPU context, one after the other): per configuration
+    ms per step, GPU ms per step, KV-tokens/s, the launches' durations and
+    fractions, and the step roofline."""
+    res = {}
+    for item in [x for x in args.other_configs.split(",") if x and x != "none"]:
+        cfg, _, lp = item.partition("@")
+        cmd = [sys.executable, os.path.abspath(__file__), "--config", cfg, "--mode", "step", "--steps", "10",
+               "--warmup", "3", "--no-cpu-baseline", "--cold-runs", "0", "--graph-steps", "0", "--other-configs", "none"]
+        if lp:
+            cmd += ["--lp", lp]
+        print(f"[bench] other configuration {item}", file=sys.stderr, flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+        lines = [l for l in r.stdout.splitlines() if l.startswith("{")]
+        if r.returncode != 0 or not lines:
+            res[item] = {"error": f"exit {r.returncode}", "stderr_tail": r.stderr[-400:]}
+            continue
+        d = json.loads(lines[-1])
+        res[item] = {"workload": d["config"]["workload"], "ms_per_step": d["ms_per_step"],
+                     "gpu_ms_per_step": d["gpu_ms_per_step"], "value": d["value"], "unit": d["unit"],
+                     "kernels": {k: {f: v[f] for f in ("avg_us", "hbm_frac", "mfma_frac") if f in v}
+                                 for k, v in d["kernels"].items()},
+                     "roofline": {k: d["roofline"].get(k) for k in ("kernel", "bound", "frac", "traffic_frac")},
+                     "step_roofline": d["step_roofline"]["frac"],
+                     "two_launches_gpu_ms_per_step": (d.get("two_launches") or {}).get("gpu_ms_per_step")}
+    return res
 
 
 def copy_probe(mib: int) -> int:
@@ -976,6 +1009,11 @@ def main():
         cpu = cpu_baseline(wl, args.cpu_seconds)
         cpu_1t = cpu_baseline(wl, args.cpu_seconds / 2, threads=1)
 
+    # ---- the other configurations (the default C1 step run only) ------------
+    others = None
+    if args.config == "C1" and args.lp is None and args.mode == "step" and args.other_configs not in ("", "none"):
+        others = other_configs(args)
+
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -1011,6 +1049,7 @@ def main():
         "cold_cache": cold_res,
         "cpu_baseline": cpu,
         "cpu_baseline_1t": cpu_1t,
+        "other_configs": others,
     }
     print(json.dumps(line), flush=True)
     return 0

@@ -146,7 +146,8 @@ def main():
     if a.layout:
         return layout_profile(a, prof_dir)
     bench = os.path.join(ROOT, "bench.py")
-    run = [bench, "--config", a.config, "--mode", a.mode, "--no-cpu-baseline", "--cold-runs", "0", "--graph-steps", "0"]
+    run = [bench, "--config", a.config, "--mode", a.mode, "--no-cpu-baseline", "--cold-runs", "0", "--graph-steps", "0",
+           "--other-configs", "none"]
     name = f"{a.config.lower()}_{a.mode}"
     cfg_key = a.config
     if a.lp is not None:
