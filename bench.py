@@ -53,6 +53,8 @@ def parse():
                     help="timed runs of the cold-cache protocol (0: skip); 10 untimed runs precede them")
     ap.add_argument("--flush-mib", type=int, default=1024, help="bytes written before each cold-cache run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the measured read and MFMA ceilings (spkv_probe_read / spkv_probe_mfma)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM traffic per launch (written by profile_step.py)")
     ap.add_argument("--sweep-lp", default=None, metavar="L1,L2,...",
@@ -87,7 +89,7 @@ def parse():
     return ap.parse_args()
 
 
-def other_configs(args) -> dict:
+def other_configs(args, ceilings=None) -> dict:
     """Short step-mode runs of further configurations, each in a child process
     (its own pools and GPU context, one after the other): per configuration
     ms per step, GPU ms per step, KV-tokens/s, the launches' durations and
@@ -96,7 +98,8 @@ def other_configs(args) -> dict:
     for item in [x for x in args.other_configs.split(",") if x and x != "none"]:
         cfg, _, lp = item.partition("@")
         cmd = [sys.executable, os.path.abspath(__file__), "--config", cfg, "--mode", "step", "--steps", "10",
-               "--warmup", "3", "--no-cpu-baseline", "--cold-runs", "0", "--graph-steps", "0", "--other-configs", "none"]
+               "--warmup", "3", "--no-cpu-baseline", "--cold-runs", "0", "--graph-steps", "0", "--other-configs", "none",
+               "--no-ceilings"]
         if lp:
             cmd += ["--lp", lp]
         print(f"[bench] other configuration {item}", file=sys.stderr, flush=True)
@@ -113,6 +116,9 @@ def other_configs(args) -> dict:
                      "roofline": {k: d["roofline"].get(k) for k in ("kernel", "bound", "frac", "traffic_frac")},
                      "step_roofline": d["step_roofline"]["frac"],
                      "two_launches_gpu_ms_per_step": (d.get("two_launches") or {}).get("gpu_ms_per_step")}
+        if ceilings:
+            for k, v in d["kernels"].items():
+                res[item]["kernels"][k]["frac_of_read_ceiling"] = round(v["gbps"] / ceilings["read_gbps"], 4)
     return res
 
 
@@ -127,6 +133,48 @@ def copy_probe(mib: int) -> int:
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
     return 0
+
+
+def measure_ceilings(torch, R, read_mib: int = 4096, reps: int = 10, mfma_iters: int = 20000):
+    """What this device achieves beside its published peaks: the best of
+    `reps` launches of a streaming read over `read_mib` MiB (well beyond the
+    caches) and of a bf16 MFMA loop on every SIMD, each timed with events on
+    the current stream (the one the probes launch on)."""
+    from shared_prefix_paged_amd import lib as _lib
+    import ctypes as C
+    cus = C.c_int32()
+    R.check(_lib.spkv_device_cus(C.byref(cus)))
+    buf = torch.empty(read_mib << 20, dtype=torch.uint8, device="cuda:0")
+    buf.fill_(1)
+    sink = torch.zeros(int(cus.value) * 16 * 4, dtype=torch.int32, device="cuda:0")   # a word per wave
+    waves = int(cus.value) * 8                   # two waves per SIMD
+    fsink = torch.empty(waves, dtype=torch.float32, device="cuda:0")
+
+    def best_ms(launch):
+        launch()
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            launch()
+            e1.record()
+            e1.synchronize()
+            best = min(best, e0.elapsed_time(e1))
+        return best
+
+    read_ms = best_ms(lambda: R.probe_read(buf, sink))
+    mfma_ms = best_ms(lambda: R.probe_mfma(waves, mfma_iters, fsink))
+    torch.cuda.synchronize()
+    nbytes = buf.numel()
+    flops = 8.0 * 32 * 32 * 16 * 2 * waves * mfma_iters
+    del buf
+    return {"read_gbps": round(nbytes / read_ms / 1e6, 1), "read_bytes": nbytes,
+            "mfma_bf16_tflops": round(flops / mfma_ms / 1e9, 1), "mfma_waves": waves, "mfma_iters": mfma_iters,
+            "note": f"best of {reps} launches each: spkv_probe_read (block-contiguous 32 KB chunks, 8 "
+                    f"nontemporal 16-byte loads in flight per lane, 16 blocks of 256 per CU, a plain store per "
+                    f"wave) and spkv_probe_mfma (8 independent "
+                    f"32x32x16 bf16 MFMA chains per wave, 2 waves per SIMD)"}
 
 
 def quiet_gc() -> None:
@@ -611,11 +659,14 @@ def admission_sweep(args) -> int:
 
 
 def source_digest() -> str:
-    """Digest of the sources that decide what the kernels read and write."""
+    """Digest of the sources that decide what the kernels read and write
+    (probes.hip holds only the measurement probes)."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "shared_prefix_paged_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
+        if f == "probes.hip":
+            continue
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
@@ -1003,6 +1054,19 @@ def main():
     if cold_res is not None:
         cold_res["step_roofline_frac"] = round(t_star / cold_res["median_us"], 4)
 
+    # ---- measured ceilings: each launch against what the device achieves ----
+    ceilings = None
+    if not args.no_ceilings:
+        ceilings = measure_ceilings(torch, R)
+        for tab in [kernels] + ([two_launches["kernels"]] if two_launches else []):
+            for k in tab.values():
+                k["frac_of_read_ceiling"] = round(k["gbps"] / ceilings["read_gbps"], 4)
+                if "tflops" in k:
+                    k["frac_of_mfma_ceiling"] = round(k["tflops"] / ceilings["mfma_bf16_tflops"], 4)
+        roofline["measured_peak"] = ceilings["read_gbps"] if roofline["bound"] == "hbm" \
+            else ceilings["mfma_bf16_tflops"]
+        roofline["frac_of_measured_peak"] = round(roofline["achieved"] / roofline["measured_peak"], 4)
+
     # ---- oracle on the host cores, bounded sample ---------------------------
     cpu = cpu_1t = None
     if not args.no_cpu_baseline:
@@ -1012,7 +1076,7 @@ def main():
     # ---- the other configurations (the default C1 step run only) ------------
     others = None
     if args.config == "C1" and args.lp is None and args.mode == "step" and args.other_configs not in ("", "none"):
-        others = other_configs(args)
+        others = other_configs(args, ceilings)
 
     line = {
         "metric": METRIC,
@@ -1046,6 +1110,7 @@ def main():
         "plan": {f: int(getattr(plan, f)) for f, _ in plan._fields_},
         "roofline": roofline,
         "step_roofline": step_roofline,
+        "ceilings": ceilings,
         "cold_cache": cold_res,
         "cpu_baseline": cpu,
         "cpu_baseline_1t": cpu_1t,

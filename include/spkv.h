@@ -472,6 +472,23 @@ spkv_status spkv_timing_reset(void);
 /* Number of compute units of the current device (SPKV_E_HIP without a GPU). */
 spkv_status spkv_device_cus(int32_t *cus_out);
 
+/* Measured ceilings, for rooflines against what this device achieves beside
+ * its published peaks.  Each is one launch on `stream`; time it with events
+ * around the call.
+ * spkv_probe_read: streams `bytes` bytes of device memory at `src` (16-byte
+ * aligned, bytes a multiple of 16 and > 0) through nontemporal 16-byte
+ * vector loads, each block of 4 waves taking contiguous 32 KB chunks in turn;
+ * min(16 * CUs, chunks, sink_words / 4) blocks.  Wave w writes the XOR of
+ * the 32-bit words it read to sink[w] (device uint32, sink_words >= 4
+ * entries; entries past the launched waves are left as they are, so the XOR
+ * of a zeroed sink is the checksum of the buffer).
+ * spkv_probe_mfma: `waves` waves (a multiple of 4, > 0) each run `iters`
+ * rounds of 8 independent v_mfma_f32_32x32x16_bf16 (8 x 32768 FLOPs per
+ * round) from register operands and write one accumulator sum per wave to
+ * sink[wave] (device float).  SPKV_E_INVAL on bad sizes. */
+spkv_status spkv_probe_read(const void *src, size_t bytes, uint32_t *sink, int32_t sink_words, void *stream);
+spkv_status spkv_probe_mfma(int32_t waves, int32_t iters, float *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -147,7 +147,7 @@ def main():
         return layout_profile(a, prof_dir)
     bench = os.path.join(ROOT, "bench.py")
     run = [bench, "--config", a.config, "--mode", a.mode, "--no-cpu-baseline", "--cold-runs", "0", "--graph-steps", "0",
-           "--other-configs", "none"]
+           "--other-configs", "none", "--no-ceilings"]
     name = f"{a.config.lower()}_{a.mode}"
     cfg_key = a.config
     if a.lp is not None:

@@ -107,6 +107,8 @@ SIGNATURES = {
     "spkv_timing_read": (c_i32, [c_i32, P_f64, P_i64]),
     "spkv_timing_reset": (c_i32, []),
     "spkv_device_cus": (c_i32, [P_i32]),
+    "spkv_probe_read": (c_i32, [c_vp, c_sz, c_vp, c_i32, c_vp]),
+    "spkv_probe_mfma": (c_i32, [c_i32, c_i32, c_vp, c_vp]),
 }
 
 

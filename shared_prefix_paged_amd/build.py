@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libspkv.so")
 
 HOST_SOURCES = ["alloc.cpp", "plan.cpp"]
-HIP_SOURCES = ["kernels.hip"]
+HIP_SOURCES = ["kernels.hip", "probes.hip"]
 ARCH = "gfx950"
 
 

@@ -475,3 +475,23 @@ class KernelTimer:
         ms, n = C.c_double(), C.c_int64()
         check(lib.spkv_timing_read(int(kernel), C.byref(ms), C.byref(n)))
         return ms.value, n.value
+
+
+def probe_read(buf, sink, stream=None):
+    """spkv_probe_read over the bytes of a contiguous device tensor: wave w
+    writes the XOR of the 32-bit words it read to sink[w] (an int32 device
+    tensor of at least 4 elements, which bounds the blocks launched)."""
+    torch = _torch()
+    if sink.dtype != torch.int32 or sink.numel() < 4:
+        raise ValueError("probe_read: sink must be int32 with at least 4 elements")
+    words = int(min(sink.numel(), 2 ** 31 - 1))
+    check(lib.spkv_probe_read(_dp(buf), buf.numel() * buf.element_size(), _dp(sink), words, stream_handle(stream)))
+
+
+def probe_mfma(waves: int, iters: int, sink, stream=None):
+    """spkv_probe_mfma: `waves` waves of `iters` rounds of 8 bf16 32x32x16
+    MFMAs; one float per wave into sink (numel >= waves)."""
+    torch = _torch()
+    if sink.dtype != torch.float32 or sink.numel() < waves:
+        raise ValueError("probe_mfma: sink must be float32 with at least `waves` elements")
+    check(lib.spkv_probe_mfma(int(waves), int(iters), _dp(sink), stream_handle(stream)))
