@@ -53,6 +53,8 @@ def parse():
                     help="timed runs of the cold-cache protocol (0: skip); 10 untimed runs precede them")
     ap.add_argument("--flush-mib", type=int, default=1024, help="bytes written before each cold-cache run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--single-launch", type=int, default=1, choices=(0, 1, 2),
+                    help="spkv_dispatch_params.single_launch of the timed steps")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the measured read and MFMA ceilings (spkv_probe_read / spkv_probe_mfma)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -99,7 +101,7 @@ def other_configs(args, ceilings=None) -> dict:
         cfg, _, lp = item.partition("@")
         cmd = [sys.executable, os.path.abspath(__file__), "--config", cfg, "--mode", "step", "--steps", "10",
                "--warmup", "3", "--no-cpu-baseline", "--cold-runs", "0", "--graph-steps", "0", "--other-configs", "none",
-               "--no-ceilings"]
+               "--no-ceilings", "--single-launch", str(args.single_launch)]
         if lp:
             cmd += ["--lp", lp]
         print(f"[bench] other configuration {item}", file=sys.stderr, flush=True)
@@ -754,6 +756,7 @@ def main():
     mode = {"step": A.SPKV_MODE_PER_GROUP, "cascade": A.SPKV_MODE_FORCE_CASCADE,
             "dense": A.SPKV_MODE_FORCE_DENSE}[args.mode]
     params = R.default_params(mode)
+    params.single_launch = args.single_launch
     lp_of = np.array([wl.prefix_len_of(b) for b in range(B)], dtype=np.int64)
     state = {"i": 0, "choice": None}
     separate = args.separate_append or cfg.dtype != "bf16"     # the fused step is bf16 only
@@ -869,7 +872,7 @@ def main():
                 one_step()
             torch.cuda.synchronize()
         kt2_ms = {k: kt2.read(k) for k in (A.SPKV_KERNEL_PREFIX, A.SPKV_KERNEL_FLAT, A.SPKV_KERNEL_MERGE)}
-        params.single_launch = 1
+        params.single_launch = args.single_launch
 
     # ---- the same steps through the HIP-graph entry point: host time of the
     # call (record, update the graph's kernel nodes in place, launch) and GPU

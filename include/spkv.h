@@ -335,8 +335,11 @@ typedef struct spkv_dispatch_params {
     double  row_cost_ns;           /* cascade cost per query row of a group that takes it
                                       (its prefix partial states: written, then merged) */
     int32_t single_launch;         /* 1 (default): the paged pass and the prefix contraction run as one
-                                      launch where the plan allows it (spkv_plan_info.single_launch);
-                                      0: always two launches.  Results are the same either way. */
+                                      launch where the plan allows it (spkv_plan_info.single_launch),
+                                      side by side in every launch block where the plan marks it
+                                      co-resident (spkv_plan_info.co_resident), else the prefix blocks
+                                      after the paged ranges; 2: one launch, never co-resident;
+                                      0: always two launches. */
 } spkv_dispatch_params;
 
 /* Defaults fitted on MI355X (see the design notes for the fit). */
@@ -348,9 +351,14 @@ spkv_status spkv_dispatch(const spkv_batch *batch, const spkv_dispatch_params *p
 /* Dispatch, then run: groups chosen for cascade take the prefix contraction,
  * the others are folded into the flat pass; one merge finishes every row.
  * Where the plan allows it and params->single_launch is set, the paged pass
- * and the prefix contraction run as one launch (the prefix blocks fill the
- * paged pass's tail); the results are bit-identical to two launches.
- * spkv_cascade_decode uses the single launch wherever the plan allows it.
+ * and the prefix contraction run as one launch.  Co-resident (the default
+ * where the plan marks it): every launch block runs a paged block on four
+ * waves and a prefix item on two or four more, the prefix in one key half,
+ * so its values differ from the two launches' by rounding order only (within
+ * the same bound of the exact result).  Otherwise the prefix blocks follow
+ * the paged ranges in the grid and the results are bit-identical to two
+ * launches.  spkv_cascade_decode uses the single launch wherever the plan
+ * allows it.
  * cascade_out (host [ng], nullable) reports the choice. */
 spkv_status spkv_decode_step(const spkv_batch *batch, const spkv_kv *kv, const spkv_dispatch_params *params,
                              float *out, float *lse, void *ws, size_t ws_bytes, void *stream,
@@ -443,6 +451,11 @@ typedef struct spkv_plan_info {
                                       (groups of more than 32 query rows per KV head)); the
                                       paged ranges come first in the grid and the prefix blocks take CUs as
                                       ranges finish */
+    int32_t co_resident;           /* 1: that one launch can run both roles in every launch block (four
+                                      paged waves beside the prefix item's waves, LDS rings of three
+                                      stages each): the prefix items of cascade groups with a prefix,
+                                      counted at prefix_mtiles for every group, number no more than the
+                                      paged blocks */
 } spkv_plan_info;
 
 spkv_status spkv_plan_query(const spkv_batch *batch, const int32_t *cascade, spkv_plan_info *out);

@@ -107,6 +107,9 @@ struct Plan {
     bool run_prefix;          // some cascade group has Lp > 0
     bool prefix_split_p;      // some cascade group is short: carry P as bf16 hi + lo
     bool single_launch;       // the paged pass and the prefix contraction may share one launch
+    int64_t co_prefix_items;  // prefix items of cascade groups with a prefix (the co-resident launch's count)
+    bool co_resident;         // single launch with both roles in every block: its prefix items fit beside
+                              // the paged blocks in one round
 };
 
 // LDS bytes of one wave of the bf16 paged pass: its ring (K and V rows of

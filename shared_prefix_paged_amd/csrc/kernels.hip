@@ -515,9 +515,9 @@ __device__ __forceinline__ void attend_range(const Args &a, const Req &r, int b,
 // reads (16 rows, one chunk each) and the transposing V reads (16 rows,
 // 32 bytes each) spread over all LDS banks.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, int S_ = spkv::kFlatMfmaStages>
 struct FlatMfmaGeom {
-    static constexpr int S = spkv::kFlatMfmaStages;
+    static constexpr int S = S_;
     static constexpr int TOK = spkv::kFlatMfmaTokens;   // tokens per stage
     static constexpr int ROWB = D * 2;                   // bytes per K/V row
     static constexpr int OPB = TOK * ROWB;               // bytes per stage operand
@@ -532,8 +532,7 @@ struct FlatMfmaGeom {
     static constexpr int KS = D / 32;                    // score MFMAs per stage
     static constexpr int NDB = D / 16;                   // 16-dim output blocks
     static_assert(TOK == 16, "one 16x16 score tile per stage");
-    static_assert(S - 1 < SPB, "prologue stays inside the first 64-token block");
-    static_assert((S & (S - 1)) == 0, "ring index is a mask");
+    static_assert(S >= 2 && S - 1 < SPB, "prologue stays inside the first 64-token block");
 };
 static_assert(FlatMfmaGeom<128>::WAVEB == spkv::flat_mfma_wave_bytes(128), "plan and kernel agree on the ring");
 static_assert(FlatMfmaGeom<64>::WAVEB == spkv::flat_mfma_wave_bytes(64), "plan and kernel agree on the ring");
@@ -572,10 +571,10 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 // ends with it loads the head's K/V rows of the token from k_new / v_new at
 // its start and, once its last stage has landed, writes them over the token's
 // row of that stage in LDS (the token's DMA lanes fetched a placeholder row).
-template <int D, int G, bool APP, bool NT>
+template <int D, int G, bool APP, bool NT, int S_ = spkv::kFlatMfmaStages>
 __device__ __forceinline__ void attend_range_mfma(const Args &a, const Req &r, int b, int h, int t0, int t1,
                                                   int slot, int lane, char *ring, uint32_t ring_off) {
-    using F = FlatMfmaGeom<D>;
+    using F = FlatMfmaGeom<D, S_>;
     constexpr int S = F::S, TOK = F::TOK, SPB = F::SPB, NDMA = F::NDMA, KS = F::KS, NDB = F::NDB;
     constexpr float kRescaleSlack = 8.f;     // see the prefix kernel: exact for any reference
     static_assert(G >= 1 && G <= 16, "query rows of a head fit the 16 MFMA columns");
@@ -676,7 +675,7 @@ __device__ __forceinline__ void attend_range_mfma(const Args &a, const Req &r, i
 
     // Stage j: tokens t0 + 16j .. t0 + 16j + 15 into ring slot j % S.
     auto issue = [&](int j) {
-        const uint32_t dst = ring_off + (uint32_t)((j & (S - 1)) * F::STAGEB);
+        const uint32_t dst = ring_off + (uint32_t)(((unsigned)j % (unsigned)S) * F::STAGEB);
 #pragma unroll
         for (int i = 0; i < NDMA; ++i) {
             const int ti = (j % SPB) * TOK + F::RPI * i + lane / F::CPR;   // token inside its 64-block
@@ -818,12 +817,12 @@ struct MergeRows {
 // One block of the paged pass: range k of the stream-K split, head group hy;
 // wave `wave` (< kFlatWavesMax) of it takes KV head hy * kFlatWavesMax + wave
 // with its ring at smem + wave * WAVEB.
-template <bool BF16, int D, int G, bool APP, bool NT>
+template <bool BF16, int D, int G, bool APP, bool NT, int S_ = spkv::kFlatMfmaStages>
 __device__ __forceinline__ void flat_block(const Args &a, const FlatLaunch &fl, const int k, const int hy,
                                            const int wave, const int lane, char *smem) {
     const int h = hy * kFlatWavesMax + wave;
     if (h >= a.Hkv) return;
-    constexpr int WAVEB = BF16 ? FlatMfmaGeom<D>::WAVEB : FlatGeom<BF16, D>::WAVEB;
+    constexpr int WAVEB = BF16 ? FlatMfmaGeom<D, S_>::WAVEB : FlatGeom<BF16, D>::WAVEB;
     char *ring = smem + wave * WAVEB;
     const uint32_t ring_off = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_offset(ring));
     const int64_t T = fl.total;
@@ -855,7 +854,8 @@ __device__ __forceinline__ void flat_block(const Args &a, const FlatLaunch &fl, 
         const int t0 = lo + (int)(lo_s - o0);
         const int t1 = min(hi, lo + (int)(hi_s - o0));   // device data shorter than the plan: clamp
         if (t1 <= t0) continue;
-        if constexpr (BF16) attend_range_mfma<D, G, APP, NT>(a, r, b, h, t0, t1, slot0 + slot, lane, ring, ring_off);
+        if constexpr (BF16)
+            attend_range_mfma<D, G, APP, NT, S_>(a, r, b, h, t0, t1, slot0 + slot, lane, ring, ring_off);
         else attend_range<BF16, D, G>(a, r, b, h, t0, t1, slot0 + slot, lane, ring, ring_off);
     }
 }
@@ -923,17 +923,37 @@ __device__ __forceinline__ int vchunk_logical(int r, int p) {
 // a row gets half as many partial states at the same number of waves per CU.
 constexpr int kPrefixStages = 4;
 constexpr int kMemberWin = 40;                 // >= 32 rows / G + 1 members
-template <int D, int KH>
-constexpr int prefix_ring_bytes() { return KH * kPrefixStages * 2 * spkv::kPrefixKeyTile * D * 2; }
+template <int D, int KH, int STAGES = kPrefixStages>
+constexpr int prefix_ring_bytes() { return KH * STAGES * 2 * spkv::kPrefixKeyTile * D * 2; }
+
+// Barrier of the W prefix waves of a block that also holds waves of another
+// role (which never reach it): a counter in LDS that only grows.  The k-th
+// barrier of each wave adds one and waits until the count reaches W * k.
+// Every prefix wave passes the same number of barriers; the wait still gives
+// up after a bounded number of polls, so no wave can wait forever.
+__device__ __forceinline__ void waves_barrier(uint32_t *ctr, uint32_t target) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's LDS reads of the tile before it arrives
+    if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    for (int poll = 0; poll < (1 << 22); ++poll) {
+        const uint32_t v = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (__builtin_amdgcn_readfirstlane(v) >= target) break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    asm volatile("" ::: "memory");
+}
 
 // One block of the prefix contraction: key split s, row tile mt, (group, KV
-// head) gz.  smem: prefix_ring_bytes<D, KH>() bytes of LDS (1 KB aligned);
-// member_win: W * KH windows of kMemberWin entries in LDS.
-template <int D, int W, bool SPLIT_P, int KH>
-__device__ __forceinline__ void prefix_block(const Args &a, const int s, const int mt, const int gz, char *smem,
-                                             int32_t (*member_win)[kMemberWin]) {
+// head) gz, run by waves wave_id = 0 .. W * KH - 1.  smem:
+// prefix_ring_bytes<D, KH, STAGES>() bytes of LDS (1 KB aligned); member_win:
+// W * KH windows of kMemberWin entries in LDS.  SWB: the block also runs
+// waves of another role, so the prefix waves meet at waves_barrier on the
+// LDS counter `bar` instead of the block-wide hardware barrier (one key half
+// only).
+template <int D, int W, bool SPLIT_P, int KH, int STAGES = kPrefixStages, bool SWB = false>
+__device__ __forceinline__ void prefix_block(const Args &a, const int s, const int mt, const int gz,
+                                             const int wave_id, char *smem, int32_t (*member_win)[kMemberWin],
+                                             uint32_t *bar = nullptr) {
     constexpr int NT = spkv::kPrefixKeyTile;   // 32 keys per tile
-    constexpr int STAGES = kPrefixStages;
     constexpr int KS = D / 16;                 // MFMA k-steps for Q.K
     constexpr int NDB = D / 32;                // 32-column blocks of the output
     constexpr int ROWB = D * 2;                // bytes per K/V row
@@ -944,7 +964,9 @@ __device__ __forceinline__ void prefix_block(const Args &a, const int s, const i
     static_assert(IPW >= 1 && (NT / RPI) % W == 0, "tile must split evenly over the waves");
     constexpr int AHEAD = (STAGES - 2) * 2 * IPW;   // DMAs issued after a tile's own
     static_assert(KH == 1 || KH == 2, "one or two key halves");
-    static_assert(prefix_ring_bytes<D, KH>() == KH * STAGES * 2 * TILEB, "ring size");
+    static_assert(prefix_ring_bytes<D, KH, STAGES>() == KH * STAGES * 2 * TILEB, "ring size");
+    static_assert(STAGES >= 3, "one tile in flight besides the one computed and the one issued");
+    static_assert(!SWB || KH == 1, "the two-half exchange uses the hardware barrier");
 
     const int g = gz / a.Hkv;
     const int h = gz % a.Hkv;
@@ -955,11 +977,10 @@ __device__ __forceinline__ void prefix_block(const Args &a, const int s, const i
     const int chunk = spkv::chunk_for(lp, a.prefix_tau, spkv::kPrefixSplitCap, NT);
     const int nsplit = spkv::splits_for(lp, chunk);
     if (s >= nsplit) return;
-    const int tid = threadIdx.x;
-    const int wave_id = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int wave = wave_id % W;            // row wave (32 query rows)
     const int khalf = wave_id / W;           // key half
-    const int lane = tid & 63;
+    const int lane = threadIdx.x & 63;
+    uint32_t bar_k = 0;                      // barriers passed (SWB)
     // Tiles of the block's chunk: the first ceil(n/2) to half 0, the rest to
     // half 1.  Every wave runs nt_loop steps (a half with fewer tiles only
     // takes part in the barriers), so the barrier count is the same for all.
@@ -1137,8 +1158,12 @@ __device__ __forceinline__ void prefix_block(const Args &a, const int s, const i
                 if (t + STAGES - 2 < ntiles) wait_vmcnt<AHEAD>();
                 else wait_vmcnt<0>();
             }
-            __builtin_amdgcn_s_barrier();      // tile t visible; every wave is done with tile t-1
-            asm volatile("" ::: "memory");
+            if constexpr (SWB) {
+                waves_barrier(bar, (uint32_t)W * ++bar_k);
+            } else {
+                __builtin_amdgcn_s_barrier();  // tile t visible; every wave is done with tile t-1
+                asm volatile("" ::: "memory");
+            }
             if (!act) continue;
             if (t + STAGES - 1 < ntiles) issue(t + STAGES - 1, (st + STAGES - 1) % STAGES);
 
@@ -1268,7 +1293,8 @@ template <int D, int W, bool SPLIT_P, int KH = 1>
 __global__ __launch_bounds__(64 * W * KH) void prefix_mfma_kernel(Args a) {
     __shared__ __attribute__((aligned(1024))) char smem[prefix_ring_bytes<D, KH>()];
     __shared__ int32_t member_win[W * KH][kMemberWin];
-    prefix_block<D, W, SPLIT_P, KH>(a, blockIdx.x, blockIdx.y, blockIdx.z, smem, member_win);
+    prefix_block<D, W, SPLIT_P, KH>(a, blockIdx.x, blockIdx.y, blockIdx.z,
+                                    __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6), smem, member_win);
 }
 
 // The paged pass and the prefix contraction in one launch (bf16, d = 128,
@@ -1306,8 +1332,97 @@ __global__ __launch_bounds__(512) void paged_prefix_kernel(Args a, FlatLaunch fl
     if ((int)(threadIdx.x >> 6) >= 2 * PW) return;
     const int r = bid - paged_blocks;
     const int s = r % psplits, mt = (r / psplits) % pmtiles, gz = r / (psplits * pmtiles);
-    prefix_block<D, PW, false, 2>(a, s, mt, gz, pp_smem,
+    prefix_block<D, PW, false, 2>(a, s, mt, gz, __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6), pp_smem,
                                   (int32_t(*)[kMemberWin])(pp_smem + prefix_ring_bytes<D, 2>()));
+}
+
+// The paged pass and the prefix contraction side by side on every CU (bf16,
+// d = 128): launch block b runs paged block b on waves 0..3 (rings of
+// kCoFlatStages stages) and prefix item b on waves 4 .. 4 + PW - 1 (one key
+// half, a ring of kCoPrefixStages tiles).  The prefix waves meet at an LDS
+// counter barrier of their own, so neither role waits for the other: the
+// MFMA-bound contraction runs beside the HBM-bound paged pass instead of
+// after it, with the same arithmetic and partial-state slots.
+constexpr int kCoFlatStages = 3;
+constexpr int kCoPrefixStages = 3;
+constexpr size_t co_flat_bytes() { return (size_t)kFlatWavesMax * FlatMfmaGeom<128, kCoFlatStages>::WAVEB; }
+constexpr size_t co_prefix_bytes() { return (size_t)prefix_ring_bytes<128, 1, kCoPrefixStages>(); }
+constexpr size_t co_lds() { return co_flat_bytes() + co_prefix_bytes() + 4 * kMemberWin * sizeof(int32_t) + 16; }
+static_assert(co_flat_bytes() % 1024 == 0, "the prefix ring starts 1 KB aligned");
+static_assert(co_lds() <= (size_t)spkv::kLdsPerCU, "one co-resident block per CU");
+
+// Prefix item r of the co-resident launch, counted over cascade groups with a
+// prefix only (group g holds nsplit_g * pmtiles * Hkv items, nsplit_g from
+// the split rule), so that no launch block is left with an empty item while
+// real ones wait for a second round.  One wave-wide pass over hot_len;
+// returns false if r is past the last item.
+__device__ __forceinline__ bool co_prefix_item(const Args &a, int r, int pmtiles, int &s, int &mt, int &gz) {
+    const int lane = threadIdx.x & 63;
+    int base = 0;                              // items of the groups before this 64-group window
+    for (int g0 = 0; g0 < a.ng; g0 += 64) {
+        const int g = g0 + lane;
+        int n = 0;
+        if (g < a.ng && mask_get(a.cascade, g)) {
+            const int lp = a.hot_len[g];
+            if (lp > 0) n = spkv::splits_for(lp, spkv::chunk_for(lp, a.prefix_tau, spkv::kPrefixSplitCap, a.prefix_granule));
+        }
+        const int c = n * pmtiles * a.Hkv;
+        int incl = c;                          // inclusive prefix sum over the window's lanes
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int v = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += v;
+        }
+        const int total = __shfl(incl, 63, 64);
+        if (r < base + total) {
+            const uint64_t hit = __ballot(r < base + incl);
+            const int gl = __builtin_ctzll(hit);   // first lane whose inclusive sum passes r
+            const int ng_items = __shfl(n, gl, 64);
+            const int local = r - base - (__shfl(incl, gl, 64) - __shfl(c, gl, 64));
+            s = local % ng_items;
+            mt = (local / ng_items) % pmtiles;
+            gz = (g0 + gl) * a.Hkv + local / (ng_items * pmtiles);
+            return true;
+        }
+        base += total;
+    }
+    return false;
+}
+
+template <int D, int G, bool APP, bool NT, int PW>
+__global__ __launch_bounds__(512) void paged_prefix_co_kernel(Args a, FlatLaunch fl, int paged_blocks,
+                                                              int prefix_items, int pmtiles) {
+    static_assert(D == 128, "ring layout sized for d = 128");
+    extern __shared__ __attribute__((aligned(1024))) char co_smem[];
+    using F = FlatMfmaGeom<D, kCoFlatStages>;
+    char *pring = co_smem + co_flat_bytes();
+    int32_t(*win)[kMemberWin] = (int32_t(*)[kMemberWin])(pring + co_prefix_bytes());
+    uint32_t *bar = (uint32_t *)(win + 4);
+    if (threadIdx.x == 0) *bar = 0u;
+    __syncthreads();                           // every wave of the block is alive here
+    const int bid = blockIdx.x;
+    const int wave = threadIdx.x >> 6;
+    if (wave < kFlatWavesMax) {
+        if (bid >= paged_blocks) return;
+        const int hpb = a.Hkv < kFlatWavesMax ? a.Hkv : kFlatWavesMax;   // 1, 2 or 4 (checked by the plan)
+        const int per = kFlatWavesMax / hpb;
+        const int pb = bid * per + wave / hpb;
+        const int head_groups = (a.Hkv + hpb - 1) / hpb;
+        if (pb >= fl.blocks * head_groups) return;
+        const int sub = wave / hpb;
+        flat_block<true, D, G, APP, NT, kCoFlatStages>(a, fl, pb % fl.blocks, pb / fl.blocks, wave - sub * hpb,
+                                                       threadIdx.x & 63, co_smem + sub * hpb * F::WAVEB);
+        return;
+    }
+    const int pw = wave - kFlatWavesMax;
+    if (pw >= PW || bid >= prefix_items) return;
+    int s = 0, mt = 0, gz = 0;
+    if (!co_prefix_item(a, bid, pmtiles, s, mt, gz)) return;   // the same answer in every prefix wave
+    s = __builtin_amdgcn_readfirstlane(s);     // wave-uniform already; say so for the scalar DMA bases
+    mt = __builtin_amdgcn_readfirstlane(mt);
+    gz = __builtin_amdgcn_readfirstlane(gz);
+    prefix_block<D, PW, false, 1, kCoPrefixStages, true>(a, s, mt, gz, __builtin_amdgcn_readfirstlane(pw), pring,
+                                                         win, bar);
 }
 
 // ---------------------------------------------------------------------------
@@ -1943,6 +2058,55 @@ spkv_status launch_paged_prefix_g(const Args &a, const Plan &p, bool app, TimedL
     return p.prefix_waves == 4 ? launch_paged_prefix_w<G, 4>(a, p, app, tl) : launch_paged_prefix_w<G, 2>(a, p, app, tl);
 }
 
+template <int G, bool APP, bool NT, int PW>
+spkv_status launch_paged_prefix_co_k(const Args &a, const Plan &p, TimedLaunch &tl) {
+    constexpr int D = 128;
+    static const hipError_t attr = hipFuncSetAttribute((const void *)paged_prefix_co_kernel<D, G, APP, NT, PW>,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, spkv::kLdsPerCU);
+    if (attr != hipSuccess)
+        return fail(SPKV_E_HIP, std::string("paged_prefix_co_kernel LDS limit: ") + hipGetErrorString(attr));
+    const FlatLaunch &f = p.flat[0];
+    const int hpb = a.Hkv < kFlatWavesMax ? a.Hkv : kFlatWavesMax;
+    const int per = kFlatWavesMax / hpb;
+    const int64_t paged = ((int64_t)f.blocks * p.flat_head_groups + per - 1) / per;
+    const int64_t prefix = p.co_prefix_items;
+    if (paged >= ((int64_t)1 << 31) || prefix >= ((int64_t)1 << 31))
+        return fail(SPKV_E_INVAL, "paged_prefix_co_kernel: grid too large");
+    dim3 grid((unsigned)std::max(paged, prefix)), block(512);
+    tl.launch(paged_prefix_co_kernel<D, G, APP, NT, PW>, grid, block, co_lds(), a, f, (int)paged, (int)prefix,
+              p.prefix_mtiles);
+    return check_launch("paged_prefix_co_kernel");
+}
+
+template <int G, int PW>
+spkv_status launch_paged_prefix_co_w(const Args &a, const Plan &p, bool app, TimedLaunch &tl) {
+    if (app) return a.cold_nt ? launch_paged_prefix_co_k<G, true, true, PW>(a, p, tl)
+                              : launch_paged_prefix_co_k<G, true, false, PW>(a, p, tl);
+    return a.cold_nt ? launch_paged_prefix_co_k<G, false, true, PW>(a, p, tl)
+                     : launch_paged_prefix_co_k<G, false, false, PW>(a, p, tl);
+}
+
+template <int G>
+spkv_status launch_paged_prefix_co_g(const Args &a, const Plan &p, bool app, TimedLaunch &tl) {
+    return p.prefix_waves == 4 ? launch_paged_prefix_co_w<G, 4>(a, p, app, tl)
+                               : launch_paged_prefix_co_w<G, 2>(a, p, app, tl);
+}
+
+spkv_status launch_paged_prefix_co(const Args &a, const Plan &p, bool app, hipStream_t st) {
+    TimedLaunch tl(SPKV_KERNEL_PAGED_PREFIX, st);
+    switch (a.G) {
+    case 1: return launch_paged_prefix_co_g<1>(a, p, app, tl);
+    case 2: return launch_paged_prefix_co_g<2>(a, p, app, tl);
+    case 3: return launch_paged_prefix_co_g<3>(a, p, app, tl);
+    case 4: return launch_paged_prefix_co_g<4>(a, p, app, tl);
+    case 5: return launch_paged_prefix_co_g<5>(a, p, app, tl);
+    case 6: return launch_paged_prefix_co_g<6>(a, p, app, tl);
+    case 7: return launch_paged_prefix_co_g<7>(a, p, app, tl);
+    case 8: return launch_paged_prefix_co_g<8>(a, p, app, tl);
+    default: return fail(SPKV_E_INVAL, "paged_prefix_co_kernel: unsupported group size");
+    }
+}
+
 spkv_status launch_paged_prefix(const Args &a, const Plan &p, bool app, hipStream_t st) {
     TimedLaunch tl(SPKV_KERNEL_PAGED_PREFIX, st);
     switch (a.G) {
@@ -2027,11 +2191,13 @@ struct AppendIn {
     const int32_t *slots;   // host [B]
 };
 
-// single_launch: run the paged pass and the prefix contraction as one
-// paged_prefix_kernel launch when the plan allows it (same results).
+// single_launch: where the plan allows one launch for the paged pass and
+// the prefix contraction, 1 runs paged_prefix_co_kernel where the plan marks
+// it co-resident and paged_prefix_kernel elsewhere, 2 always
+// paged_prefix_kernel, 0 two launches.
 spkv_status run_decode(const spkv_batch *b, const spkv_kv *kv, const int32_t *cascade, float *out, float *lse,
                        void *ws, size_t ws_bytes, void *stream, const AppendIn *app = nullptr,
-                       bool single_launch = true) {
+                       int single_launch = 1) {
     spkv_status st = spkv::validate_batch(b, kv);
     if (st != SPKV_OK) return st;
     if (!kv) return fail(SPKV_E_INVAL, "null kv");
@@ -2067,8 +2233,9 @@ spkv_status run_decode(const spkv_batch *b, const spkv_kv *kv, const int32_t *ca
     // last-level cache when the merge reads them, and their write-back does
     // not compete with the paged pass's reads.  Sub-batch i is entry i of
     // both paged passes.
-    if (p.single_launch && single_launch) {
-        st = launch_paged_prefix(a, p, app != nullptr, hs);
+    if (p.single_launch && single_launch != 0) {
+        st = p.co_resident && single_launch == 1 ? launch_paged_prefix_co(a, p, app != nullptr, hs)
+                                                 : launch_paged_prefix(a, p, app != nullptr, hs);
         if (st != SPKV_OK) return st;
     } else {
         for (size_t i = 0; i < p.flat.size(); ++i) {
@@ -2283,7 +2450,7 @@ spkv_status spkv_decode_step(const spkv_batch *batch, const spkv_kv *kv, const s
     if (cascade_out)
         for (int g = 0; g < batch->num_groups; ++g) cascade_out[g] = choice[(size_t)g];
     return run_decode(batch, kv, choice.data(), out, lse, ws, ws_bytes, stream, nullptr,
-                      !params || params->single_launch != 0);
+                      params ? params->single_launch : 1);
 }
 
 spkv_status spkv_decode_step_append(const spkv_batch *batch, const spkv_kv *kv, const spkv_dispatch_params *params,
@@ -2314,7 +2481,7 @@ spkv_status spkv_decode_step_append(const spkv_batch *batch, const spkv_kv *kv, 
         for (int g = 0; g < batch->num_groups; ++g) cascade_out[g] = choice[(size_t)g];
     const AppendIn app{k_new, v_new, host_slots};
     return run_decode(batch, kv, choice.data(), out, lse, ws, ws_bytes, stream, &app,
-                      !params || params->single_launch != 0);
+                      params ? params->single_launch : 1);
 }
 
 spkv_status spkv_decode_step_append_noalloc(const spkv_batch *batch, const spkv_kv *kv,

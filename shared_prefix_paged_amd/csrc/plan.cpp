@@ -242,6 +242,24 @@ spkv_status make_plan(const spkv_batch *b, const int32_t *cascade, int32_t num_c
     p->single_launch = paged_one_launch && p->run_prefix && p->prefix_waves >= 2 && p->prefix_key_halves == 2 &&
                        !p->prefix_split_p;
 
+    // Prefix items as the co-resident launch numbers them: every cascade group
+    // with a prefix, members or not, at the plan's row tiles.
+    p->co_prefix_items = 0;
+    if (p->run_prefix)
+        for (int g = 0; g < ng; ++g) {
+            const int64_t lp = b->host_hot_len[g];
+            if (lp <= 0 || !mask_get(p->cascade, g)) continue;
+            p->co_prefix_items += (int64_t)Hkv * p->prefix_mtiles *
+                                  splits_for(lp, chunk_for(lp, p->prefix_chunk, kPrefixSplitCap, kPrefixKeyTile));
+        }
+
+    {
+        const int per = kFlatWaves / hpb;
+        const int64_t paged_blocks =
+            p->flat.empty() ? 0 : ((int64_t)p->flat[0].blocks * p->flat_head_groups + per - 1) / per;
+        p->co_resident = p->single_launch && p->co_prefix_items <= paged_blocks;
+    }
+
     // Item counts (informational).
     p->flat_items = 0;
     p->prefix_items = 0;
@@ -310,6 +328,7 @@ spkv_status spkv_plan_query(const spkv_batch *batch, const int32_t *cascade, spk
     out->prefix_granule = kPrefixKeyTile;
     out->prefix_key_halves = p.prefix_key_halves;
     out->single_launch = p.single_launch ? 1 : 0;
+    out->co_resident = p.co_resident ? 1 : 0;
     return SPKV_OK;
 }
 

@@ -374,7 +374,17 @@ def _single_launch_cases():
         "one_group_1_head": lambda: W.make_custom(
             batch=41, num_q_heads=4, num_kv_heads=1, head_dim=128, dtype="bf16", group_prefix_len=[900],
             group_of=[0] * 40 + [-1], suffix_len=[int(x) for x in rng.integers(1, 500, 41)], seed=66),
+        # one large group beside seven single-request groups: every group counted at the large one's
+        # 4 row tiles gives more prefix items than paged blocks, so the one launch is not co-resident
+        "uneven_groups_not_co_resident": lambda: W.make_custom(
+            batch=107, num_q_heads=32, num_kv_heads=8, head_dim=128, dtype="bf16",
+            group_prefix_len=[2000, 1800, 2100, 1900, 2200, 1700, 2300, 1600],
+            group_of=[0] * 100 + [1, 2, 3, 4, 5, 6, 7], suffix_len=[int(x) for x in rng.integers(1, 100, 107)],
+            seed=70),
     }
+
+# co_resident of each case's plan (every group on the cascade)
+SINGLE_CO = {name: name != "uneven_groups_not_co_resident" for name in _single_launch_cases()}
 
 
 SINGLE = _single_launch_cases()
@@ -382,17 +392,21 @@ SINGLE = _single_launch_cases()
 
 @pytest.mark.parametrize("name", sorted(SINGLE))
 def test_single_launch_matches_two_launches(name):
-    # paged_prefix_kernel runs the paged pass's ranges and the prefix blocks
-    # of the same plan in one launch: outputs bit-identical to the two
-    # launches, for the decode step and for the step with fused appends (pools,
-    # block tables and lengths too), and both within the bound of the oracle.
+    # paged_prefix_kernel (single_launch = 2) runs the paged pass's ranges and
+    # the prefix blocks of the same plan in one launch: outputs bit-identical
+    # to the two launches (single_launch = 0), for the decode step and for the
+    # step with fused appends (pools, block tables and lengths too), and both
+    # within the bound of the oracle.  The default (single_launch = 1) runs
+    # paged_prefix_co_kernel, both roles side by side in every launch block,
+    # where the plan marks it co-resident, else paged_prefix_kernel.
     note(f"[gpu] single launch {name}")
     wl = SINGLE[name]()
     ref_o, ref_l = decode_reference(wl)
-    states = [setup_single_step(wl, max_blocks=int(wl.suffix_len.max()) + 4) for _ in range(2)]
-    assert int(states[0].batch.plan().single_launch) == 1
+    states = [setup_single_step(wl, max_blocks=int(wl.suffix_len.max()) + 4) for _ in range(3)]
+    info = states[0].batch.plan()
+    assert int(info.single_launch) == 1 and int(info.co_resident) == int(SINGLE_CO[name])
     res = []
-    for one, st in zip((1, 0), states):
+    for one, st in zip((2, 0, 1), states):
         params = R.default_params(A.SPKV_MODE_FORCE_CASCADE)
         params.single_launch = one
         ws = R.workspace(st.batch)
@@ -414,12 +428,26 @@ def test_single_launch_matches_two_launches(name):
         out2, lse2, _ = R.decode_step_append(st.batch, st.pools, params, R.workspace(st.batch), k, v, slots)
         torch.cuda.synchronize()
         res.append((out, lse, out2, lse2))
-    for x, y in zip(*res):
+    for x, y in zip(res[0], res[1]):
         assert torch.equal(x, y)
-    a, b = states
-    for t0, t1 in ((a.pools.k_cold, b.pools.k_cold), (a.pools.v_cold, b.pools.v_cold)):
+    # the co-resident launch runs each prefix item in one key half instead of
+    # two (another online-softmax reference, so other bf16 roundings of the
+    # weights): within the oracle's bound of the two launches; without it the
+    # default is paged_prefix_kernel, bit-identical
+    for x, y in zip(res[2], res[1]):
+        if not SINGLE_CO[name]:
+            assert torch.equal(x, y)
+            continue
+        fin = torch.isfinite(y)
+        assert torch.equal(fin, torch.isfinite(x))
+        assert float((x[fin] - y[fin]).abs().max()) <= TOL_O
+    a, b, c = states
+    for t0, t1, t2 in ((a.pools.k_cold, b.pools.k_cold, c.pools.k_cold),
+                       (a.pools.v_cold, b.pools.v_cold, c.pools.v_cold)):
         np.testing.assert_array_equal(pool_bytes(t0), pool_bytes(t1))
-    assert torch.equal(a.batch.tables, b.batch.tables) and torch.equal(a.batch.lens, b.batch.lens)
+        np.testing.assert_array_equal(pool_bytes(t2), pool_bytes(t1))
+    for st in (a, c):
+        assert torch.equal(st.batch.tables, b.batch.tables) and torch.equal(st.batch.lens, b.batch.lens)
 
 
 def test_prefix_only_requests_and_a_64k_prefix():

@@ -157,6 +157,36 @@ def test_single_launch_only_where_both_plans_keep_their_shapes():
     assert int(R.DecodeBatch(q32, [0] * 64, [0], [16384], tables, lens, 1, 8).plan().single_launch) == 0
 
 
+def test_co_resident_where_the_prefix_items_fit_beside_the_paged_blocks():
+    # The default one launch runs both roles in every launch block where the
+    # prefix items of cascade groups with a prefix, each counted at the plan's
+    # row tiles, number no more than the paged blocks: brute-force count here.
+    def chunk_for(lp, tau, cap, gran):
+        c = max(tau, -(-lp // cap))
+        return -(-c // gran) * gran
+
+    def check(lens, groups, group_len, expect, **kw):
+        bt = batch_of(lens, groups, group_len, **kw)
+        info = bt.plan()
+        hkv = kw.get("hkv", 8)
+        items = sum(hkv * int(info.prefix_mtiles) * -(-lp // chunk_for(lp, int(info.prefix_chunk), 64, 32))
+                    for lp in group_len if lp > 0)
+        per = 4 // min(hkv, 4)
+        paged = -(-int(info.flat_items) // per)
+        assert int(info.co_resident) == int(bool(info.single_launch) and items <= paged) == expect
+
+    check([300] * 64, [0] * 64, [16384], 1)                          # 8B shape, Lp 16K
+    # two paged blocks per launch block: 150 launch blocks for 300 ranges, fewer than 256 prefix items
+    check([300] * 64, [0] * 64, [16384], 0, hkv=2, hq=8)
+    check([300] * 64, [0] * 64, [200], 0)                            # not a single launch at all
+    # one large group and seven single-request groups: every group at the large one's row tiles
+    check([50] * 107, [0] * 100 + list(range(1, 8)), [2000, 1800, 2100, 1900, 2200, 1700, 2300, 1600], 0)
+    # eight groups of 16 (C4 shape): 248 real items in a 6-split x 64 grid, all beside 256 paged blocks
+    rng = np.random.default_rng(3)
+    lens = [int(x) for x in rng.integers(128, 4096, 128)]
+    check(lens, [g for g in range(8) for _ in range(16)], [12134, 14070, 6942, 11971, 5849, 5146, 4709, 3846], 1)
+
+
 def test_two_launches_by_parameter():
     p = R.default_params()
     assert p.single_launch == 1
