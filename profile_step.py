@@ -38,7 +38,7 @@ import sys
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 KERNELS = {"flat_kernel": "flat_paged", "prefix_mfma_kernel": "prefix_mfma", "merge_kernel": "merge",
-           "paged_prefix_kernel": "paged_prefix"}
+           "paged_prefix_kernel": "paged_prefix", "paged_prefix_co_kernel": "paged_prefix"}
 COPY_MIB = 256
 NUM_CUS, SIMDS_PER_CU, NUM_XCC = 256, 4, 8
 # Counter passes: at most 8 SQ and 2 GRBM counters each (one hardware pass).

@@ -368,21 +368,21 @@ void spkv_dispatch_params_default(spkv_dispatch_params *p) {
     // Hkv 8) and 32B-shaped (Hq 10, Hkv 2) layers: prefix length 64 .. 32768
     // at 64 and 256 requests, and 1 .. 256 requests sharing a 4096- or
     // 16384-token prefix.  The flat pass re-reads a shared prefix at ~10 TB/s
-    // (the re-reads are mostly cache hits); the cascade path costs ~3.2 us per
-    // step (the prefix blocks' start-up; they share the paged pass's launch
-    // where the plan allows it) plus ~3.9 ns per query row of the groups that
-    // take it (their partial states, written and merged).  Any fixed cost in
-    // [2.5, 4.0] us picks the faster backend at 51 of the 52 swept points (the
-    // other a tie under 1 us).  The
-    // prefix contraction's own rates matter little near the crossover; they
-    // are those of the kernel at the 8B shape.
+    // (the re-reads are mostly cache hits); the cascade path costs ~7.5 us per
+    // step (the prefix items beside the paged blocks in the co-resident launch,
+    // and the merge's share) plus ~2 ns per query row of the groups that take
+    // it (their partial states, written and merged).  With 2 ns per row, any
+    // fixed cost in [7.0, 8.0] us picks the faster backend at every swept
+    // point whose two times differ by more than 1 us (51 of the 52; the other
+    // differs by 0.3 us).  The prefix contraction's own rates matter little
+    // near the crossover; they are those of the kernel at the 8B shape.
     p->mode = SPKV_MODE_PER_GROUP;
     p->min_group_requests = 2;
-    p->fixed_cost_us = 3.2;
+    p->fixed_cost_us = 7.5;
     p->flat_gbps = 10000.0;
     p->prefix_gbps = 4000.0;
     p->prefix_tflops = 420.0;
-    p->row_cost_ns = 3.9;
+    p->row_cost_ns = 2.0;
     p->single_launch = 1;
 }
 
