@@ -189,7 +189,7 @@ def main():
         kib, _ = max(copy.values(), key=lambda v: v[0])        # the copy kernel: the largest reading
         factors[counter] = (COPY_MIB << 20) / (kib * 1024.0)
     runs = {}
-    for k in KERNELS.values():
+    for k in dict.fromkeys(KERNELS.values()):
         f = readings["FETCH_SIZE"][0].get(k)
         w = readings["WRITE_SIZE"][0].get(k)
         if f is None or w is None:
@@ -245,7 +245,7 @@ def main():
           "LDS bank-conflict share = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE.", "",
           "| kernel | avg us | MFMA busy | bf16 MFMA TFLOP/s | % of peak | VALU insts | LDS insts | "
           "bank-conflict share |", "|---|---|---|---|---|---|---|---|"]
-    for k in KERNELS.values():
+    for k in dict.fromkeys(KERNELS.values()):
         v = sq.get(k)
         if not v:
             continue
@@ -258,7 +258,7 @@ def main():
         cm.append(f"| {k} | {t * 1e6:.2f} | {100 * busy:.1f} % | {tf:.1f} | {100 * tf / 2500:.1f} % | "
                   f"{v.get('SQ_INSTS_VALU', 0):.0f} | {v.get('SQ_INSTS_LDS', 0):.0f} | {100 * bc:.1f} % |")
     cm += ["", "Raw means per dispatch:", "", "| kernel | counter | value |", "|---|---|---|"]
-    for k in KERNELS.values():
+    for k in dict.fromkeys(KERNELS.values()):
         for counter, val in sorted(sq.get(k, {}).items()):
             cm.append(f"| {k} | {counter} | {val:.1f} |")
     cm += ["", "Commands (from /tmp, TMPDIR=/tmp):", "", "```"]
