@@ -452,10 +452,14 @@ typedef struct spkv_plan_info {
                                       paged ranges come first in the grid and the prefix blocks take CUs as
                                       ranges finish */
     int32_t co_resident;           /* 1: that one launch can run both roles in every launch block (four
-                                      paged waves beside the prefix item's waves, LDS rings of three
-                                      stages each): the prefix items of cascade groups with a prefix,
-                                      counted at prefix_mtiles for every group, number no more than the
-                                      paged blocks */
+                                      paged waves beside the prefix item's waves): the prefix items of
+                                      cascade groups with a prefix, counted at prefix_mtiles for every
+                                      group, number no more than the paged blocks */
+    int32_t co_prefix_stages;      /* ring depth of the co-resident launch's prefix waves (tiles of 32
+                                      keys): 3 beside paged rings of 3 stages, or 5 beside paged rings of 2
+                                      when its prefix items (tiles of 4 row waves) hold more key tiles than
+                                      a paged wave's range holds ring stages of 16 tokens; 0 when not
+                                      co-resident */
 } spkv_plan_info;
 
 spkv_status spkv_plan_query(const spkv_batch *batch, const int32_t *cascade, spkv_plan_info *out);

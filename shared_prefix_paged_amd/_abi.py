@@ -50,7 +50,8 @@ class spkv_plan_info(C.Structure):
                 ("prefix_waves", c_i32), ("prefix_mtiles", c_i32), ("flat_items", c_i64),
                 ("prefix_items", c_i64), ("workspace_bytes", c_i64), ("flat_split_cap", c_i32),
                 ("flat_head_tokens", c_i32), ("prefix_split_cap", c_i32), ("prefix_granule", c_i32),
-                ("prefix_key_halves", c_i32), ("single_launch", c_i32), ("co_resident", c_i32)]
+                ("prefix_key_halves", c_i32), ("single_launch", c_i32), ("co_resident", c_i32),
+                ("co_prefix_stages", c_i32)]
 
 
 P_batch, P_kv, P_params = C.POINTER(spkv_batch), C.POINTER(spkv_kv), C.POINTER(spkv_dispatch_params)

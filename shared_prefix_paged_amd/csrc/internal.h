@@ -110,6 +110,7 @@ struct Plan {
     int64_t co_prefix_items;  // prefix items of cascade groups with a prefix (the co-resident launch's count)
     bool co_resident;         // single launch with both roles in every block: its prefix items fit beside
                               // the paged blocks in one round
+    int32_t co_prefix_stages; // co-resident: prefix ring depth, 3 (paged rings of 3) or 5 (paged rings of 2)
 };
 
 // LDS bytes of one wave of the bf16 paged pass: its ring (K and V rows of

@@ -1337,19 +1337,26 @@ __global__ __launch_bounds__(512) void paged_prefix_kernel(Args a, FlatLaunch fl
 }
 
 // The paged pass and the prefix contraction side by side on every CU (bf16,
-// d = 128): launch block b runs paged block b on waves 0..3 (rings of
-// kCoFlatStages stages) and prefix item b on waves 4 .. 4 + PW - 1 (one key
-// half, a ring of kCoPrefixStages tiles).  The prefix waves meet at an LDS
-// counter barrier of their own, so neither role waits for the other: the
-// MFMA-bound contraction runs beside the HBM-bound paged pass instead of
-// after it, with the same arithmetic and partial-state slots.
-constexpr int kCoFlatStages = 3;
-constexpr int kCoPrefixStages = 3;
-constexpr size_t co_flat_bytes() { return (size_t)kFlatWavesMax * FlatMfmaGeom<128, kCoFlatStages>::WAVEB; }
-constexpr size_t co_prefix_bytes() { return (size_t)prefix_ring_bytes<128, 1, kCoPrefixStages>(); }
-constexpr size_t co_lds() { return co_flat_bytes() + co_prefix_bytes() + 4 * kMemberWin * sizeof(int32_t) + 16; }
-static_assert(co_flat_bytes() % 1024 == 0, "the prefix ring starts 1 KB aligned");
-static_assert(co_lds() <= (size_t)spkv::kLdsPerCU, "one co-resident block per CU");
+// d = 128): launch block b runs paged block b on waves 0..3 (rings of FS
+// stages) and prefix item b on waves 4 .. 4 + PW - 1 (one key half, a ring of
+// PS tiles).  The prefix waves meet at an LDS counter barrier of their own,
+// so neither role waits for the other: the MFMA-bound contraction runs beside
+// the HBM-bound paged pass instead of after it, with the same arithmetic and
+// partial-state slots.  Both roles share the memory system, and each gets a
+// share of its bandwidth in proportion to the bytes it keeps in flight, i.e.
+// to its ring depth; the LDS holds FS = PS = 3, or FS = 2 and PS = 5 for
+// plans whose prefix items have more key tiles than the paged waves have
+// ring stages of tokens (the prefix role would finish last).
+template <int FS, int PS>
+constexpr size_t co_flat_bytes() { return (size_t)kFlatWavesMax * FlatMfmaGeom<128, FS>::WAVEB; }
+template <int FS, int PS>
+constexpr size_t co_lds() {
+    return co_flat_bytes<FS, PS>() + prefix_ring_bytes<128, 1, PS>() + 4 * kMemberWin * sizeof(int32_t) + 16;
+}
+static_assert(co_flat_bytes<3, 3>() % 1024 == 0 && co_flat_bytes<2, 5>() % 1024 == 0,
+              "the prefix ring starts 1 KB aligned");
+static_assert(co_lds<3, 3>() <= (size_t)spkv::kLdsPerCU && co_lds<2, 5>() <= (size_t)spkv::kLdsPerCU,
+              "one co-resident block per CU");
 
 // Prefix item r of the co-resident launch, counted over cascade groups with a
 // prefix only (group g holds nsplit_g * pmtiles * Hkv items, nsplit_g from
@@ -1389,14 +1396,14 @@ __device__ __forceinline__ bool co_prefix_item(const Args &a, int r, int pmtiles
     return false;
 }
 
-template <int D, int G, bool APP, bool NT, int PW>
+template <int D, int G, bool APP, bool NT, int PW, int FS, int PS>
 __global__ __launch_bounds__(512) void paged_prefix_co_kernel(Args a, FlatLaunch fl, int paged_blocks,
                                                               int prefix_items, int pmtiles) {
     static_assert(D == 128, "ring layout sized for d = 128");
     extern __shared__ __attribute__((aligned(1024))) char co_smem[];
-    using F = FlatMfmaGeom<D, kCoFlatStages>;
-    char *pring = co_smem + co_flat_bytes();
-    int32_t(*win)[kMemberWin] = (int32_t(*)[kMemberWin])(pring + co_prefix_bytes());
+    using F = FlatMfmaGeom<D, FS>;
+    char *pring = co_smem + co_flat_bytes<FS, PS>();
+    int32_t(*win)[kMemberWin] = (int32_t(*)[kMemberWin])(pring + prefix_ring_bytes<128, 1, PS>());
     uint32_t *bar = (uint32_t *)(win + 4);
     if (threadIdx.x == 0) *bar = 0u;
     __syncthreads();                           // every wave of the block is alive here
@@ -1410,8 +1417,8 @@ __global__ __launch_bounds__(512) void paged_prefix_co_kernel(Args a, FlatLaunch
         const int head_groups = (a.Hkv + hpb - 1) / hpb;
         if (pb >= fl.blocks * head_groups) return;
         const int sub = wave / hpb;
-        flat_block<true, D, G, APP, NT, kCoFlatStages>(a, fl, pb % fl.blocks, pb / fl.blocks, wave - sub * hpb,
-                                                       threadIdx.x & 63, co_smem + sub * hpb * F::WAVEB);
+        flat_block<true, D, G, APP, NT, FS>(a, fl, pb % fl.blocks, pb / fl.blocks, wave - sub * hpb,
+                                            threadIdx.x & 63, co_smem + sub * hpb * F::WAVEB);
         return;
     }
     const int pw = wave - kFlatWavesMax;
@@ -1421,8 +1428,7 @@ __global__ __launch_bounds__(512) void paged_prefix_co_kernel(Args a, FlatLaunch
     s = __builtin_amdgcn_readfirstlane(s);     // wave-uniform already; say so for the scalar DMA bases
     mt = __builtin_amdgcn_readfirstlane(mt);
     gz = __builtin_amdgcn_readfirstlane(gz);
-    prefix_block<D, PW, false, 1, kCoPrefixStages, true>(a, s, mt, gz, __builtin_amdgcn_readfirstlane(pw), pring,
-                                                         win, bar);
+    prefix_block<D, PW, false, 1, PS, true>(a, s, mt, gz, __builtin_amdgcn_readfirstlane(pw), pring, win, bar);
 }
 
 // ---------------------------------------------------------------------------
@@ -2058,10 +2064,10 @@ spkv_status launch_paged_prefix_g(const Args &a, const Plan &p, bool app, TimedL
     return p.prefix_waves == 4 ? launch_paged_prefix_w<G, 4>(a, p, app, tl) : launch_paged_prefix_w<G, 2>(a, p, app, tl);
 }
 
-template <int G, bool APP, bool NT, int PW>
+template <int G, bool APP, bool NT, int PW, int FS, int PS>
 spkv_status launch_paged_prefix_co_k(const Args &a, const Plan &p, TimedLaunch &tl) {
     constexpr int D = 128;
-    static const hipError_t attr = hipFuncSetAttribute((const void *)paged_prefix_co_kernel<D, G, APP, NT, PW>,
+    static const hipError_t attr = hipFuncSetAttribute((const void *)paged_prefix_co_kernel<D, G, APP, NT, PW, FS, PS>,
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, spkv::kLdsPerCU);
     if (attr != hipSuccess)
         return fail(SPKV_E_HIP, std::string("paged_prefix_co_kernel LDS limit: ") + hipGetErrorString(attr));
@@ -2073,23 +2079,26 @@ spkv_status launch_paged_prefix_co_k(const Args &a, const Plan &p, TimedLaunch &
     if (paged >= ((int64_t)1 << 31) || prefix >= ((int64_t)1 << 31))
         return fail(SPKV_E_INVAL, "paged_prefix_co_kernel: grid too large");
     dim3 grid((unsigned)std::max(paged, prefix)), block(512);
-    tl.launch(paged_prefix_co_kernel<D, G, APP, NT, PW>, grid, block, co_lds(), a, f, (int)paged, (int)prefix,
-              p.prefix_mtiles);
+    tl.launch(paged_prefix_co_kernel<D, G, APP, NT, PW, FS, PS>, grid, block, co_lds<FS, PS>(), a, f, (int)paged,
+              (int)prefix, p.prefix_mtiles);
     return check_launch("paged_prefix_co_kernel");
 }
 
-template <int G, int PW>
+template <int G, int PW, int FS, int PS>
 spkv_status launch_paged_prefix_co_w(const Args &a, const Plan &p, bool app, TimedLaunch &tl) {
-    if (app) return a.cold_nt ? launch_paged_prefix_co_k<G, true, true, PW>(a, p, tl)
-                              : launch_paged_prefix_co_k<G, true, false, PW>(a, p, tl);
-    return a.cold_nt ? launch_paged_prefix_co_k<G, false, true, PW>(a, p, tl)
-                     : launch_paged_prefix_co_k<G, false, false, PW>(a, p, tl);
+    if (app) return a.cold_nt ? launch_paged_prefix_co_k<G, true, true, PW, FS, PS>(a, p, tl)
+                              : launch_paged_prefix_co_k<G, true, false, PW, FS, PS>(a, p, tl);
+    return a.cold_nt ? launch_paged_prefix_co_k<G, false, true, PW, FS, PS>(a, p, tl)
+                     : launch_paged_prefix_co_k<G, false, false, PW, FS, PS>(a, p, tl);
 }
 
+// The deep prefix ring (FS = 2, PS = 5) for tiles of 4 row waves only, the
+// shape whose contraction can outlast the paged pass.
 template <int G>
 spkv_status launch_paged_prefix_co_g(const Args &a, const Plan &p, bool app, TimedLaunch &tl) {
-    return p.prefix_waves == 4 ? launch_paged_prefix_co_w<G, 4>(a, p, app, tl)
-                               : launch_paged_prefix_co_w<G, 2>(a, p, app, tl);
+    if (p.prefix_waves != 4) return launch_paged_prefix_co_w<G, 2, 3, 3>(a, p, app, tl);
+    return p.co_prefix_stages == 5 ? launch_paged_prefix_co_w<G, 4, 2, 5>(a, p, app, tl)
+                                   : launch_paged_prefix_co_w<G, 4, 3, 3>(a, p, app, tl);
 }
 
 spkv_status launch_paged_prefix_co(const Args &a, const Plan &p, bool app, hipStream_t st) {

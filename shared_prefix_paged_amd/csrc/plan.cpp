@@ -259,6 +259,19 @@ spkv_status make_plan(const spkv_batch *b, const int32_t *cascade, int32_t num_c
             p->flat.empty() ? 0 : ((int64_t)p->flat[0].blocks * p->flat_head_groups + per - 1) / per;
         p->co_resident = p->single_launch && p->co_prefix_items <= paged_blocks;
     }
+    // Ring depths of the co-resident launch.  Each role's share of the memory
+    // bandwidth follows the bytes it keeps in flight; the deeper prefix ring
+    // (and shallower paged rings) pays where the prefix items' key tiles
+    // outnumber the ring stages of a paged wave's range, i.e. where the
+    // prefix role would otherwise finish last.
+    p->co_prefix_stages = 0;
+    if (p->co_resident) {
+        const int64_t item_tiles = (std::min<int64_t>(max_lp_c, chunk_for(max_lp_c, p->prefix_chunk, kPrefixSplitCap,
+                                                                          kPrefixKeyTile)) +
+                                    kPrefixKeyTile - 1) / kPrefixKeyTile;
+        const int64_t paged_stages = (p->flat_chunk + kFlatMfmaTokens - 1) / kFlatMfmaTokens;
+        p->co_prefix_stages = p->prefix_waves == 4 && item_tiles > paged_stages ? 5 : 3;
+    }
 
     // Item counts (informational).
     p->flat_items = 0;
@@ -329,6 +342,7 @@ spkv_status spkv_plan_query(const spkv_batch *batch, const int32_t *cascade, spk
     out->prefix_key_halves = p.prefix_key_halves;
     out->single_launch = p.single_launch ? 1 : 0;
     out->co_resident = p.co_resident ? 1 : 0;
+    out->co_prefix_stages = p.co_prefix_stages;
     return SPKV_OK;
 }
 

@@ -187,6 +187,36 @@ def test_co_resident_where_the_prefix_items_fit_beside_the_paged_blocks():
     check(lens, [g for g in range(8) for _ in range(16)], [12134, 14070, 6942, 11971, 5849, 5146, 4709, 3846], 1)
 
 
+def test_co_resident_ring_depths():
+    # The co-resident launch deepens the prefix ring (5 tiles beside paged
+    # rings of 2 stages) where a prefix item's key tiles outnumber the 16-token
+    # ring stages of a paged wave's range, for tiles of 4 row waves; else 3
+    # and 3.  The configurations' shapes, with the counts recomputed here.
+    rng = np.random.default_rng(5)
+
+    def check(lens, groups, group_len, expect, **kw):
+        info = batch_of(lens, groups, group_len, **kw).plan()
+        assert int(info.co_resident) == 1
+        lp = max(group_len)
+        chunk = max(int(info.prefix_chunk), -(-lp // 64))
+        chunk = -(-chunk // 32) * 32
+        tiles = -(-min(lp, chunk) // 32)
+        stages = -(-int(info.flat_chunk) // 16)
+        deep = int(info.prefix_waves) == 4 and tiles > stages
+        assert int(info.co_prefix_stages) == (5 if deep else 3) == expect
+
+    # 8B shape, 64 requests, Lp 16K: 32 tiles per item, ~44 stages per paged range
+    check([int(x) for x in rng.integers(256, 2049, 64)], [0] * 64, [16384], 3)
+    # 32B-shaped share, 256 requests: 43 tiles per item, ~36 stages per paged range
+    check([int(x) for x in rng.integers(128, 2049, 256)], [0] * 256, [16384], 5, hkv=2, hq=10)
+    # 14B-shaped share, 128 requests: 43 tiles, ~68 stages
+    check([int(x) for x in rng.integers(128, 4097, 128)], [0] * 128, [16384], 3, hkv=4, hq=20)
+    # eight groups of 16 (tiles of 2 row waves): always 3
+    lens = [int(x) for x in rng.integers(128, 4097, 128)]
+    check(lens, [g for g in range(8) for _ in range(16)], [12134, 14070, 6942, 11971, 5849, 5146, 4709, 3846], 3)
+    assert int(batch_of([300] * 64, [0] * 64, [200]).plan().co_prefix_stages) == 0   # not co-resident
+
+
 def test_two_launches_by_parameter():
     p = R.default_params()
     assert p.single_launch == 1
