@@ -949,7 +949,7 @@ __device__ __forceinline__ void waves_barrier(uint32_t *ctr, uint32_t target) {
 // waves of another role, so the prefix waves meet at waves_barrier on the
 // LDS counter `bar` instead of the block-wide hardware barrier (one key half
 // only).
-template <int D, int W, bool SPLIT_P, int KH, int STAGES = kPrefixStages, bool SWB = false>
+template <int D, int W, bool SPLIT_P, int KH, int STAGES = kPrefixStages, bool SWB = false, bool PIPE = false>
 __device__ __forceinline__ void prefix_block(const Args &a, const int s, const int mt, const int gz,
                                              const int wave_id, char *smem, int32_t (*member_win)[kMemberWin],
                                              uint32_t *bar = nullptr) {
@@ -1146,100 +1146,140 @@ __device__ __forceinline__ void prefix_block(const Args &a, const int s, const i
     const lds_char_t *lsm = (const lds_char_t *)(smem + khalf * STAGES * 2 * TILEB);
     constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;   // (1.0, 1.0) in bf16
 
-    // Tile t sits in stage t % STAGES; the stage loop is unrolled so that all
-    // LDS addresses are a per-lane offset plus an immediate.
-    for (int t0 = 0; t0 < nt_loop; t0 += STAGES) {
+    // One tile's scores S^T = K . Q^T from ring stage st (tile t of the range).
+    auto scores = [&](int st, int t) {
+        const lds_char_t *ks = lsm + st * 2 * TILEB;
+        const int kt = k0 + t * NT;
+        f32x16_t sacc;
 #pragma unroll
-        for (int st = 0; st < STAGES; ++st) {
-            const int t = t0 + st;
-            if (t >= nt_loop) break;
-            const bool act = t < ntiles;   // this half still has tile t
-            if (act) {
-                if (t + STAGES - 2 < ntiles) wait_vmcnt<AHEAD>();
-                else wait_vmcnt<0>();
-            }
-            if constexpr (SWB) {
-                waves_barrier(bar, (uint32_t)W * ++bar_k);
+        for (int j = 0; j < 16; ++j) sacc[j] = 0.f;
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+            const bf16x8_t af = *(const bf16x8_t __attribute__((address_space(3))) *)(ks + kofs[k]);
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[k], sacc, 0, 0, 0);
+        }
+        if (kt + NT > k1) {   // last tile of the range: mask keys past its end
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                if (kt + 16 * (j >> 3) + 8 * half + (j & 7) >= k1) sacc[j] = -INFINITY;
+        }
+        return sacc;
+    };
+    // The online softmax of one tile's scores and O^T += V^T . P^T with the
+    // tile's V from ring stage st.
+    auto accumulate = [&](f32x16_t &sacc, int st) {
+        const lds_char_t *vs = lsm + st * 2 * TILEB + TILEB;
+        // Online softmax along keys (one query row per lane, two lane halves).
+        float mx = fmaxf(fmaxf(sacc[0], sacc[1]), sacc[2]);
+#pragma unroll
+        for (int j = 3; j < 16; j += 2) mx = fmaxf(fmaxf(mx, sacc[j]), sacc[j + 1 < 16 ? j + 1 : j]);
+        mx = max_of_halves(mx) * c2;
+        const bool grow = mx > m_run + kRescaleSlack;
+        if (__any(grow)) {
+            const float mnew = grow ? mx : m_run;
+            const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
+            m_run = mnew;
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
+        }
+        const float nm = -m_run;
+        uint32_t pk[8], pl[8];
+#pragma unroll
+        for (int j = 0; j < 16; j += 2) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[j], c2, nm));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[j + 1], c2, nm));
+            bf16x2_t pp = {(__bf16)p0, (__bf16)p1};   // round to nearest even
+            const uint32_t w = __builtin_bit_cast(uint32_t, pp);
+            pk[j >> 1] = w;
+            if constexpr (SPLIT_P) {
+                bf16x2_t ll = {(__bf16)(p0 - bf16lo(w)), (__bf16)(p1 - bf16hi(w))};
+                pl[j >> 1] = __builtin_bit_cast(uint32_t, ll);
+                l_run += p0 + p1;
             } else {
-                __builtin_amdgcn_s_barrier();  // tile t visible; every wave is done with tile t-1
-                asm volatile("" ::: "memory");
+                // Normalise by the weights the MFMA actually uses, so the
+                // output stays a convex combination of V rows.
+                l_run = fdot2(w, kOnesBf16x2, l_run);
             }
-            if (!act) continue;
-            if (t + STAGES - 1 < ntiles) issue(t + STAGES - 1, (st + STAGES - 1) % STAGES);
+        }
 
-            const lds_char_t *ks = lsm + st * 2 * TILEB;
-            const lds_char_t *vs = ks + TILEB;
-            const int kt = k0 + t * NT;
+        // O^T += V^T . P^T, two 16-key steps; V^T operands by transposing reads.
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const u32x4_t pb = {pk[4 * kb + 0], pk[4 * kb + 1], pk[4 * kb + 2], pk[4 * kb + 3]};
+            const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pb);
+            const u32x4_t plb = {pl[4 * kb + 0], pl[4 * kb + 1], pl[4 * kb + 2], pl[4 * kb + 3]};
+            const bf16x8_t pfl = __builtin_bit_cast(bf16x8_t, plb);
+            const lds_char_t *vk = vs + kb * 16 * ROWB;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                typedef v4i16_t __attribute__((address_space(3))) *lds_v4i16_ptr;
+                const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(vk + vofs[db]));
+                const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(vk + 4 * ROWB + vofs[db]));
+                const u32x4_t w = {__builtin_bit_cast(u32x2_t, lo).x, __builtin_bit_cast(u32x2_t, lo).y,
+                                   __builtin_bit_cast(u32x2_t, hi).x, __builtin_bit_cast(u32x2_t, hi).y};
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w), pf, oacc[db], 0, 0, 0);
+                if constexpr (SPLIT_P)
+                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w), pfl, oacc[db], 0, 0, 0);
+            }
+        }
+    };
 
-            // S^T = K . Q^T
-            f32x16_t sacc;
+    if constexpr (PIPE) {
+        // Software-pipelined: the scores of tile t + 1 are computed before the
+        // softmax and P.V of tile t, so one wave's matrix-core work overlaps
+        // its own VALU work (one prefix wave per SIMD beside the paged pass).
+        // At step t the wave needs tile t + 1 landed (one tile less in
+        // flight), and the stage freed at step t still held tile t - 1.
+        static_assert(PIPE == false || (KH == 1 && SWB && STAGES >= 4), "pipelined: one key half, deep ring");
+        if (ntiles > STAGES - 2) wait_vmcnt<(STAGES - 2) * 2 * IPW>();   // tile 0; tiles 1 .. STAGES-2 in flight
+        else wait_vmcnt<0>();
+        waves_barrier(bar, (uint32_t)W * ++bar_k);
+        f32x16_t s_cur = scores(0, 0);
+        for (int t0 = 0; t0 < ntiles; t0 += STAGES) {
 #pragma unroll
-            for (int j = 0; j < 16; ++j) sacc[j] = 0.f;
-#pragma unroll
-            for (int k = 0; k < KS; ++k) {
-                const bf16x8_t af = *(const bf16x8_t __attribute__((address_space(3))) *)(ks + kofs[k]);
-                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[k], sacc, 0, 0, 0);
+            for (int st = 0; st < STAGES; ++st) {
+                const int t = t0 + st;
+                if (t >= ntiles) break;
+                const bool more = t + 1 < ntiles;
+                f32x16_t s_nxt = s_cur;
+                if (more) {
+                    // tile t + 1; tiles t + 2 .. t + STAGES - 2 issued after it
+                    if (t + STAGES - 2 < ntiles) wait_vmcnt<(STAGES - 3) * 2 * IPW>();
+                    else wait_vmcnt<0>();
+                    waves_barrier(bar, (uint32_t)W * ++bar_k);   // every wave is done with tile t - 1
+                    if (t + STAGES - 1 < ntiles) issue(t + STAGES - 1, (st + STAGES - 1) % STAGES);
+                    s_nxt = scores((st + 1) % STAGES, t + 1);
+                }
+                accumulate(s_cur, st);
+                s_cur = s_nxt;
             }
-            if (kt + NT > k1) {   // last tile of the range: mask keys past its end
+        }
+    } else {
+        // Tile t sits in stage t % STAGES; the stage loop is unrolled so that all
+        // LDS addresses are a per-lane offset plus an immediate.
+        for (int t0 = 0; t0 < nt_loop; t0 += STAGES) {
 #pragma unroll
-                for (int j = 0; j < 16; ++j)
-                    if (kt + 16 * (j >> 3) + 8 * half + (j & 7) >= k1) sacc[j] = -INFINITY;
-            }
-            // Online softmax along keys (one query row per lane, two lane halves).
-            float mx = fmaxf(fmaxf(sacc[0], sacc[1]), sacc[2]);
-#pragma unroll
-            for (int j = 3; j < 16; j += 2) mx = fmaxf(fmaxf(mx, sacc[j]), sacc[j + 1 < 16 ? j + 1 : j]);
-            mx = max_of_halves(mx) * c2;
-            const bool grow = mx > m_run + kRescaleSlack;
-            if (__any(grow)) {
-                const float mnew = grow ? mx : m_run;
-                const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
-                m_run = mnew;
-                l_run *= alpha;
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
-            }
-            const float nm = -m_run;
-            uint32_t pk[8], pl[8];
-#pragma unroll
-            for (int j = 0; j < 16; j += 2) {
-                const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[j], c2, nm));
-                const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[j + 1], c2, nm));
-                bf16x2_t pp = {(__bf16)p0, (__bf16)p1};   // round to nearest even
-                const uint32_t w = __builtin_bit_cast(uint32_t, pp);
-                pk[j >> 1] = w;
-                if constexpr (SPLIT_P) {
-                    bf16x2_t ll = {(__bf16)(p0 - bf16lo(w)), (__bf16)(p1 - bf16hi(w))};
-                    pl[j >> 1] = __builtin_bit_cast(uint32_t, ll);
-                    l_run += p0 + p1;
+            for (int st = 0; st < STAGES; ++st) {
+                const int t = t0 + st;
+                if (t >= nt_loop) break;
+                const bool act = t < ntiles;   // this half still has tile t
+                if (act) {
+                    if (t + STAGES - 2 < ntiles) wait_vmcnt<AHEAD>();
+                    else wait_vmcnt<0>();
+                }
+                if constexpr (SWB) {
+                    waves_barrier(bar, (uint32_t)W * ++bar_k);
                 } else {
-                    // Normalise by the weights the MFMA actually uses, so the
-                    // output stays a convex combination of V rows.
-                    l_run = fdot2(w, kOnesBf16x2, l_run);
+                    __builtin_amdgcn_s_barrier();  // tile t visible; every wave is done with tile t-1
+                    asm volatile("" ::: "memory");
                 }
-            }
-
-            // O^T += V^T . P^T, two 16-key steps; V^T operands by transposing reads.
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const u32x4_t pb = {pk[4 * kb + 0], pk[4 * kb + 1], pk[4 * kb + 2], pk[4 * kb + 3]};
-                const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pb);
-                const u32x4_t plb = {pl[4 * kb + 0], pl[4 * kb + 1], pl[4 * kb + 2], pl[4 * kb + 3]};
-                const bf16x8_t pfl = __builtin_bit_cast(bf16x8_t, plb);
-                const lds_char_t *vk = vs + kb * 16 * ROWB;
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    typedef v4i16_t __attribute__((address_space(3))) *lds_v4i16_ptr;
-                    const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(vk + vofs[db]));
-                    const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(vk + 4 * ROWB + vofs[db]));
-                    const u32x4_t w = {__builtin_bit_cast(u32x2_t, lo).x, __builtin_bit_cast(u32x2_t, lo).y,
-                                       __builtin_bit_cast(u32x2_t, hi).x, __builtin_bit_cast(u32x2_t, hi).y};
-                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w), pf, oacc[db], 0, 0, 0);
-                    if constexpr (SPLIT_P)
-                        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w), pfl, oacc[db], 0, 0, 0);
-                }
+                if (!act) continue;
+                if (t + STAGES - 1 < ntiles) issue(t + STAGES - 1, (st + STAGES - 1) % STAGES);
+                f32x16_t sacc = scores(st, t);
+                accumulate(sacc, st);
             }
         }
     }
@@ -1428,7 +1468,8 @@ __global__ __launch_bounds__(512) void paged_prefix_co_kernel(Args a, FlatLaunch
     s = __builtin_amdgcn_readfirstlane(s);     // wave-uniform already; say so for the scalar DMA bases
     mt = __builtin_amdgcn_readfirstlane(mt);
     gz = __builtin_amdgcn_readfirstlane(gz);
-    prefix_block<D, PW, false, 1, PS, true>(a, s, mt, gz, __builtin_amdgcn_readfirstlane(pw), pring, win, bar);
+    prefix_block<D, PW, false, 1, PS, true, (PS >= 5)>(a, s, mt, gz, __builtin_amdgcn_readfirstlane(pw), pring, win,
+                                                       bar);
 }
 
 // ---------------------------------------------------------------------------
