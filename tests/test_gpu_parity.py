@@ -374,6 +374,12 @@ def _single_launch_cases():
         "one_group_1_head": lambda: W.make_custom(
             batch=41, num_q_heads=4, num_kv_heads=1, head_dim=128, dtype="bf16", group_prefix_len=[900],
             group_of=[0] * 40 + [-1], suffix_len=[int(x) for x in rng.integers(1, 500, 41)], seed=66),
+        # the deep, pipelined prefix ring with items of 1, 2 and 3 key tiles (the last chunks of
+        # 513-, 576- and 608-key prefixes) beside 8-tile items
+        "deep_ring_short_items": lambda: W.make_custom(
+            batch=36, num_q_heads=64, num_kv_heads=8, head_dim=128, dtype="bf16", group_prefix_len=[513, 576, 608],
+            group_of=[0] * 12 + [1] * 12 + [2] * 12, suffix_len=[int(x) for x in rng.integers(40, 89, 36)],
+            seed=71),
         # one large group beside seven single-request groups: every group counted at the large one's
         # 4 row tiles gives more prefix items than paged blocks, so the one launch is not co-resident
         "uneven_groups_not_co_resident": lambda: W.make_custom(
@@ -405,6 +411,8 @@ def test_single_launch_matches_two_launches(name):
     states = [setup_single_step(wl, max_blocks=int(wl.suffix_len.max()) + 4) for _ in range(3)]
     info = states[0].batch.plan()
     assert int(info.single_launch) == 1 and int(info.co_resident) == int(SINGLE_CO[name])
+    if name == "deep_ring_short_items":
+        assert int(info.co_prefix_stages) == 5   # the pipelined prefix loop
     res = []
     for one, st in zip((2, 0, 1), states):
         params = R.default_params(A.SPKV_MODE_FORCE_CASCADE)
