@@ -1146,29 +1146,32 @@ __device__ __forceinline__ void prefix_block(const Args &a, const int s, const i
     const lds_char_t *lsm = (const lds_char_t *)(smem + khalf * STAGES * 2 * TILEB);
     constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;   // (1.0, 1.0) in bf16
 
-    // One tile's scores S^T = K . Q^T from ring stage st (tile t of the range).
-    auto scores = [&](int st, int t) {
+    // One tile step, in parts: the K fragments of a tile from ring stage st;
+    // its scores S^T = K . Q^T; the keys past the range masked; the online
+    // softmax's reference update and O rescale; the weights P (bf16, and the
+    // low parts for SPLIT_P); O^T += V^T . P^T with V from stage st.
+    auto k_frags = [&](int st, bf16x8_t (&kf)[KS]) {
         const lds_char_t *ks = lsm + st * 2 * TILEB;
-        const int kt = k0 + t * NT;
+#pragma unroll
+        for (int k = 0; k < KS; ++k) kf[k] = *(const bf16x8_t __attribute__((address_space(3))) *)(ks + kofs[k]);
+    };
+    auto qk = [&](const bf16x8_t (&kf)[KS]) {
         f32x16_t sacc;
 #pragma unroll
         for (int j = 0; j < 16; ++j) sacc[j] = 0.f;
 #pragma unroll
-        for (int k = 0; k < KS; ++k) {
-            const bf16x8_t af = *(const bf16x8_t __attribute__((address_space(3))) *)(ks + kofs[k]);
-            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[k], sacc, 0, 0, 0);
-        }
+        for (int k = 0; k < KS; ++k) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[k], qf[k], sacc, 0, 0, 0);
+        return sacc;
+    };
+    auto mask_tail = [&](f32x16_t &sacc, int t) {
+        const int kt = k0 + t * NT;
         if (kt + NT > k1) {   // last tile of the range: mask keys past its end
 #pragma unroll
             for (int j = 0; j < 16; ++j)
                 if (kt + 16 * (j >> 3) + 8 * half + (j & 7) >= k1) sacc[j] = -INFINITY;
         }
-        return sacc;
     };
-    // The online softmax of one tile's scores and O^T += V^T . P^T with the
-    // tile's V from ring stage st.
-    auto accumulate = [&](f32x16_t &sacc, int st) {
-        const lds_char_t *vs = lsm + st * 2 * TILEB + TILEB;
+    auto rescale = [&](const f32x16_t &sacc) {
         // Online softmax along keys (one query row per lane, two lane halves).
         float mx = fmaxf(fmaxf(sacc[0], sacc[1]), sacc[2]);
 #pragma unroll
@@ -1185,8 +1188,9 @@ __device__ __forceinline__ void prefix_block(const Args &a, const int s, const i
 #pragma unroll
                 for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
         }
+    };
+    auto probs = [&](const f32x16_t &sacc, uint32_t (&pk)[8], uint32_t (&pl)[8]) {
         const float nm = -m_run;
-        uint32_t pk[8], pl[8];
 #pragma unroll
         for (int j = 0; j < 16; j += 2) {
             const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[j], c2, nm));
@@ -1204,7 +1208,9 @@ __device__ __forceinline__ void prefix_block(const Args &a, const int s, const i
                 l_run = fdot2(w, kOnesBf16x2, l_run);
             }
         }
-
+    };
+    auto pv = [&](const uint32_t (&pk)[8], const uint32_t (&pl)[8], int st) {
+        const lds_char_t *vs = lsm + st * 2 * TILEB + TILEB;
         // O^T += V^T . P^T, two 16-key steps; V^T operands by transposing reads.
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -1226,34 +1232,62 @@ __device__ __forceinline__ void prefix_block(const Args &a, const int s, const i
             }
         }
     };
+    auto scores = [&](int st, int t) {
+        bf16x8_t kf[KS];
+        k_frags(st, kf);
+        f32x16_t sacc = qk(kf);
+        mask_tail(sacc, t);
+        return sacc;
+    };
 
     if constexpr (PIPE) {
-        // Software-pipelined: the scores of tile t + 1 are computed before the
-        // softmax and P.V of tile t, so one wave's matrix-core work overlaps
-        // its own VALU work (one prefix wave per SIMD beside the paged pass).
-        // At step t the wave needs tile t + 1 landed (one tile less in
-        // flight), and the stage freed at step t still held tile t - 1.
+        // Software-pipelined: tile t + 1's QK^T MFMAs are interleaved with
+        // tile t's softmax weights (VALU and transcendental), so one wave's
+        // matrix-core work overlaps its own VALU work (one prefix wave per SIMD
+        // beside the paged pass).  At step t the wave needs tile t + 1 landed
+        // (one tile less in flight), and the stage freed at step t still held
+        // tile t - 1.  On the last step the K fragments come from a stage no
+        // DMA writes any more and their scores are dropped.  A tile's keys
+        // past the range are masked at the start of its own step.
         static_assert(PIPE == false || (KH == 1 && SWB && STAGES >= 4), "pipelined: one key half, deep ring");
         if (ntiles > STAGES - 2) wait_vmcnt<(STAGES - 2) * 2 * IPW>();   // tile 0; tiles 1 .. STAGES-2 in flight
         else wait_vmcnt<0>();
         waves_barrier(bar, (uint32_t)W * ++bar_k);
-        f32x16_t s_cur = scores(0, 0);
+        f32x16_t s_cur;
+        {
+            bf16x8_t kf[KS];
+            k_frags(0, kf);
+            s_cur = qk(kf);               // masked at step 0
+        }
         for (int t0 = 0; t0 < ntiles; t0 += STAGES) {
 #pragma unroll
             for (int st = 0; st < STAGES; ++st) {
                 const int t = t0 + st;
                 if (t >= ntiles) break;
                 const bool more = t + 1 < ntiles;
-                f32x16_t s_nxt = s_cur;
                 if (more) {
                     // tile t + 1; tiles t + 2 .. t + STAGES - 2 issued after it
                     if (t + STAGES - 2 < ntiles) wait_vmcnt<(STAGES - 3) * 2 * IPW>();
                     else wait_vmcnt<0>();
                     waves_barrier(bar, (uint32_t)W * ++bar_k);   // every wave is done with tile t - 1
                     if (t + STAGES - 1 < ntiles) issue(t + STAGES - 1, (st + STAGES - 1) % STAGES);
-                    s_nxt = scores((st + 1) % STAGES, t + 1);
                 }
-                accumulate(s_cur, st);
+                bf16x8_t kf[KS];
+                k_frags((st + 1) % STAGES, kf);
+                // Branches (uniform) first, so that tile t's weights and tile
+                // t + 1's MFMAs share one scheduling region.
+                mask_tail(s_cur, t);
+                rescale(s_cur);
+                uint32_t pk[8], pl[8];
+                probs(s_cur, pk, pl);
+                f32x16_t s_nxt = qk(kf);
+                // one MFMA of tile t + 1, then a few VALU of tile t's weights
+#pragma unroll
+                for (int k = 0; k < KS; ++k) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                }
+                pv(pk, pl, st);
                 s_cur = s_nxt;
             }
         }
@@ -1279,7 +1313,10 @@ __device__ __forceinline__ void prefix_block(const Args &a, const int s, const i
                 if (!act) continue;
                 if (t + STAGES - 1 < ntiles) issue(t + STAGES - 1, (st + STAGES - 1) % STAGES);
                 f32x16_t sacc = scores(st, t);
-                accumulate(sacc, st);
+                rescale(sacc);
+                uint32_t pk[8], pl[8];
+                probs(sacc, pk, pl);
+                pv(pk, pl, st);
             }
         }
     }
