@@ -104,7 +104,7 @@ def layout_profile(a, prof_dir):
                        [bench, "--layout-study", "--layout-variant", v, "--steps", "3", "--cold-runs", "0"], limit=240)
         cmds.append(c)
         m = counter_means(f, "FETCH_SIZE")
-        per_step = sum(m[k][0] for k in KERNELS.values() if k in m) * 1024 * factor
+        per_step = sum(m[k][0] for k in dict.fromkeys(KERNELS.values()) if k in m) * 1024 * factor
         rows.append((v, rec, per_step))
     rel = lambda c: " ".join(os.path.relpath(x, ROOT) if x.startswith(ROOT) else x for x in c)
     md = ["# Prefix storage layout in isolation", "",
