@@ -1688,6 +1688,13 @@ __global__ __launch_bounds__(256) void prefix_f32_kernel(Args a) {
 // lengths has finished by now (same stream), so extra blocks copy each
 // request's K/V rows into its slot and advance its block table and length,
 // as spkv_append_tokens does.
+// Kernel arguments are limited to 4 KB; the by-value tables are sized so the
+// largest argument lists (the merge's, the paged launches') stay within it.
+struct MergeKernargs { Args a; float *out, *lse; FlatLaunch fr; MergeRows ap; };
+struct PagedKernargs { Args a; FlatLaunch fl; int x, y, z; };
+static_assert(sizeof(MergeKernargs) <= 4096, "merge kernel arguments exceed 4 KB");
+static_assert(sizeof(PagedKernargs) <= 4096, "paged-pass kernel arguments exceed 4 KB");
+
 template <int D, bool APPEND = false>
 __global__ __launch_bounds__(256) void merge_kernel(Args a, float *out, float *lse_out, FlatLaunch fr,
                                                     MergeRows ap) {
@@ -1912,6 +1919,7 @@ struct AppendArgs {
     int32_t slots[kAppendArgTokens];
     int32_t rows[kAppendArgTokens];
 };
+static_assert(sizeof(AppendArgs) + 10 * sizeof(void *) <= 4096, "append kernel arguments exceed 4 KB");
 
 __global__ __launch_bounds__(256) void append_tokens_kernel(const u32x4_t *knew, const u32x4_t *vnew, AppendArgs aa,
                                                             u32x4_t *kcold, u32x4_t *vcold, int64_t cold_slots,
