@@ -1679,9 +1679,9 @@ __global__ __launch_bounds__(256) void prefix_f32_kernel(Args a) {
 
 // ---------------------------------------------------------------------------
 // Merge of a row's partial states (Eq. (1) applied across all partials).
-// One wave per (request, query head) row; four rows per block.  Lane k first
-// holds partial k's weight exp2(lse_k - max); then each wave-wide load brings
-// PPW partial rows (LPP lanes x 16 bytes each), several loads in flight.
+// One wave per (request, query head) row; four rows per block.  Each
+// wave-wide load brings PPW partial rows (LPP lanes x 16 bytes each), several
+// loads in flight; every lane keeps an online merge of the partials it reads.
 // ---------------------------------------------------------------------------
 // APPEND: the merge launch also lands the step's new tokens, which the paged
 // pass read from k_new / v_new: every reader of the pools, block tables and
@@ -1759,65 +1759,73 @@ __global__ __launch_bounds__(256) void merge_kernel(Args a, float *out, float *l
         return (const f32x4v_t *)(prow_base + (uint32_t)(slot_of(k) * (D * 4) + sub * 16));
     };
 
-    // Issue the weights' loads and the first batch of partial rows together:
-    // a row costs about one memory round trip, not one per few partials.
-    // Loads past the last partial re-read partial 0 (in bounds; weight 0), so
-    // a batch is straight-line code with a single wait; rows with few partials
-    // take a smaller batch.  (Non-temporal: partial states are read once, and
-    // must not displace K/V lines the next step reads again.)
-    const float l0 = lane < n ? a.lse_part[prow0 + slot_of(lane)] : -INFINITY;
-    const float l1 = lane + 64 < n ? a.lse_part[prow0 + slot_of(lane + 64)] : -INFINITY;
+    // Each lane reads the log-sum-exp of the partials whose rows it reads, so
+    // its weights need no cross-lane step: a batch is one round of loads (the
+    // partial rows and their log-sum-exps together), a running maximum per
+    // lane, and FMAs; the LPP-lane groups that read different partials merge
+    // their states once at the end (Eq. (1) between lanes).  Loads past the
+    // last partial re-read partial 0 (in bounds; weight 0), so a batch is
+    // straight-line code with a single wait; rows with few partials take a
+    // smaller batch.  (Non-temporal: partial states are read once, and must
+    // not displace K/V lines the next step reads again.)
+    const float *lrow = a.lse_part + prow0;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     float mx = -INFINITY, wsum = 0.f;
     auto run = [&](auto nb_tag) {
         constexpr int NB = decltype(nb_tag)::value;
         f32x4v_t v[NB];
-#pragma unroll
-        for (int u = 0; u < NB; ++u) {
-            const int k = u * PPW + which;
-            v[u] = __builtin_nontemporal_load(part_ptr(k < n ? k : 0));
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        // Weights: lane k holds partials k and k + 64.
-        mx = fmaxf(l0, l1);
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-        const float muse = mx == -INFINITY ? 0.f : mx;
-        const float w0 = exp2f(l0 - muse), w1 = exp2f(l1 - muse);
-        wsum = w0 + w1;
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) wsum += __shfl_xor(wsum, off, 64);
-        auto weight = [&](int k) {
-            const int kk = k < n ? k : 0;
-            const float wa = __shfl(w0, kk & 63, 64), wb = __shfl(w1, kk & 63, 64);
-            return k < n ? (kk < 64 ? wa : wb) : 0.f;
-        };
-        for (int k0 = 0;;) {
+        float lk[NB];
+        for (int k0 = 0; k0 < n; k0 += PPW * NB) {
 #pragma unroll
             for (int u = 0; u < NB; ++u) {
-                const float w = weight(k0 + u * PPW + which);
+                const int k = k0 + u * PPW + which;
+                const int kk = k < n ? k : 0;
+                v[u] = __builtin_nontemporal_load(part_ptr(kk));
+                lk[u] = __builtin_nontemporal_load(lrow + slot_of(kk));
+            }
+            float bm = -INFINITY;
+#pragma unroll
+            for (int u = 0; u < NB; ++u) {
+                if (k0 + u * PPW + which >= n) lk[u] = -INFINITY;
+                bm = fmaxf(bm, lk[u]);
+            }
+            const float nm = fmaxf(mx, bm);
+            const float muse = nm == -INFINITY ? 0.f : nm;
+            const float sc = exp2f(mx - muse);   // 0 while mx is -inf
+            acc.x *= sc;
+            acc.y *= sc;
+            acc.z *= sc;
+            acc.w *= sc;
+            wsum *= sc;
+#pragma unroll
+            for (int u = 0; u < NB; ++u) {
+                const float w = exp2f(lk[u] - muse);
                 acc.x = fmaf(w, v[u].x, acc.x);
                 acc.y = fmaf(w, v[u].y, acc.y);
                 acc.z = fmaf(w, v[u].z, acc.z);
                 acc.w = fmaf(w, v[u].w, acc.w);
+                wsum += w;
             }
-            k0 += PPW * NB;
-            if (k0 >= n) break;
-#pragma unroll
-            for (int u = 0; u < NB; ++u) {
-                const int k = k0 + u * PPW + which;
-                v[u] = __builtin_nontemporal_load(part_ptr(k < n ? k : 0));
-            }
+            mx = nm;
         }
     };
     if (n <= PPW * SMALL) run(std::integral_constant<int, SMALL>{});
     else run(std::integral_constant<int, BATCH>{});
 #pragma unroll
     for (int off = LPP; off < 64; off <<= 1) {
-        acc.x += __shfl_xor(acc.x, off, 64);
-        acc.y += __shfl_xor(acc.y, off, 64);
-        acc.z += __shfl_xor(acc.z, off, 64);
-        acc.w += __shfl_xor(acc.w, off, 64);
+        const float om = __shfl_xor(mx, off, 64);
+        const float ow = __shfl_xor(wsum, off, 64);
+        const float ox = __shfl_xor(acc.x, off, 64), oy = __shfl_xor(acc.y, off, 64);
+        const float oz = __shfl_xor(acc.z, off, 64), ov = __shfl_xor(acc.w, off, 64);
+        const float nm = fmaxf(mx, om);
+        const float muse = nm == -INFINITY ? 0.f : nm;
+        const float s0 = exp2f(mx - muse), s1 = exp2f(om - muse);
+        acc.x = acc.x * s0 + ox * s1;
+        acc.y = acc.y * s0 + oy * s1;
+        acc.z = acc.z * s0 + oz * s1;
+        acc.w = acc.w * s0 + ov * s1;
+        wsum = wsum * s0 + ow * s1;
+        mx = nm;
     }
     const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
     if (which == 0)
