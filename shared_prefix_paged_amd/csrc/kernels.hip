@@ -804,10 +804,13 @@ __device__ __forceinline__ void attend_range_mfma(const Args &a, const Req &r, i
 //  - slots: the step's new COLD slot (append mode), checked on the host (in
 //    range, room in the block table);
 //  - prefix_np: partial states of the MFMA prefix pass, from the host copies
-//    of the group arrays, so no merging wave waits on a geometry load.
+//    of the group arrays, so no merging wave waits on a geometry load;
+//  - flat_np: partial states of the paged pass (its ranges over the request,
+//    from the launch's offsets), so no merging wave divides 64-bit integers.
 struct MergeRows {
     int32_t slots[spkv::kFlatArgReqs];
     uint8_t prefix_np[spkv::kFlatArgReqs];
+    uint8_t flat_np[spkv::kFlatArgReqs];
 };
 
 // Occupancy, float32: 4 waves per SIMD (<= 128 VGPRs) up to G = 6, 3 above;
@@ -1701,7 +1704,9 @@ __global__ __launch_bounds__(256) void merge_kernel(Args a, float *out, float *l
     constexpr int LPP = D / 4;      // lanes per partial row (float4 each)
     constexpr int PPW = 64 / LPP;   // partial rows per wave-wide load
     constexpr int BATCH = 40 / PPW; // wave-wide loads in flight (40 partials)
-    constexpr int SMALL = 16 / PPW; // the same for rows of at most 16 partials
+    constexpr int MID = 24 / PPW;   // the same for rows of at most 24 partials,
+    constexpr int SMALL = 16 / PPW; // 16
+    constexpr int TINY = 8 / PPW;   // and 8
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: geometry by scalar loads
     const int lane = threadIdx.x & 63;
     if constexpr (APPEND) {
@@ -1737,9 +1742,8 @@ __global__ __launch_bounds__(256) void merge_kernel(Args a, float *out, float *l
     if (row >= (int64_t)(fr.b0 + fr.nreq) * a.Hq) return;
     const int b = (int)(row / a.Hq);
     const int i = b - fr.b0;
-    int first;
     int np = a.prefix_mode == 1 ? ap.prefix_np[i] : 0;
-    int nf = flat_parts(fr, i, &first);
+    int nf = ap.flat_np[i];
     np = max(0, min(np, a.prefix_splits));   // never read past this row's partial slots
     nf = max(0, min(nf, a.flat_splits));
     const int n = np + nf;           // <= 128
@@ -1765,8 +1769,8 @@ __global__ __launch_bounds__(256) void merge_kernel(Args a, float *out, float *l
     // lane, and FMAs; the LPP-lane groups that read different partials merge
     // their states once at the end (Eq. (1) between lanes).  Loads past the
     // last partial re-read partial 0 (in bounds; weight 0), so a batch is
-    // straight-line code with a single wait; rows with few partials take a
-    // smaller batch.  (Non-temporal: partial states are read once, and must
+    // straight-line code with a single wait; a row takes the smallest batch
+    // that holds its partials (loads that only re-read partial 0 still cost).  (Non-temporal: partial states are read once, and must
     // not displace K/V lines the next step reads again.)
     const float *lrow = a.lse_part + prow0;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -1809,7 +1813,9 @@ __global__ __launch_bounds__(256) void merge_kernel(Args a, float *out, float *l
             mx = nm;
         }
     };
-    if (n <= PPW * SMALL) run(std::integral_constant<int, SMALL>{});
+    if (n <= PPW * TINY) run(std::integral_constant<int, TINY>{});
+    else if (n <= PPW * SMALL) run(std::integral_constant<int, SMALL>{});
+    else if (n <= PPW * MID) run(std::integral_constant<int, MID>{});
     else run(std::integral_constant<int, BATCH>{});
 #pragma unroll
     for (int off = LPP; off < 64; off <<= 1) {
@@ -2234,6 +2240,10 @@ spkv_status launch_merge(const Args &a, int d, float *out, float *lse, const Fla
     MergeRows ap{};
     if (prefix_np)
         for (int i = 0; i < fr.nreq; ++i) ap.prefix_np[i] = prefix_np[fr.b0 + i];
+    for (int i = 0; i < fr.nreq; ++i) {
+        int first;
+        ap.flat_np[i] = (uint8_t)std::min(flat_parts(fr, i, &first), 255);
+    }
     if (append_slots) {
         for (int i = 0; i < fr.nreq; ++i) ap.slots[i] = append_slots[fr.b0 + i];
         grid.x += (unsigned)((fr.nreq + 3) / 4);   // the new-token waves
