@@ -458,14 +458,17 @@ def test_single_launch_matches_two_launches(name):
         assert torch.equal(st.batch.tables, b.batch.tables) and torch.equal(st.batch.lens, b.batch.lens)
 
 
-def test_prefix_only_requests_and_a_64k_prefix():
+@pytest.mark.parametrize("d", [128, 64])
+def test_prefix_only_requests_and_a_64k_prefix(d):
     # Degenerate lengths: requests whose whole context is their group's
     # prefix (no COLD token: the suffix part is empty, weight 0 in Eq. (1)),
     # a request with neither (zero output, log-sum-exp -inf), and one group
     # with a 65536-token prefix (key chunks at the 64-split cap), in every mode.
-    note("[gpu] prefix-only requests, 64K prefix")
+    # Rows of that group merge more partial states than one load batch holds
+    # (over 40), so the merge's later batches rescale what the first summed.
+    note(f"[gpu] prefix-only requests, 64K prefix, d={d}")
     suffix = [0, 7, 0, 300, 1, 0, 45, 0]
-    wl = W.make_custom(batch=8, num_q_heads=8, num_kv_heads=2, head_dim=128, dtype="bf16",
+    wl = W.make_custom(batch=8, num_q_heads=8, num_kv_heads=2, head_dim=d, dtype="bf16",
                        group_prefix_len=[65536, 700], group_of=[0, 0, 1, 1, 0, -1, 1, 0], suffix_len=suffix, seed=70)
     ref_o, ref_l = decode_reference(wl)
     st = setup_single_step(wl)            # appends at least one token per request ...
@@ -473,6 +476,8 @@ def test_prefix_only_requests_and_a_64k_prefix():
     st.batch.lens_h[zero] = 0             # ... so the empty suffixes are set afterwards, host and device
     st.batch.lens.copy_(torch.from_numpy(st.batch.lens_h).to(st.batch.lens.device))
     ws = R.workspace(st.batch)
+    fp, pp = st.batch.plan_parts([1, 1])
+    assert int((fp + pp).max()) > 40, "a row merges more partials than one load batch"
     for mode, fn in (("cascade", lambda: R.cascade_decode(st.batch, st.pools, ws)),
                      ("dense", lambda: R.dense_decode(st.batch, st.pools, ws)),
                      ("per_group", lambda: R.decode_step(st.batch, st.pools, R.default_params(A.SPKV_MODE_PER_GROUP), ws)[:2])):
